@@ -61,14 +61,17 @@ def quantize_int8(W: np.ndarray, rows: np.ndarray | None = None):
 
     W is float32 [N, K].  Returns (q int8 [N, K] (or [len(rows), K] when
     ``rows`` selects output rows; the scale still comes from the whole tensor),
-    scale float32).  An all-zero tensor has scale 0 and all-zero codes.
+    scale float32).  An all-zero tensor, or one whose scale underflows fp32, has
+    scale 0 and all-zero codes; a non-finite weight raises ValueError.
     """
     W = np.asarray(W, dtype=np.float32)
+    if not np.all(np.isfinite(W)):
+        raise ValueError("non-finite weight")
     m = np.float32(np.max(np.abs(W))) if W.size else np.float32(0.0)
     sel = W if rows is None else W[np.asarray(rows)]
-    if m == 0:
-        return np.zeros(sel.shape, np.int8), np.float32(0.0)
     s = np.float32(m / np.float32(INT8_QMAX))           # fp32 division
+    if s == 0:                                          # all zero, or the scale underflows
+        return np.zeros(sel.shape, np.int8), np.float32(0.0)
     t = sel / s                                           # fp32 IEEE division, elementwise
     q = np.clip(np.rint(t), -INT8_QMAX, INT8_QMAX)        # half to even
     return q.astype(np.int8), s
@@ -146,9 +149,11 @@ def quantize_int4o(W: np.ndarray, perm: np.ndarray, n_out: int, group: int = GRO
     W is float32 [N, K] in original channel order.  Returns
     (codes int8 [N, K_pad] in [-7, 7] with zero padding,
      scales float16 [N, G], w_out float16 [N, n_out]).
-    Raises ValueError if a group scale overflows fp16.
+    Raises ValueError for a non-finite weight or a group scale that overflows fp16.
     """
     W = np.asarray(W, np.float32)
+    if not np.all(np.isfinite(W)):
+        raise ValueError("non-finite weight")
     N, K = W.shape
     geo = int4o_geometry(K, n_out, group)
     K_bg, G, K_pad = geo["K_bg"], geo["G"], geo["K_pad"]

@@ -48,6 +48,11 @@ def test_int8_closed_form_bound(seed):
 def test_int8_zero_tensor_and_empty():
     q, s = O.quantize_int8(np.zeros((3, 4), np.float32))
     assert s == 0 and not q.any()
+    # max|W| = 2^-149 (smallest subnormal): max/127 underflows to 0
+    q, s = O.quantize_int8(np.array([[np.float32(2.0 ** -149), 0]], np.float32))
+    assert s == 0 and not q.any()
+    with pytest.raises(ValueError):
+        O.quantize_int8(np.array([[1.0, np.nan]], np.float32))
     q, s = O.quantize_int8(np.zeros((0, 4), np.float32))
     assert q.shape == (0, 4)
 
