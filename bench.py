@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the weight-only quantised linear stack on one MI355X.
+
+Default workload: the 3B-shaped outlier-INT4 decode stack (hidden 3072,
+intermediate 8192, 28 layers, 24 q / 8 kv heads of 128), batch 1, every weight
+resident in HBM.  One step = one decode pass through every linear of every
+layer (q|k|v, o, gate|up, down per layer; each with its input permutation).
+
+Prints one JSON line.  ``value`` is the achieved algorithmic bandwidth of the
+whole step (bytes the method must move per step / step time); ``decode_tok_s``
+is batch / step time.  ``roofline`` covers the dominant kernel (the product
+kernel), timed with HIP events on its own stream inside the timed region.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dequant-GEMV achieved HBM GB/s (% of peak) and decode tok/s, batch 1, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(fmt: str, N: int, K: int, b: int) -> int:
+    """Bytes the method must move for one linear call: codes (unpadded), scales,
+    FP16 outlier columns, fp16 activations in and out."""
+    if fmt == "int8":
+        return N * K + 4 + 2 * b * (K + N)
+    n_out = (K + 99) // 100
+    K_bg = K - n_out
+    G = -(-K_bg // 128)
+    return (N * K_bg) // 2 + 2 * N * G + 2 * N * n_out + 2 * b * (K + N)
+
+
+def cpu_baseline(spec, b: int, budget_s: float = 12.0):
+    """The oracle, untuned, on a bounded sample: the decode products of layer 0
+    (and more layers while the budget lasts), scaled to a whole step."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    groups = ((("q", "k", "v"), 0), (("o",), 1), (("gate", "up"), 2), (("down",), 3))
+    t_dec = 0.0
+    layers_done = 0
+    bytes_done = 0
+    t_start = time.perf_counter()
+    for layer in range(spec.layers):
+        prepared = []
+        for names, inp in groups:
+            x = synth.decode_input(spec, layer, inp, b)
+            for n in names:
+                lin = spec.linear(n)
+                W = synth.weight(spec, layer, lin)
+                if spec.fmt == "int4o":
+                    perm = O.global_perm(lin.K, synth.planted_set(spec, lin.space))
+                    prepared.append(("int4o", O.quantize_int4o(W, perm, O.n_outliers(lin.K)), perm, x, lin))
+                else:
+                    prepared.append(("int8", O.quantize_int8(W), None, x, lin))
+                del W
+        t0 = time.perf_counter()
+        for fmt, qw, perm, x, lin in prepared:
+            if fmt == "int4o":
+                x_bg, x_out = O.permute_split(x, perm, O.n_outliers(lin.K))
+                O.linear_int4o(*qw, x_bg, x_out)
+            else:
+                O.linear_int8(*qw, x)
+            bytes_done += algorithmic_bytes(fmt, lin.N, lin.K, b)
+        t_dec += time.perf_counter() - t0
+        layers_done += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    step_s = t_dec / layers_done * spec.layers
+    per_step = bytes_done / layers_done * spec.layers
+    return {"value": round(per_step / step_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "decode_tok_s": round(b / step_s, 5),
+            "sample": f"float64 NumPy oracle decode products of {layers_done} of {spec.layers} layers at batch {b} "
+                      f"(weights quantised by the oracle outside the timing), {t_dec:.1f} s, scaled to one step; "
+                      f"host os.cpu_count()={os.cpu_count()}, BLAS threads={blas_threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4])
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="resident layers (default: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the decode linears are measured on one "
+              "device's share); --gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from weight_only_quantized_quantize_amd import woq
+    from weight_only_quantized_quantize_amd.stack import ResidentStack
+
+    woq.require_gpu()
+    spec = synth.stack_spec(args.config)
+    b = args.batch or spec.batches[0]
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+    t0 = time.perf_counter()
+    rs = ResidentStack(spec, lambda layer, lin, out: synth.weight(spec, layer, lin, out=out),
+                       lambda space: synth.profile(spec, space), layers=args.layers, log=log)
+    L = rs.n_layers
+    log(f"prepared {L} layers in {time.perf_counter() - t0:.1f} s; {rs.device_bytes() / 1e9:.3f} GB resident")
+
+    inputs, outputs = [], []
+    for layer in range(L):
+        for gi, (names, inp) in enumerate(((("q", "k", "v"), 0), (("o",), 1), (("gate", "up"), 2), (("down",), 3))):
+            x = synth.decode_input(spec, layer, inp, b)
+            inputs.append(torch.from_numpy(x).cuda())
+            N = sum(spec.linear(n).N for n in names)
+            outputs.append(torch.empty(b, N, dtype=torch.float16, device="cuda"))
+    runner = rs.make_runner(max(b, 1))
+    runner.bind(inputs, outputs)
+    stream = torch.cuda.current_stream()
+
+    shapes = rs.group_shapes()
+    step_bytes = sum(algorithmic_bytes(spec.fmt, N, K, b) for N, K, _ in shapes)
+
+    for _ in range(args.warmup):
+        runner.run(b, stream)
+    torch.cuda.synchronize()
+
+    # timed region: K passes, HIP events around every product launch and pass
+    t_start = time.perf_counter()
+    step_ms, pass_ms = runner.time(b, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    kern_ms = sum(step_ms)
+    kname = ("qgemv_int4o_valu" if b < 8 else "qgemm_int4o_mfma") if spec.fmt == "int4o" else "qgemv_int8_valu"
+    achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32 on int4 codes" if spec.fmt == "int4o" else "f16xf16->f32 on int8 codes",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}, batch {b}" + (f", {L} layers resident" if L != spec.layers else ""),
+                   "format": spec.fmt, "layers": L, "hidden": spec.hidden, "intermediate": spec.inter,
+                   "q_heads": spec.q_heads, "kv_heads": spec.kv_heads, "head_dim": spec.head_dim,
+                   "batch": b, "launches_per_step": 2 * len(shapes) if spec.fmt == "int4o" else len(shapes),
+                   "algorithmic_bytes_per_step": step_bytes},
+        "decode_tok_s": round(b / (ms_per_step * 1e-3), 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "event_pass_ms": round(pass_ms, 5),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launches_per_step": len(shapes),
+                     "mean_launch_us": round(1e3 * kern_ms / len(shapes), 3),
+                     "mean_algorithmic_bytes_per_launch": step_bytes // len(shapes)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(spec, b)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

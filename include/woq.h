@@ -1,0 +1,297 @@
+/*
+ * woq.h - C ABI of libwoq: weight-only quantised linear layers for LLM decode
+ * on AMD MI355X (gfx950).
+ *
+ * Two weight formats are supported.
+ *
+ *  INT8  - symmetric per-tensor quantisation: scale = max|W| / 127 and
+ *          code = round(W / scale), reconstructed as code * scale ("Open Origin -
+ *          ELG Stream Layer" README, Technical Architecture: "INT8 Quantization
+ *          & Direct Mapping" and "FP16 On-The-Fly GPU Reconstruction").
+ *  INT4O - outlier-aware INT4 ("On-The-Fly Weight Synthesizer (OTF-LLM Engine)",
+ *          Architecture & Key Innovations, the architecture diagram and item 3):
+ *          a global input-channel permutation puts the top 1% of channels by
+ *          |W| x |X_profile| at the end and keeps them as FP16; the other 99%
+ *          are INT4 codes in [-7, 7] with zero-point 0, packed two per byte,
+ *          with one fp16 scale per output row per 128 background channels; the
+ *          output is X_out W_out^T + X_bg deq(W_bg)^T.
+ *
+ * Conventions for every entry point.
+ *  - Matrices are row-major.  A weight is [N, K] (N output features, K input
+ *    features); activations are x [b, K] and outputs y [b, N].
+ *  - fp16 values cross the ABI as uint16_t bit patterns.
+ *  - Rounding is IEEE round-to-nearest-even everywhere (W / scale is an fp32
+ *    division; a code is the nearest integer, ties to even, then clamped to
+ *    +-127 or +-7).
+ *  - Every function returns an int status (WOQ_OK or a negative WOQ_E* code).
+ *    Arguments are checked before any work starts; on an error nothing is
+ *    written.  No C++ exception crosses the ABI.
+ *  - Host functions are synchronous, run on the calling thread plus a pool of
+ *    worker threads (WOQ_NUM_THREADS, default min(16, hardware threads)) and
+ *    give bit-identical results for any thread count.
+ *  - Device functions are asynchronous on the caller's stream (a hipStream_t
+ *    passed as void*; NULL is the default stream).  Pointers are device memory
+ *    owned by the caller and must stay valid until the stream reaches the
+ *    work.  Vector-loaded pointers must be 16-byte aligned (WOQ_EALIGN
+ *    otherwise).  A launch failure returns WOQ_EHIP (see woq_last_hip_error);
+ *    a fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - The library allocates no memory visible to the caller, except inside the
+ *    opaque runtime objects, which own their buffers until destroyed.
+ */
+#ifndef WOQ_H
+#define WOQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+
+#define WOQ_OK            0
+#define WOQ_EINVAL       (-1)  /* bad argument: null pointer, negative or inconsistent size */
+#define WOQ_EALIGN       (-2)  /* pointer or leading dimension not aligned as required */
+#define WOQ_ENOMEM       (-3)  /* host or device allocation failed (runtime objects only) */
+#define WOQ_EHIP         (-4)  /* a HIP call failed; woq_last_hip_error() gives its code */
+#define WOQ_EUNSUPPORTED (-5)  /* valid request that this build does not implement */
+#define WOQ_ERANGE       (-6)  /* value not representable: non-finite weight, fp16 scale overflow */
+
+#define WOQ_ABI_VERSION 1
+
+/* Static English text for a status code (never NULL). */
+const char* woq_strerror(int status);
+/* hipError_t of the last failing HIP call on this thread (0 if none). */
+int woq_last_hip_error(void);
+/* WOQ_ABI_VERSION of the built library. */
+int woq_abi_version(void);
+
+/* ---------------------------------------------------------------- geometry */
+
+/*
+ * Sizes of the outlier split of one input space of width K.
+ *   canonical: K_bg = K - n_out background channels in G = ceil(K_bg/128)
+ *              groups, zero-padded to K_pad = 128 * G.
+ *   device   : G4 = G rounded up to a multiple of 4, n_out8 = n_out rounded
+ *              up to a multiple of 8; a permuted activation row (woq_permute_x)
+ *              holds xp_len = 128 * G4 + n_out8 fp16 values: the background
+ *              channels, zeros up to 128 * G4, the outlier channels, zeros.
+ */
+typedef struct {
+    int64_t K, n_out, K_bg, G, K_pad;
+    int64_t G4, n_out8, xp_len;
+} woq_int4o_geom;
+
+/* Fill *g for an input space of width K >= 1 with 0 <= n_out <= K outlier
+ * channels.  n_out < 0 selects the default ceil(K/100) (the pages' 1%). */
+int woq_int4o_geometry(int64_t K, int64_t n_out, woq_int4o_geom* g);
+
+/* ------------------------------------------------------------ host: INT8 */
+
+/*
+ * Quantise W (float32 [N, K]) with one fp32 scale for the whole tensor:
+ * *scale = fp32(max|W| / 127), q = clamp(rne(fp32(W / *scale)), -127, 127).
+ * An all-zero tensor (or one whose scale underflows to 0) gives *scale = 0 and
+ * q = 0.  WOQ_ERANGE if W holds a NaN or an infinity.  q is int8 [N, K].
+ * ("Open Origin - ELG Stream Layer", Technical Architecture: the scale and
+ * int8 equations.)
+ */
+int woq_quantize_int8(const float* W, int64_t N, int64_t K, int8_t* q, float* scale);
+
+/* ----------------------------------------------------------- host: INT4O */
+
+/*
+ * colsum[j] += sum_n |W[n, j]| in float64, for every input channel j of one
+ * linear (W float32 [N, K]).  Call once for every linear of every layer that
+ * reads the input space, then woq_outlier_select.  The sum over n runs in
+ * row order for each j, whatever the thread count.
+ */
+int woq_colabs_accumulate(const float* W, int64_t N, int64_t K, double* colsum);
+
+/*
+ * Global static permutation of one input space ("On-The-Fly Weight
+ * Synthesizer (OTF-LLM Engine)", item 3): score_j = mean_t |xprof[t, j]| *
+ * colsum[j] in float64 (xprof fp16 [T, K], T >= 1); the n_out channels with the
+ * largest score (ties to the lower index) are the outliers.  perm (int32 [K])
+ * receives the background channels in ascending order followed by the outlier
+ * channels in ascending order.  n_out < 0 selects ceil(K/100).
+ */
+int woq_outlier_select(const double* colsum, const uint16_t* xprof, int64_t T, int64_t K,
+                       int64_t n_out, int32_t* perm);
+
+/*
+ * Outlier-aware INT4 encoding of W (float32 [N, K], original channel order)
+ * under perm (int32 [K], as from woq_outlier_select) with n_out outlier
+ * channels (n_out < 0: ceil(K/100)).  Writes the canonical arrays:
+ *   packed uint8 [N, K_pad/2]  - byte j of a row holds the code of permuted
+ *                                background channel 2j in its low nibble and
+ *                                2j+1 in its high nibble, two's complement,
+ *                                zero codes in the padding;
+ *   scales fp16  [N, G]        - scale of group g = fp16(fp32(max|W_g| / 7))
+ *                                over the group's real channels;
+ *   w_out  fp16  [N, n_out]    - fp16(W[:, perm[K_bg + i]]).
+ * Codes are clamp(rne(fp32(W / fp32(scale))), -7, 7), or 0 where the scale is 0.
+ * WOQ_ERANGE for a non-finite weight or a scale that overflows fp16;
+ * WOQ_EINVAL if perm is not a permutation of 0..K-1.
+ */
+int woq_quantize_int4o(const float* W, int64_t N, int64_t K, const int32_t* perm, int64_t n_out,
+                       uint8_t* packed, uint16_t* scales, uint16_t* w_out);
+
+/* Unpack canonical packed codes (uint8 [N, K_pad/2]) to int8 [N, K_pad]. */
+int woq_unpack_int4(const uint8_t* packed, int64_t N, int64_t K_pad, int8_t* q);
+
+/* ---------------------------------------------------- host: device layouts */
+
+/*
+ * INT8 device layout: N4 = N rounded up to 4 rows, Kd = K rounded up to 64
+ * columns; row-major [N4, Kd] bytes holding code + 128 (offset binary), with
+ * code 0 in the padding.  woq_int8_dev_bytes gives the size.
+ */
+int64_t woq_int8_dev_bytes(int64_t N, int64_t K);
+int woq_layout_int8(const int8_t* q, int64_t N, int64_t K, uint8_t* dev);
+int woq_layout_int8_inverse(const uint8_t* dev, int64_t N, int64_t K, int8_t* q);
+
+/*
+ * INT4O device layout (N4 = N rounded up to 4):
+ *   codes  : N4 rows of 64 * G4 bytes.  Row n holds, for each group g and each
+ *            32-channel chunk c of the group, 16 bytes: the codes of background
+ *            channels 128g + 32c + 16P + t (P = 0, 1; t = 0..15) as offset-binary
+ *            nibbles (code + 8), dword e (0, 1) of half P holding, at nibble
+ *            positions 0,4,2,6 the channels t = 4e+0..4e+3 and at positions
+ *            1,5,3,7 the channels t = 8+4e+0..8+4e+3.  Padding holds code 0.
+ *   scales : [N4/4][G4][4] fp16 - the four rows of a quad side by side per group.
+ *   w_out  : [N4, n_out8] fp16, zero-padded.
+ * Byte sizes from woq_int4o_dev_sizes.  The inverse reproduces the canonical
+ * arrays bit for bit.
+ */
+int woq_int4o_dev_sizes(int64_t N, const woq_int4o_geom* g, int64_t* codes_bytes,
+                        int64_t* scales_bytes, int64_t* wout_bytes);
+int woq_layout_int4o(const uint8_t* packed, const uint16_t* scales, const uint16_t* w_out, int64_t N,
+                     const woq_int4o_geom* g, uint8_t* dev_codes, uint16_t* dev_scales,
+                     uint16_t* dev_wout);
+int woq_layout_int4o_inverse(const uint8_t* dev_codes, const uint16_t* dev_scales,
+                             const uint16_t* dev_wout, int64_t N, const woq_int4o_geom* g,
+                             uint8_t* packed, uint16_t* scales, uint16_t* w_out);
+
+/* ----------------------------------------------------------- device ops */
+
+#define WOQ_MAX_SEGMENTS 8
+
+/*
+ * An INT8 weight resident in device memory (woq_layout_int8 of N rows).  Rows
+ * [seg_end[i-1], seg_end[i]) use seg_scale[i] (seg_end[-1] = 0,
+ * seg_end[nseg-1] = N): one segment for a single linear, several for linears
+ * that read the same input and are stacked along N into one launch.
+ */
+typedef struct {
+    const void* codes;
+    int64_t N, K;
+    int32_t nseg;
+    int64_t seg_end[WOQ_MAX_SEGMENTS];
+    float seg_scale[WOQ_MAX_SEGMENTS];
+} woq_int8_w;
+
+/* An INT4O weight resident in device memory (woq_layout_int4o of N rows). */
+typedef struct {
+    const void* codes;
+    const void* scales;
+    const void* w_out;
+    int64_t N;
+    woq_int4o_geom geom;
+} woq_int4o_w;
+
+/*
+ * Permute and split activations for an INT4O input space (the architecture
+ * diagram's "Global Static Permutation" and its outlier / background split):
+ * xp[r, k] = x[r, perm[k]] for k < K_bg, 0 for K_bg <= k < 128*G4,
+ * xp[r, 128*G4 + i] = x[r, perm[K_bg + i]] for i < n_out, 0 up to n_out8.
+ * x fp16 [b, ldx] (ldx >= K), perm int32 [K] in device memory, xp fp16
+ * [b, g->xp_len] (16-byte aligned).  b = 0 is a no-op.
+ */
+int woq_permute_x(const uint16_t* x, int64_t ldx, const int32_t* perm, int64_t b,
+                  const woq_int4o_geom* g, uint16_t* xp, void* stream);
+
+/*
+ * y[r, n] = fp16(scale(n) * sum_k code[n, k] * x[r, k]) for r < b, n < N, with
+ * fp32 accumulation, reading the INT8 codes once from HBM and converting them
+ * in registers (the reconstruction step of "Open Origin - ELG Stream Layer",
+ * fused into the product).  x fp16 [b, ldx], 16-byte aligned, ldx a multiple
+ * of 8 and >= K; y fp16 [b, ldy], ldy >= N.  1 <= b <= 8 (b = 0 is a no-op).
+ */
+int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t b,
+                   uint16_t* y, int64_t ldy, void* stream);
+
+/*
+ * y[r, n] = fp16(sum_i w_out[n, i] xp[r, 128*G4 + i]
+ *               + sum_g scale[n, g] sum_{k in g} code[n, k] xp[r, k])
+ * with fp32 accumulation ("On-The-Fly Weight Synthesizer (OTF-LLM Engine)",
+ * architecture diagram: the outlier GEMM and the fused background GEMM added
+ * into one FP16 output).  xp from woq_permute_x (fp16 [b, xp_len]); y fp16
+ * [b, ldy], ldy >= N.  b <= 7 runs the vector-ALU kernel, b >= 8 the matrix-core
+ * kernel (woq_qgemm_int4o).  1 <= b <= 64 (b = 0 is a no-op).
+ */
+int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
+                    int64_t ldy, void* stream);
+
+/* The matrix-core (MFMA) kernel of woq_qgemv_int4o for any 1 <= b <= 64. */
+int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
+                    int64_t ldy, void* stream);
+
+/* --------------------------------------------------------- layer stack */
+
+#define WOQ_FMT_INT8  1
+#define WOQ_FMT_INT4O 2
+
+/*
+ * One step of a decode stack: a (possibly N-stacked) linear that reads input
+ * slot in_slot and writes output slot out_slot.  fmt selects w8 or w4; an
+ * INT4O step also names the device permutation of its input space (int32
+ * [geom.K]).  Slots index the pointer arrays given to woq_stack_run.
+ */
+typedef struct {
+    int32_t fmt;
+    int32_t in_slot, out_slot;
+    woq_int8_w w8;
+    woq_int4o_w w4;
+    const int32_t* perm;
+} woq_stack_step;
+
+typedef struct woq_stack woq_stack;
+
+/*
+ * Create a runner for n_steps steps executed in order on one stream ("Open
+ * Origin - ELG Stream Layer", Key Features 2: each layer's cycle, and the
+ * OTF-LLM runner that drives the model through the fused kernels).  The step
+ * array is copied; the weights it points to stay owned by the caller.  The
+ * runner owns an activation workspace for batches up to max_b (allocated on
+ * the current device here).  WOQ_ENOMEM if that allocation fails.
+ */
+int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b, woq_stack** out);
+
+/*
+ * Run every step once: for each step, permute its input (INT4O) and launch
+ * its product, all on `stream`.  inputs[slot] are fp16 [b, K of the step]
+ * activations (rows contiguous), outputs[slot] fp16 [b, N of the step].
+ * 1 <= b <= max_b.  Asynchronous; the caller synchronises.
+ */
+int woq_stack_run(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                  void* stream);
+
+/*
+ * woq_stack_run repeated `iters` times with a pair of HIP events recorded on
+ * `stream` around every product launch and around every pass.  On return
+ * (the stream is synchronised) step_ms[i] (n_steps floats) holds the mean
+ * duration of step i's product kernel and *pass_ms the mean duration of one
+ * pass.  For measurement only; iters >= 1.
+ */
+int woq_stack_time(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                   void* stream, int32_t iters, float* step_ms, float* pass_ms);
+
+/* Release the runner and its workspace (after the stream has finished). */
+int woq_stack_destroy(woq_stack* st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WOQ_H */

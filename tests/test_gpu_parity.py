@@ -1,0 +1,255 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the oracle.
+
+Outputs are compared element by element with the float64 oracle on the same
+seeded inputs; the gate is the normwise relative error
+max|y - y_ref| / max|y_ref| <= 2e-3 (fp32 accumulation, fp16 output).  The
+permutation kernel is integer work and must match bit for bit.  Full-size
+shapes are checked on sampled output rows, which the oracle can compute one by
+one because every output row depends only on its own weight row.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from weight_only_quantized_quantize_amd import woq
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _empty16(*shape):
+    import torch
+    return torch.empty(*shape, dtype=torch.float16, device="cuda")
+
+
+def _print_case(*args):
+    print("case:", *args, flush=True)
+
+
+# ------------------------------------------------------------------ helpers
+
+def int8_case(W_parts, x):
+    """Quantise with the library (bit-exactness to the oracle is a CPU test),
+    run the kernel, and return (y_gpu, y_oracle)."""
+    parts = [woq.woq_quantize_int8(W) for W in W_parts]
+    dw = woq.DeviceInt8(parts)
+    xd = _dev(x)
+    y = _empty16(x.shape[0], dw.N)
+    woq.woq_qgemv_int8(dw.desc, xd, y)
+    ref = np.concatenate([O.linear_int8(*O.quantize_int8(W), x) for W in W_parts], axis=1)
+    return _host(y).astype(np.float64), ref
+
+
+def int4o_parts(W_list, perm, n_out):
+    return [woq.woq_quantize_int4o(W, perm, n_out) for W in W_list]
+
+
+def int4o_run(parts, g, perm, x, force_mfma=False):
+    dw = woq.DeviceInt4o(parts, g)
+    xd = _dev(x)
+    xp = _empty16(x.shape[0], g.xp_len)
+    woq.woq_permute_x(xd, _dev(perm), g, xp)
+    y = _empty16(x.shape[0], dw.N)
+    (woq.woq_qgemm_int4o if force_mfma else woq.woq_qgemv_int4o)(dw.desc, xp, y)
+    return _host(y).astype(np.float64), _host(xp)
+
+
+def int4o_ref(W_list, perm, n_out, x):
+    x_bg, x_out = O.permute_split(x, perm, n_out)
+    ys = []
+    for W in W_list:
+        c, s, wo = O.quantize_int4o(W, perm, n_out)
+        ys.append(O.linear_int4o(c, s, wo, x_bg, x_out))
+    return np.concatenate(ys, axis=1)
+
+
+def check(y, ref, what):
+    err = O.normwise_rel_err(y, ref)
+    print(f"{what}: normwise rel err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(y)), what
+    assert err <= TOL, (what, err)
+    return err
+
+
+# ------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("K,n_out,b", [(3072, -1, 1), (300, 3, 5), (129, 1, 2), (256, 0, 3), (16, 16, 1),
+                                       (28672, -1, 2)])
+def test_permute_x_bit_exact(gpu_lib, K, n_out, b):
+    _print_case("permute", K, n_out, b)
+    rng = np.random.default_rng(K)
+    g = woq.woq_int4o_geometry(K, n_out)
+    perm = O.global_perm(K, np.sort(rng.choice(K, g.n_out, replace=False)))
+    x = rng.standard_normal((b, K)).astype(np.float16)
+    xd = _dev(x)
+    xp = _empty16(b, g.xp_len)
+    xp.fill_(7.0)                      # padding must be overwritten with zeros
+    woq.woq_permute_x(xd, _dev(perm), g, xp)
+    got = _host(xp)
+    x_bg, x_out = O.permute_split(x, perm, g.n_out)
+    want = np.zeros((b, g.xp_len), np.float16)
+    want[:, : g.K_pad] = x_bg
+    want[:, 128 * g.G4: 128 * g.G4 + g.n_out] = x_out
+    np.testing.assert_array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+# -------------------------------------------------------------------- INT8
+
+def test_int8_single_linear_4096(gpu_lib):
+    _print_case("int8 4096x4096 b=1 seed 0")
+    W, x = synth.config1_inputs()
+    y, ref = int8_case([W], x)
+    check(y, ref, "int8 4096^2")
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (5, 33), (130, 1000), (67, 3584), (4, 17)])
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+def test_int8_ragged(gpu_lib, N, K, b):
+    _print_case("int8", N, K, b)
+    rng = np.random.default_rng(N * 7 + K + b)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((b, K)).astype(np.float16)
+    y, ref = int8_case([W], x)
+    check(y, ref, f"int8 {N}x{K} b={b}")
+
+
+def test_int8_fused_segments(gpu_lib):
+    _print_case("int8 fused q|k|v")
+    spec = synth.small_stack_spec(3, layers=1)
+    Ws = [synth.weight(spec, 0, n) for n in ("q", "k", "v")]
+    Ws[1] = Ws[1] * np.float32(7.0)        # distinct per-tensor scales
+    x = synth.decode_input(spec, 0, 0, 4)
+    y, ref = int8_case(Ws, x)
+    check(y, ref, "int8 fused")
+
+
+def test_int8_config3_full_shapes_sampled(gpu_lib):
+    spec = synth.stack_spec(3)
+    rng = np.random.default_rng(3)
+    for lin in spec.linears():
+        _print_case("int8 cfg3", lin.name, lin.N, lin.K)
+        W = synth.weight(spec, 0, lin)
+        x = synth.decode_input(spec, 0, lin.inp, 4)
+        q, s = woq.woq_quantize_int8(W)
+        dw = woq.DeviceInt8([(q, s)])
+        for b in (1, 4):
+            y = _empty16(b, lin.N)
+            woq.woq_qgemv_int8(dw.desc, _dev(x[:b]), y)
+            rows = np.sort(rng.choice(lin.N, 64, replace=False))
+            qo, so = O.quantize_int8(W, rows=rows)
+            ref = O.linear_int8(qo, so, x[:b])
+            check(_host(y)[:, rows].astype(np.float64), ref, f"int8 cfg3 {lin.name} b={b}")
+
+
+# ------------------------------------------------------------------- INT4O
+
+@pytest.mark.parametrize("N,K,n_out", [(4, 128, 0), (5, 300, 3), (130, 1000, -1), (9, 129, 1), (8, 16, 16),
+                                       (67, 3072, -1), (3, 700, 0)])
+@pytest.mark.parametrize("b", [1, 2, 3, 7])
+def test_int4o_valu_ragged(gpu_lib, N, K, n_out, b):
+    _print_case("int4o valu", N, K, n_out, b)
+    rng = np.random.default_rng(N + K + b)
+    g = woq.woq_int4o_geometry(K, n_out)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x)
+    check(y, int4o_ref([W], perm, g.n_out, x), f"int4o {N}x{K} n_out={g.n_out} b={b}")
+
+
+@pytest.mark.parametrize("N,K,n_out", [(16, 128, 0), (37, 300, 3), (130, 1000, -1), (64, 3072, -1), (20, 16, 16)])
+@pytest.mark.parametrize("b", [1, 8, 16, 17, 32, 64])
+def test_int4o_mfma_ragged(gpu_lib, N, K, n_out, b):
+    _print_case("int4o mfma", N, K, n_out, b)
+    rng = np.random.default_rng(N * 3 + K + b)
+    g = woq.woq_int4o_geometry(K, n_out)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x, force_mfma=True)
+    check(y, int4o_ref([W], perm, g.n_out, x), f"int4o mfma {N}x{K} n_out={g.n_out} b={b}")
+
+
+def test_int4o_small_stack_layer_fused(gpu_lib):
+    """A reduced config-2 layer: global perms from the library's own selection,
+    q|k|v and gate|up fused along N."""
+    spec = synth.small_stack_spec(2, layers=2)
+    perms = {}
+    for space in synth.SPACES:
+        K = spec.space_width(space)
+        cs = np.zeros(K)
+        for layer in range(spec.layers):
+            for lin in spec.linears():
+                if lin.space == space:
+                    woq.woq_colabs_accumulate(synth.weight(spec, layer, lin), cs)
+        perms[space] = woq.woq_outlier_select(cs, synth.profile(spec, space))
+    for layer in range(spec.layers):
+        for names, inp in ((("q", "k", "v"), 0), (("o",), 1), (("gate", "up"), 2), (("down",), 3)):
+            _print_case("int4o small stack", layer, names)
+            lin0 = spec.linear(names[0])
+            perm = perms[lin0.space]
+            g = woq.woq_int4o_geometry(lin0.K)
+            Ws = [synth.weight(spec, layer, n) for n in names]
+            x = synth.decode_input(spec, layer, inp, 1)
+            y, _ = int4o_run(int4o_parts(Ws, perm, g.n_out), g, perm, x)
+            check(y, int4o_ref(Ws, perm, g.n_out, x), f"layer {layer} {'|'.join(names)}")
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_int4o_full_shapes_sampled(gpu_lib, cfg):
+    """Every linear shape of the 3B- and 70B-shaped stacks at full size (layer 0),
+    in the launch configuration the benchmark uses, on sampled output rows.
+    The permutation is the planted set, which selection recovers (CPU test)."""
+    spec = synth.stack_spec(cfg)
+    rng = np.random.default_rng(cfg)
+    for lin in spec.linears():
+        K = lin.K
+        g = woq.woq_int4o_geometry(K)
+        perm = O.global_perm(K, synth.planted_set(spec, lin.space))
+        W = synth.weight(spec, 0, lin)
+        part = woq.woq_quantize_int4o(W, perm, g.n_out)
+        rows = np.sort(rng.choice(lin.N, 48, replace=False))
+        c, s, wo = O.quantize_int4o(W[rows], perm, g.n_out)
+        del W
+        x = synth.decode_input(spec, 0, lin.inp)
+        for b in spec.batches:
+            _print_case("int4o full", cfg, lin.name, lin.N, K, b)
+            y, _ = int4o_run([part], g, perm, x[:b])
+            x_bg, x_out = O.permute_split(x[:b], perm, g.n_out)
+            check(y[:, rows], O.linear_int4o(c, s, wo, x_bg, x_out), f"cfg{cfg} {lin.name} b={b}")
+
+
+def test_batch_prefix_invariant(gpu_lib):
+    """Row 0 of a b=32 matrix-core call agrees with the b=1 vector-ALU call."""
+    _print_case("prefix invariant")
+    rng = np.random.default_rng(5)
+    K, N = 1000, 96
+    g = woq.woq_int4o_geometry(K)
+    perm = O.global_perm(K, np.sort(rng.choice(K, g.n_out, replace=False)))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((32, K)).astype(np.float16)
+    parts = int4o_parts([W], perm, g.n_out)
+    y32, _ = int4o_run(parts, g, perm, x)
+    y1, _ = int4o_run(parts, g, perm, x[:1])
+    assert O.normwise_rel_err(y32[:1], y1) <= 1e-3

@@ -1,0 +1,555 @@
+// Device kernels of libwoq for gfx950 (CDNA4), and their C-ABI launchers.
+//
+// Decode linears are bound by HBM bandwidth: every packed weight byte is read
+// once per call and never reused, while the activations are a few kilobytes
+// shared by every row.  The kernels therefore
+//   * stream the codes with 16-byte non-temporal vector loads (each lane owns
+//     one 16-byte chunk of each of four consecutive rows, so a wave's load of
+//     one row is a contiguous kilobyte),
+//   * turn codes into exact fp16 values in registers with the exponent-bias
+//     trick (an offset-binary code u in the low mantissa bits of 0x6400 is the
+//     fp16 number 1024 + u; subtracting 1024 + offset leaves the signed code),
+//   * multiply with v_dot2_f32_f16 (two fp16 products summed into an fp32
+//     accumulator, so the products are exact and the accumulation is fp32),
+//   * apply the per-group (INT4O) or per-tensor (INT8) scale in fp32 and
+//     reduce the 64 lanes of a wave with cross-lane shuffles,
+//   * for batch >= 8 (INT4O), feed the same in-register fp16 codes to the
+//     16x16x32 fp16 matrix-core instruction, where the work becomes a real
+//     contraction over the batch.
+//
+// Formats: "Open Origin - ELG Stream Layer" (INT8 per-tensor scale, the
+// reconstruction code * scale, fused here into the product) and "On-The-Fly
+// Weight Synthesizer (OTF-LLM Engine)" (outlier-aware INT4: permuted input,
+// FP16 outlier columns plus INT4 background with per-128-channel scales, both
+// partial products added into one FP16 output).
+#include <hip/hip_runtime.h>
+
+#include "woq_internal.h"
+
+namespace woq {
+static thread_local int g_last_hip_error = 0;
+void set_hip_error(int code) { g_last_hip_error = code; }
+}  // namespace woq
+
+extern "C" int woq_last_hip_error(void) { return woq::g_last_hip_error; }
+
+namespace {
+
+typedef _Float16 f16;
+typedef f16 h2 __attribute__((ext_vector_type(2)));
+typedef f16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ float h_to_f(uint16_t v) { return (float)__builtin_bit_cast(f16, v); }
+__device__ __forceinline__ uint16_t f_to_h(float v) { return __builtin_bit_cast(uint16_t, (f16)v); }
+
+__device__ __forceinline__ float dot2(h2 a, h2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Streamed 16-byte load: weight bytes are read exactly once, so they are
+// marked non-temporal and do not push the shared activations out of cache.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// fp16 pairs from an INT4O device dword (see woq_layout_int4o): returns the
+// two unscaled pairs (channels 4e+0,1 and 4e+2,3 of the half-chunk) and the
+// two pairs that carry 16 x code (channels 8+4e+0,1 and 8+4e+2,3).
+struct Int4Pairs {
+    h2 lo0, lo1, hi0, hi1;
+};
+__device__ __forceinline__ Int4Pairs int4_pairs(uint32_t w) {
+    const h2 off_lo = {(f16)1032.0f, (f16)1032.0f};   // 1024 + 8
+    const h2 off_hi = {(f16)1152.0f, (f16)1152.0f};   // 1024 + 16 * 8
+    uint32_t s = w >> 8;
+    Int4Pairs p;
+    p.lo0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - off_lo;
+    p.lo1 = as_h2((s & 0x000F000Fu) | 0x64006400u) - off_lo;
+    p.hi0 = as_h2((w & 0x00F000F0u) | 0x64006400u) - off_hi;
+    p.hi1 = as_h2((s & 0x00F000F0u) | 0x64006400u) - off_hi;
+    return p;
+}
+
+// fp16 pairs (channels 0,1 and 2,3) of an INT8 device dword (offset binary).
+__device__ __forceinline__ void int8_pairs(uint32_t w, h2& a, h2& b) {
+    const h2 off = {(f16)1152.0f, (f16)1152.0f};      // 1024 + 128
+    a = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00050004u)) - off;
+    b = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00070006u)) - off;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// ------------------------------------------------------------ permute/split
+
+__global__ void permute_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ perm,
+                                 int K, int K_bg, int n_out, int bg_len, int xp_len, uint16_t* __restrict__ xp) {
+    const int64_t r = blockIdx.y;
+    const uint16_t* xr = x + r * ldx;
+    for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < xp_len; k += gridDim.x * blockDim.x) {
+        int src = -1;
+        if (k < K_bg) src = perm[k];
+        else if (k >= bg_len && k - bg_len < n_out) src = perm[K_bg + (k - bg_len)];
+        // an index outside [0, K) cannot come from a valid permutation; read 0
+        uint16_t v = ((unsigned)src < (unsigned)K) ? xr[src] : (uint16_t)0;
+        xp[r * xp_len + k] = v;
+    }
+}
+
+// ------------------------------------------------------- INT4O, batch <= 7
+
+struct Int4oArgs {
+    const uint4* codes;     // [N4][4*G4] chunks of 16 bytes
+    const uint2* scales;    // [N4/4][G4] x 4 fp16
+    const uint4* wout;      // [N4][n_out8/8] chunks of 8 fp16
+    const uint16_t* xp;     // [b][xp_len]
+    uint16_t* y;            // [b][ldy]
+    int N, G4, no8, xp_len, ldy;
+};
+
+// One wave per quad of four output rows; lanes stride over the rows' 16-byte
+// chunks (a chunk = 32 background channels of one group).
+template <int B>
+__global__ __launch_bounds__(64) void qgemv_int4o_valu(Int4oArgs a) {
+    const int lane = threadIdx.x;
+    const int quad = blockIdx.x;
+    const int CPR = a.G4 * 4;
+    const uint4* w0 = a.codes + (int64_t)quad * 4 * CPR;
+    float acc[4][B];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+
+#pragma unroll 2
+    for (int cc = lane; cc < CPR; cc += 64) {
+        uint4 w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = load_stream(w0 + r * CPR + cc);
+        const uint2 sc = a.scales[(int64_t)quad * a.G4 + (cc >> 2)];
+        uint4 xv[B][4];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const uint4* xs = reinterpret_cast<const uint4*>(a.xp + (int64_t)b * a.xp_len + 32 * cc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[b][j] = xs[j];
+        }
+        const float s[4] = {h_to_f((uint16_t)(sc.x & 0xFFFF)), h_to_f((uint16_t)(sc.x >> 16)),
+                            h_to_f((uint16_t)(sc.y & 0xFFFF)), h_to_f((uint16_t)(sc.y >> 16))};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+            Int4Pairs p[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d]);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                // x pairs of channels 0..15 (xv[b][0..1]) and 16..31 (xv[b][2..3])
+                const uint32_t xw[16] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
+                                         xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w,
+                                         xv[b][2].x, xv[b][2].y, xv[b][2].z, xv[b][2].w,
+                                         xv[b][3].x, xv[b][3].y, xv[b][3].z, xv[b][3].w};
+                float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+                for (int P = 0; P < 2; ++P) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const Int4Pairs& q = p[2 * P + e];
+                        lo = dot2(q.lo0, as_h2(xw[8 * P + 2 * e + 0]), lo);
+                        lo = dot2(q.lo1, as_h2(xw[8 * P + 2 * e + 1]), lo);
+                        hi = dot2(q.hi0, as_h2(xw[8 * P + 4 + 2 * e + 0]), hi);
+                        hi = dot2(q.hi1, as_h2(xw[8 * P + 4 + 2 * e + 1]), hi);
+                    }
+                }
+                acc[r][b] = fmaf(s[r], fmaf(hi, 0.0625f, lo), acc[r][b]);
+            }
+        }
+    }
+
+    // FP16 outlier columns: 8 per 16-byte chunk
+    const uint16_t* xo_base = a.xp + 128 * a.G4;
+    for (int oc = lane; oc < a.no8; oc += 64) {
+        uint4 wo[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wo[r] = a.wout[((int64_t)quad * 4 + r) * a.no8 + oc];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const uint4 xo = *reinterpret_cast<const uint4*>(xo_base + (int64_t)b * a.xp_len + 8 * oc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float t = acc[r][b];
+                t = dot2(as_h2(wo[r].x), as_h2(xo.x), t);
+                t = dot2(as_h2(wo[r].y), as_h2(xo.y), t);
+                t = dot2(as_h2(wo[r].z), as_h2(xo.z), t);
+                t = dot2(as_h2(wo[r].w), as_h2(xo.w), t);
+                acc[r][b] = t;
+            }
+        }
+    }
+
+    float out = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float v = wave_sum(acc[r][b]);
+            if (lane == r * B + b) out = v;
+        }
+    if (lane < 4 * B) {
+        const int r = lane / B, b = lane % B;
+        const int n = quad * 4 + r;
+        if (n < a.N) a.y[(int64_t)b * a.ldy + n] = f_to_h(out);
+    }
+}
+
+// --------------------------------------------------------- INT8, batch <= 8
+
+struct Int8Args {
+    const uint4* codes;     // [N4][Kd/16] chunks of 16 bytes
+    const uint16_t* x;      // [b][ldx]
+    uint16_t* y;            // [b][ldy]
+    int N, K, CPR, ldx, ldy, nseg;
+    int seg_end[WOQ_MAX_SEGMENTS];
+    float seg_scale[WOQ_MAX_SEGMENTS];
+};
+
+template <int B>
+__global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
+    const int lane = threadIdx.x;
+    const int quad = blockIdx.x;
+    const uint4* w0 = a.codes + (int64_t)quad * 4 * a.CPR;
+    const int nchunks = (a.K + 15) >> 4;   // chunks that hold real columns
+    float acc[4][B];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+
+#pragma unroll 2
+    for (int cc = lane; cc < nchunks; cc += 64) {
+        uint4 w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = load_stream(w0 + r * a.CPR + cc);
+        uint4 xv[B][2];
+        const int k0 = 16 * cc;
+        if (k0 + 16 <= a.K) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint4* xs = reinterpret_cast<const uint4*>(a.x + (int64_t)b * a.ldx + k0);
+                xv[b][0] = xs[0];
+                xv[b][1] = xs[1];
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                uint16_t t[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) t[j] = (k0 + j < a.K) ? a.x[(int64_t)b * a.ldx + k0 + j] : (uint16_t)0;
+                xv[b][0] = make_uint4(t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16));
+                xv[b][1] = make_uint4(t[8] | (t[9] << 16), t[10] | (t[11] << 16), t[12] | (t[13] << 16),
+                                      t[14] | (t[15] << 16));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+            h2 q[8];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) int8_pairs(wd[d], q[2 * d], q[2 * d + 1]);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint32_t xw[8] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
+                                        xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w};
+                float t = acc[r][b];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) t = dot2(q[j], as_h2(xw[j]), t);
+                acc[r][b] = t;
+            }
+        }
+    }
+
+    float out = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float v = wave_sum(acc[r][b]);
+            if (lane == r * B + b) out = v;
+        }
+    if (lane < 4 * B) {
+        const int r = lane / B, b = lane % B;
+        const int n = quad * 4 + r;
+        if (n < a.N) {
+            float s = a.seg_scale[a.nseg - 1];
+            for (int i = a.nseg - 1; i >= 0; --i)
+                if (n < a.seg_end[i]) s = a.seg_scale[i];
+            a.y[(int64_t)b * a.ldy + n] = f_to_h(out * s);
+        }
+    }
+}
+
+// ------------------------------------------------ INT4O, matrix cores (b >= 8)
+
+// A workgroup of four waves owns 16 output rows; wave w takes the groups
+// g = w, w + 4, ...  Lane l holds row l & 15 of the 16-row tile and the
+// 16-byte chunk l >> 4 of each group (32 channels) - exactly the A operand of
+// v_mfma_f32_16x16x32_f16 for four k-steps: the unscaled pairs feed steps 0
+// and 2, the pairs that carry 16 x code feed steps 1 and 3 into a second
+// accumulator that is divided by 16 before the group scale is applied.  The B
+// operand (activations, batch column l & 15) is read from memory in the same
+// channel order.  Partial sums of the four waves meet in LDS.
+template <int NBT>
+__global__ __launch_bounds__(256) void qgemm_int4o_mfma(Int4oArgs a, int b) {
+    __shared__ float red[4][NBT][16][17];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15;           // row within the tile (A) / batch column (B)
+    const int c = lane >> 4;           // 32-channel chunk of the group / k-block
+    const int row = blockIdx.x * 16 + m;
+    const int N4 = (a.N + 3) & ~3;
+    const bool row_ok = row < N4;
+    const int CPR = a.G4 * 4;
+    const uint4* wrow = a.codes + (int64_t)row * CPR;
+    const int quad0 = blockIdx.x * 4;  // first quad of the tile
+
+    f4 acc[NBT];
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) acc[t] = (f4){0.f, 0.f, 0.f, 0.f};
+
+    for (int g = wave; g < a.G4; g += 4) {
+        uint4 w = row_ok ? load_stream(wrow + 4 * g + c) : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        Int4Pairs p[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d]);
+        // A operands of the four k-steps (8 fp16 each)
+        h8 A[4];
+#pragma unroll
+        for (int P = 0; P < 2; ++P) {
+            const Int4Pairs& e0 = p[2 * P];
+            const Int4Pairs& e1 = p[2 * P + 1];
+            A[2 * P + 0] = (h8){e0.lo0[0], e0.lo0[1], e0.lo1[0], e0.lo1[1], e1.lo0[0], e1.lo0[1], e1.lo1[0], e1.lo1[1]};
+            A[2 * P + 1] = (h8){e0.hi0[0], e0.hi0[1], e0.hi1[0], e0.hi1[1], e1.hi0[0], e1.hi0[1], e1.hi1[0], e1.hi1[1]};
+        }
+        // per-row scales of this group for the four D rows this lane holds
+        float s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * c + i;      // D row held by this lane
+            const int q = quad0 + (rr >> 2);
+            s[i] = (q * 4 < N4) ? h_to_f(reinterpret_cast<const uint16_t*>(a.scales)[((int64_t)q * a.G4 + g) * 4 + (rr & 3)]) : 0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) {
+            const int col = t * 16 + m;    // batch column of the B operand
+            h8 Bv[4];
+            if (col < b) {
+                const uint4* xs = reinterpret_cast<const uint4*>(a.xp + (int64_t)col * a.xp_len + 128 * g + 32 * c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Bv[j] = __builtin_bit_cast(h8, xs[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Bv[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+            }
+            f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
+            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], Bv[0], lo, 0, 0, 0);
+            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], Bv[1], hi, 0, 0, 0);
+            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], Bv[2], lo, 0, 0, 0);
+            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], Bv[3], hi, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(s[i], fmaf(hi[i], 0.0625f, lo[i]), acc[t][i]);
+        }
+    }
+
+    // FP16 outlier columns, 32 per k-step, split over the waves
+    const uint16_t* xo_base = a.xp + 128 * a.G4;
+    const int n_o8 = a.no8 * 8;
+    for (int st = wave; st * 32 < n_o8; st += 4) {
+        const int col0 = 32 * st + 8 * c;
+        h8 Av = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+        if (row_ok && col0 < n_o8)
+            Av = __builtin_bit_cast(h8, a.wout[(int64_t)row * a.no8 + (col0 >> 3)]);
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) {
+            const int bc = t * 16 + m;
+            h8 Bv = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+            if (bc < b && col0 < n_o8)
+                Bv = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(xo_base + (int64_t)bc * a.xp_len + col0));
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Bv, acc[t], 0, 0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < NBT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][t][4 * c + i][m] = acc[t][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < NBT * 256; e += 256) {
+        const int t = e >> 8, rr = (e >> 4) & 15, col = e & 15;
+        const int bc = t * 16 + col;
+        const int n = blockIdx.x * 16 + rr;
+        if (bc < b && n < a.N) {
+            float v = red[0][t][rr][col] + red[1][t][rr][col] + red[2][t][rr][col] + red[3][t][rr][col];
+            a.y[(int64_t)bc * a.ldy + n] = f_to_h(v);
+        }
+    }
+}
+
+int launch_status(hipError_t e) {
+    if (e != hipSuccess) {
+        woq::set_hip_error((int)e);
+        return WOQ_EHIP;
+    }
+    return WOQ_OK;
+}
+
+template <int B>
+void launch_int4o_valu(const Int4oArgs& a, int quads, hipStream_t s) {
+    hipLaunchKernelGGL(qgemv_int4o_valu<B>, dim3(quads), dim3(64), 0, s, a);
+}
+
+template <int B>
+void launch_int8_valu(const Int8Args& a, int quads, hipStream_t s) {
+    hipLaunchKernelGGL(qgemv_int8_valu<B>, dim3(quads), dim3(64), 0, s, a);
+}
+
+template <int NBT>
+void launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
+    const int tiles = (int)woq::ceil_div(woq::round_up(a.N, 4), 16);
+    hipLaunchKernelGGL(qgemm_int4o_mfma<NBT>, dim3(tiles), dim3(256), 0, s, a, b);
+}
+
+int check_int4o_w(const woq_int4o_w* w) {
+    if (!w || w->N < 0 || !woq::int4o_geom_valid(&w->geom)) return WOQ_EINVAL;
+    if (w->N > 0 && (!w->codes || !w->scales || (w->geom.n_out8 && !w->w_out))) return WOQ_EINVAL;
+    if (!woq::aligned16(w->codes) || !woq::aligned16(w->w_out) || (((uintptr_t)w->scales) & 7u)) return WOQ_EALIGN;
+    if (w->N > (int64_t)INT32_MAX - 64 || w->geom.xp_len > (int64_t)INT32_MAX / 64) return WOQ_EUNSUPPORTED;
+    return WOQ_OK;
+}
+
+Int4oArgs make_int4o_args(const woq_int4o_w* w, const uint16_t* xp, uint16_t* y, int64_t ldy) {
+    Int4oArgs a;
+    a.codes = reinterpret_cast<const uint4*>(w->codes);
+    a.scales = reinterpret_cast<const uint2*>(w->scales);
+    a.wout = reinterpret_cast<const uint4*>(w->w_out);
+    a.xp = xp;
+    a.y = y;
+    a.N = (int)w->N;
+    a.G4 = (int)w->geom.G4;
+    a.no8 = (int)(w->geom.n_out8 / 8);
+    a.xp_len = (int)w->geom.xp_len;
+    a.ldy = (int)ldy;
+    return a;
+}
+
+int int4o_common_checks(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy) {
+    int st = check_int4o_w(w);
+    if (st) return st;
+    if (b < 0 || b > 64 || ldy < w->N || ldy > INT32_MAX) return WOQ_EINVAL;
+    if (b > 0 && w->N > 0 && (!xp || !y)) return WOQ_EINVAL;
+    if (!woq::aligned16(xp) || ((uintptr_t)y & 1u)) return WOQ_EALIGN;
+    return WOQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int woq_permute_x(const uint16_t* x, int64_t ldx, const int32_t* perm, int64_t b, const woq_int4o_geom* g,
+                  uint16_t* xp, void* stream) {
+    if (!woq::int4o_geom_valid(g) || b < 0 || ldx < g->K) return WOQ_EINVAL;
+    if (b == 0) return WOQ_OK;
+    if (!x || !perm || !xp) return WOQ_EINVAL;
+    if (!woq::aligned16(xp) || ((uintptr_t)x & 1u) || ((uintptr_t)perm & 3u)) return WOQ_EALIGN;
+    if (b > 65535 || g->xp_len > INT32_MAX) return WOQ_EUNSUPPORTED;
+    const int threads = 256;
+    int blocks = (int)std::min<int64_t>(woq::ceil_div(g->xp_len, threads), 1024);
+    hipLaunchKernelGGL(permute_x_kernel, dim3(blocks, (unsigned)b), dim3(threads), 0, (hipStream_t)stream, x, ldx,
+                       perm, (int)g->K, (int)g->K_bg, (int)g->n_out, (int)(128 * g->G4), (int)g->xp_len, xp);
+    return launch_status(hipGetLastError());
+}
+
+int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy, void* stream) {
+    int st = int4o_common_checks(w, xp, b, y, ldy);
+    if (st) return st;
+    if (b == 0 || w->N == 0) return WOQ_OK;
+    if (b >= 8) return woq_qgemm_int4o(w, xp, b, y, ldy, stream);
+    Int4oArgs a = make_int4o_args(w, xp, y, ldy);
+    const int quads = (int)woq::ceil_div(w->N, 4);
+    hipStream_t s = (hipStream_t)stream;
+    switch (b) {
+        case 1: launch_int4o_valu<1>(a, quads, s); break;
+        case 2: launch_int4o_valu<2>(a, quads, s); break;
+        case 3: launch_int4o_valu<3>(a, quads, s); break;
+        case 4: launch_int4o_valu<4>(a, quads, s); break;
+        case 5: launch_int4o_valu<5>(a, quads, s); break;
+        case 6: launch_int4o_valu<6>(a, quads, s); break;
+        default: launch_int4o_valu<7>(a, quads, s); break;
+    }
+    return launch_status(hipGetLastError());
+}
+
+int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy, void* stream) {
+    int st = int4o_common_checks(w, xp, b, y, ldy);
+    if (st) return st;
+    if (b == 0 || w->N == 0) return WOQ_OK;
+    Int4oArgs a = make_int4o_args(w, xp, y, ldy);
+    hipStream_t s = (hipStream_t)stream;
+    const int nbt = (int)woq::ceil_div(b, 16);
+    switch (nbt) {
+        case 1: launch_int4o_mfma<1>(a, (int)b, s); break;
+        case 2: launch_int4o_mfma<2>(a, (int)b, s); break;
+        case 3: launch_int4o_mfma<3>(a, (int)b, s); break;
+        default: launch_int4o_mfma<4>(a, (int)b, s); break;
+    }
+    return launch_status(hipGetLastError());
+}
+
+int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t b, uint16_t* y, int64_t ldy,
+                   void* stream) {
+    if (!w || w->N < 0 || w->K < 1 || b < 0 || b > 8 || ldx < w->K || ldy < w->N) return WOQ_EINVAL;
+    if (w->nseg < 1 || w->nseg > WOQ_MAX_SEGMENTS || w->seg_end[w->nseg - 1] != w->N) return WOQ_EINVAL;
+    for (int i = 0; i < w->nseg; ++i) {
+        int64_t lo = i ? w->seg_end[i - 1] : 0;
+        if (w->seg_end[i] < lo) return WOQ_EINVAL;
+    }
+    if (b == 0 || w->N == 0) return WOQ_OK;
+    if (!w->codes || !x || !y) return WOQ_EINVAL;
+    if (!woq::aligned16(w->codes) || !woq::aligned16(x) || (ldx & 7) || ((uintptr_t)y & 1u)) return WOQ_EALIGN;
+    if (w->N > (int64_t)INT32_MAX - 64 || w->K > (int64_t)INT32_MAX - 64 || ldx > INT32_MAX || ldy > INT32_MAX)
+        return WOQ_EUNSUPPORTED;
+    Int8Args a;
+    a.codes = reinterpret_cast<const uint4*>(w->codes);
+    a.x = x;
+    a.y = y;
+    a.N = (int)w->N;
+    a.K = (int)w->K;
+    a.CPR = (int)(woq::round_up(w->K, 64) / 16);
+    a.ldx = (int)ldx;
+    a.ldy = (int)ldy;
+    a.nseg = w->nseg;
+    for (int i = 0; i < WOQ_MAX_SEGMENTS; ++i) {
+        a.seg_end[i] = i < w->nseg ? (int)w->seg_end[i] : (int)w->N;
+        a.seg_scale[i] = i < w->nseg ? w->seg_scale[i] : 0.0f;
+    }
+    const int quads = (int)woq::ceil_div(w->N, 4);
+    hipStream_t s = (hipStream_t)stream;
+    switch (b) {
+        case 1: launch_int8_valu<1>(a, quads, s); break;
+        case 2: launch_int8_valu<2>(a, quads, s); break;
+        case 3: launch_int8_valu<3>(a, quads, s); break;
+        case 4: launch_int8_valu<4>(a, quads, s); break;
+        case 5: launch_int8_valu<5>(a, quads, s); break;
+        case 6: launch_int8_valu<6>(a, quads, s); break;
+        case 7: launch_int8_valu<7>(a, quads, s); break;
+        default: launch_int8_valu<8>(a, quads, s); break;
+    }
+    return launch_status(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal helpers shared by the host and device translation units of libwoq.
+#pragma once
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <thread>
+#include <vector>
+
+#include "woq.h"
+
+namespace woq {
+
+// hipError_t of the last failing HIP call on this thread.
+void set_hip_error(int code);
+
+inline int64_t round_up(int64_t a, int64_t m) { return (a + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t a, int64_t m) { return (a + m - 1) / m; }
+
+// Geometry of an outlier split (validated); mirrors woq_int4o_geometry.
+int int4o_geom(int64_t K, int64_t n_out, woq_int4o_geom* g);
+// True if *g is what woq_int4o_geometry gives for its own K and n_out.
+bool int4o_geom_valid(const woq_int4o_geom* g);
+
+inline int num_threads() {
+    static int n = [] {
+        int hw = (int)std::thread::hardware_concurrency();
+        if (hw <= 0) hw = 1;
+        int want = std::min(hw, 16);
+        if (const char* e = std::getenv("WOQ_NUM_THREADS")) {
+            int v = std::atoi(e);
+            if (v > 0) want = v;
+        }
+        return want;
+    }();
+    return n;
+}
+
+// Run f(lo, hi) over [0, n) split into contiguous ranges, one per worker.
+// The split only decides which thread does which range; every caller makes
+// each element's result independent of the split, so results do not depend on
+// the thread count.
+template <class F>
+void parallel_for(int64_t n, F&& f, int64_t min_per_thread = 1) {
+    if (n <= 0) return;
+    int64_t nt = std::min<int64_t>(num_threads(), std::max<int64_t>(1, n / std::max<int64_t>(1, min_per_thread)));
+    if (nt <= 1) {
+        f((int64_t)0, n);
+        return;
+    }
+    std::vector<std::thread> th;
+    th.reserve(nt - 1);
+    int64_t chunk = ceil_div(n, nt);
+    for (int64_t t = 1; t < nt; ++t) {
+        int64_t lo = t * chunk, hi = std::min(n, lo + chunk);
+        if (lo >= hi) break;
+        th.emplace_back([&f, lo, hi] { f(lo, hi); });
+    }
+    f((int64_t)0, std::min(n, chunk));
+    for (auto& t : th) t.join();
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace woq

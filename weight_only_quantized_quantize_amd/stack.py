@@ -1,0 +1,141 @@
+"""Build a resident decode stack on the GPU and run it through libwoq.
+
+Host orchestration only: weights come from a caller-supplied generator, every
+quantisation / selection / packing / layout step is a libwoq call, and the
+decode pass is ``woq_stack_run``.  Per layer there are four launches groups,
+each one N-stacked product: q|k|v (hidden input), o (attention output),
+gate|up (hidden input), down (intermediate input).
+"""
+from __future__ import annotations
+
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import woq
+
+GROUPS = ((("q", "k", "v"), 0), (("o",), 1), (("gate", "up"), 2), (("down",), 3))
+
+
+def _map_weights(spec, jobs, weight_fn, fn, threads):
+    """Run fn(layer, lin, W) over jobs with W drawn into per-thread buffers."""
+    jobs = list(jobs)
+    if not jobs:
+        return []
+    maxel = max(lin.N * lin.K for _, lin in jobs)
+    local = threading.local()
+
+    def run(job):
+        layer, lin = job
+        buf = getattr(local, "buf", None)
+        if buf is None:
+            buf = local.buf = np.ones(maxel, np.float32)
+        W = buf[: lin.N * lin.K].reshape(lin.N, lin.K)
+        weight_fn(layer, lin, W)
+        return fn(layer, lin, W)
+
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(run, jobs))
+
+
+class ResidentStack:
+    """All layers of a stack resident in HBM plus the runner.
+
+    spec: object with .fmt ("int8" | "int4o"), .layers, .linears(),
+          .space_width(space), .bmax
+    weight_fn(layer, lin, out): fill ``out`` (float32 [N, K]) with the weight
+    profile_fn(space): fp16 activation profile [T, K] of an input space
+    """
+
+    def __init__(self, spec, weight_fn, profile_fn=None, device="cuda", threads=None, layers=None, log=None):
+        import torch
+        self.spec = spec
+        self.device = device
+        self.fmt = spec.fmt
+        self.n_layers = spec.layers if layers is None else layers
+        threads = threads or min(16, os.cpu_count() or 1)
+        log = log or (lambda *a: None)
+        lin_by = {l.name: l for l in spec.linears()}
+        self.perm_host = {}
+        self.perm_dev = {}
+        self.geom = {}
+        if self.fmt == "int4o":
+            spaces = sorted({l.space for l in spec.linears()})
+            jobs = [(layer, lin) for layer in range(spec.layers) for lin in spec.linears()]
+            log(f"column sums over {len(jobs)} weights")
+
+            def colsum(layer, lin, W):
+                return woq.woq_colabs_accumulate(W, np.zeros(lin.K))
+
+            sums = _map_weights(spec, jobs, weight_fn, colsum, threads)
+            for space in spaces:
+                K = spec.space_width(space)
+                acc = np.zeros(K)
+                for (layer, lin), cs in zip(jobs, sums):      # fixed (layer, linear) order
+                    if lin.space == space:
+                        acc += cs
+                perm = woq.woq_outlier_select(acc, profile_fn(space))
+                self.perm_host[space] = perm
+                self.perm_dev[space] = torch.from_numpy(perm).to(device)
+                self.geom[space] = woq.woq_int4o_geometry(K)
+        self.layers = []          # per layer: list of (group names, input index, device weight)
+        chunk = 4
+        for l0 in range(0, self.n_layers, chunk):
+            ls = range(l0, min(self.n_layers, l0 + chunk))
+            jobs = [(layer, lin) for layer in ls for lin in spec.linears()]
+            log(f"quantising layers {ls.start}..{ls.stop - 1}")
+            if self.fmt == "int4o":
+                res = _map_weights(spec, jobs, weight_fn,
+                                   lambda layer, lin, W: woq.woq_quantize_int4o(W, self.perm_host[lin.space]),
+                                   threads)
+            else:
+                res = _map_weights(spec, jobs, weight_fn, lambda layer, lin, W: woq.woq_quantize_int8(W), threads)
+            got = {(layer, lin.name): r for (layer, lin), r in zip(jobs, res)}
+            for layer in ls:
+                groups = []
+                for names, inp in GROUPS:
+                    parts = [got[(layer, n)] for n in names]
+                    if self.fmt == "int4o":
+                        dev = woq.DeviceInt4o(parts, self.geom[lin_by[names[0]].space], device)
+                    else:
+                        dev = woq.DeviceInt8(parts, device)
+                    groups.append((names, inp, dev))
+                self.layers.append(groups)
+            del got, res
+        self.runner = None
+
+    def steps(self):
+        out = []
+        for layer, groups in enumerate(self.layers):
+            for gi, (names, inp, dev) in enumerate(groups):
+                slot = 4 * layer + gi
+                if self.fmt == "int4o":
+                    space = self.spec.linear(names[0]).space
+                    out.append(woq.step_int4o(dev, self.perm_dev[space], slot, slot))
+                else:
+                    out.append(woq.step_int8(dev, slot, slot))
+        return out
+
+    def make_runner(self, max_b: int):
+        self.runner = woq.Stack(self.steps(), max_b)
+        return self.runner
+
+    def group_shapes(self):
+        """(N, K) of every launch in step order."""
+        shapes = []
+        for groups in self.layers:
+            for names, inp, dev in groups:
+                shapes.append((dev.N, self.spec.linear(names[0]).K, names))
+        return shapes
+
+    def device_bytes(self) -> int:
+        tot = 0
+        for groups in self.layers:
+            for _, _, dev in groups:
+                for t in ("codes", "scales", "w_out"):
+                    x = getattr(dev, t, None)
+                    if x is not None:
+                        tot += x.numel() * x.element_size()
+        return tot

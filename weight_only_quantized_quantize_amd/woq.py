@@ -1,0 +1,390 @@
+"""Thin ctypes binding of libwoq (include/woq.h).
+
+Every function named ``woq_*`` here marshals its arguments and calls the C
+entry point of the same name; nothing is computed in Python.  Host arrays are
+NumPy arrays; device buffers are torch tensors (torch is used only for device
+memory and streams).  Errors raise :class:`WoqError`.  The library must have
+been built (``python -m weight_only_quantized_quantize_amd.build``); there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_uint8, c_uint16, c_void_p
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwoq.so")
+
+WOQ_OK, WOQ_EINVAL, WOQ_EALIGN, WOQ_ENOMEM, WOQ_EHIP, WOQ_EUNSUPPORTED, WOQ_ERANGE = 0, -1, -2, -3, -4, -5, -6
+MAX_SEGMENTS = 8
+
+
+class WoqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().woq_strerror(status).decode() if _LIB is not None else str(status)
+        if status == WOQ_EHIP and _LIB is not None:
+            msg += f" (hipError {_LIB.woq_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+
+
+class Int4oGeom(ctypes.Structure):
+    _fields_ = [(n, c_int64) for n in ("K", "n_out", "K_bg", "G", "K_pad", "G4", "n_out8", "xp_len")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class Int8W(ctypes.Structure):
+    _fields_ = [("codes", c_void_p), ("N", c_int64), ("K", c_int64), ("nseg", c_int32),
+                ("seg_end", c_int64 * MAX_SEGMENTS), ("seg_scale", c_float * MAX_SEGMENTS)]
+
+
+class Int4oW(ctypes.Structure):
+    _fields_ = [("codes", c_void_p), ("scales", c_void_p), ("w_out", c_void_p), ("N", c_int64),
+                ("geom", Int4oGeom)]
+
+
+class StackStep(ctypes.Structure):
+    _fields_ = [("fmt", c_int32), ("in_slot", c_int32), ("out_slot", c_int32), ("w8", Int8W), ("w4", Int4oW),
+                ("perm", c_void_p)]
+
+
+FMT_INT8, FMT_INT4O = 1, 2
+
+_LIB = None
+
+_SIGS = {
+    "woq_strerror": (ctypes.c_char_p, [c_int]),
+    "woq_last_hip_error": (c_int, []),
+    "woq_abi_version": (c_int, []),
+    "woq_int4o_geometry": (c_int, [c_int64, c_int64, POINTER(Int4oGeom)]),
+    "woq_quantize_int8": (c_int, [c_void_p, c_int64, c_int64, c_void_p, POINTER(c_float)]),
+    "woq_colabs_accumulate": (c_int, [c_void_p, c_int64, c_int64, c_void_p]),
+    "woq_outlier_select": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
+    "woq_quantize_int4o": (c_int, [c_void_p, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
+    "woq_unpack_int4": (c_int, [c_void_p, c_int64, c_int64, c_void_p]),
+    "woq_int8_dev_bytes": (c_int64, [c_int64, c_int64]),
+    "woq_layout_int8": (c_int, [c_void_p, c_int64, c_int64, c_void_p]),
+    "woq_layout_int8_inverse": (c_int, [c_void_p, c_int64, c_int64, c_void_p]),
+    "woq_int4o_dev_sizes": (c_int, [c_int64, POINTER(Int4oGeom), POINTER(c_int64), POINTER(c_int64), POINTER(c_int64)]),
+    "woq_layout_int4o": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, POINTER(Int4oGeom), c_void_p, c_void_p, c_void_p]),
+    "woq_layout_int4o_inverse": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, POINTER(Int4oGeom), c_void_p, c_void_p, c_void_p]),
+    "woq_permute_x": (c_int, [c_void_p, c_int64, c_void_p, c_int64, POINTER(Int4oGeom), c_void_p, c_void_p]),
+    "woq_qgemv_int8": (c_int, [POINTER(Int8W), c_void_p, c_int64, c_int64, c_void_p, c_int64, c_void_p]),
+    "woq_qgemv_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
+    "woq_qgemm_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
+    "woq_stack_create": (c_int, [POINTER(StackStep), c_int32, c_int64, POINTER(c_void_p)]),
+    "woq_stack_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
+    "woq_stack_time": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
+                               POINTER(c_float), POINTER(c_float)]),
+    "woq_stack_destroy": (c_int, [c_void_p]),
+}
+
+# symbols the header declares (checked by the CPU tests)
+EXPORTS = tuple(_SIGS)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libwoq.so is not built ({LIB_PATH}); run "
+                               "`python -m weight_only_quantized_quantize_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    """The loaded ctypes library (loads it on first use)."""
+    return _lib()
+
+
+def require_gpu():
+    """Raise unless a GPU is visible and the HIP library is loaded."""
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible: the weight-only quantised kernels run only on the GPU")
+    _lib()
+
+
+def _check(status: int, where: str):
+    if status != WOQ_OK:
+        raise WoqError(status, where)
+
+
+def _ptr(a) -> int:
+    """Address of a NumPy array (C-contiguous) or a torch tensor (contiguous)."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        assert a.flags["C_CONTIGUOUS"], "array must be C-contiguous"
+        return a.ctypes.data
+    assert a.is_contiguous(), "tensor must be contiguous"
+    return a.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ----------------------------------------------------------------- geometry
+
+def woq_int4o_geometry(K: int, n_out: int = -1) -> Int4oGeom:
+    g = Int4oGeom()
+    _check(_lib().woq_int4o_geometry(K, n_out, ctypes.byref(g)), "woq_int4o_geometry")
+    return g
+
+
+# ---------------------------------------------------------------- host prep
+
+def woq_quantize_int8(W: np.ndarray):
+    W = np.ascontiguousarray(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = c_float()
+    _check(_lib().woq_quantize_int8(_ptr(W), N, K, _ptr(q), ctypes.byref(s)), "woq_quantize_int8")
+    return q, np.float32(s.value)
+
+
+def woq_colabs_accumulate(W: np.ndarray, colsum: np.ndarray):
+    W = np.ascontiguousarray(W, np.float32)
+    assert colsum.dtype == np.float64 and colsum.shape == (W.shape[1],)
+    _check(_lib().woq_colabs_accumulate(_ptr(W), W.shape[0], W.shape[1], _ptr(colsum)), "woq_colabs_accumulate")
+    return colsum
+
+
+def woq_outlier_select(colsum: np.ndarray, xprof: np.ndarray, n_out: int = -1) -> np.ndarray:
+    colsum = np.ascontiguousarray(colsum, np.float64)
+    xprof = np.ascontiguousarray(xprof, np.float16)
+    T, K = xprof.shape
+    perm = np.empty(K, np.int32)
+    _check(_lib().woq_outlier_select(_ptr(colsum), _ptr(xprof.view(np.uint16)), T, K, n_out, _ptr(perm)),
+           "woq_outlier_select")
+    return perm
+
+
+def woq_quantize_int4o(W: np.ndarray, perm: np.ndarray, n_out: int = -1):
+    W = np.ascontiguousarray(W, np.float32)
+    perm = np.ascontiguousarray(perm, np.int32)
+    N, K = W.shape
+    g = woq_int4o_geometry(K, n_out)
+    packed = np.empty((N, g.K_pad // 2), np.uint8)
+    scales = np.empty((N, g.G), np.uint16)
+    w_out = np.empty((N, g.n_out), np.uint16)
+    _check(_lib().woq_quantize_int4o(_ptr(W), N, K, _ptr(perm), g.n_out, _ptr(packed), _ptr(scales), _ptr(w_out)),
+           "woq_quantize_int4o")
+    return packed, scales.view(np.float16), w_out.view(np.float16)
+
+
+def woq_unpack_int4(packed: np.ndarray) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, np.uint8)
+    N, half = packed.shape
+    q = np.empty((N, 2 * half), np.int8)
+    _check(_lib().woq_unpack_int4(_ptr(packed), N, 2 * half, _ptr(q)), "woq_unpack_int4")
+    return q
+
+
+def woq_layout_int8(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.int8)
+    N, K = q.shape
+    nbytes = _lib().woq_int8_dev_bytes(N, K)
+    dev = np.empty(nbytes, np.uint8)
+    _check(_lib().woq_layout_int8(_ptr(q), N, K, _ptr(dev)), "woq_layout_int8")
+    return dev
+
+
+def woq_layout_int8_inverse(dev: np.ndarray, N: int, K: int) -> np.ndarray:
+    q = np.empty((N, K), np.int8)
+    _check(_lib().woq_layout_int8_inverse(_ptr(np.ascontiguousarray(dev, np.uint8)), N, K, _ptr(q)),
+           "woq_layout_int8_inverse")
+    return q
+
+
+def woq_int4o_dev_sizes(N: int, g: Int4oGeom):
+    a, b, c = c_int64(), c_int64(), c_int64()
+    _check(_lib().woq_int4o_dev_sizes(N, ctypes.byref(g), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "woq_int4o_dev_sizes")
+    return a.value, b.value, c.value
+
+
+def woq_layout_int4o(packed, scales, w_out, g: Int4oGeom):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    scales = np.ascontiguousarray(np.asarray(scales).view(np.uint16))
+    w_out = np.ascontiguousarray(np.asarray(w_out).view(np.uint16))
+    N = packed.shape[0]
+    cb, sb, wb = woq_int4o_dev_sizes(N, g)
+    dc = np.empty(cb, np.uint8)
+    ds = np.empty(sb // 2, np.uint16)
+    dw = np.empty(wb // 2, np.uint16)
+    _check(_lib().woq_layout_int4o(_ptr(packed), _ptr(scales), _ptr(w_out), N, ctypes.byref(g), _ptr(dc), _ptr(ds),
+                                   _ptr(dw) if dw.size else None), "woq_layout_int4o")
+    return dc, ds, dw
+
+
+def woq_layout_int4o_inverse(dc, ds, dw, N: int, g: Int4oGeom):
+    packed = np.empty((N, g.K_pad // 2), np.uint8)
+    scales = np.empty((N, g.G), np.uint16)
+    w_out = np.empty((N, g.n_out), np.uint16)
+    _check(_lib().woq_layout_int4o_inverse(_ptr(dc), _ptr(ds), _ptr(dw) if dw.size else None, N, ctypes.byref(g),
+                                           _ptr(packed), _ptr(scales), _ptr(w_out)), "woq_layout_int4o_inverse")
+    return packed, scales.view(np.float16), w_out.view(np.float16)
+
+
+# --------------------------------------------------------------- device ops
+
+def woq_permute_x(x, perm_dev, g: Int4oGeom, xp, stream=None, ldx: int | None = None):
+    b = x.shape[0]
+    _check(_lib().woq_permute_x(_ptr(x), ldx or x.shape[1], _ptr(perm_dev), b, ctypes.byref(g), _ptr(xp),
+                                _stream(stream)), "woq_permute_x")
+    return xp
+
+
+def woq_qgemv_int8(w: Int8W, x, y, stream=None, b: int | None = None):
+    b = x.shape[0] if b is None else b
+    _check(_lib().woq_qgemv_int8(ctypes.byref(w), _ptr(x), x.shape[1], b, _ptr(y), y.shape[1], _stream(stream)),
+           "woq_qgemv_int8")
+    return y
+
+
+def woq_qgemv_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
+    b = xp.shape[0] if b is None else b
+    _check(_lib().woq_qgemv_int4o(ctypes.byref(w), _ptr(xp), b, _ptr(y), y.shape[1], _stream(stream)),
+           "woq_qgemv_int4o")
+    return y
+
+
+def woq_qgemm_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
+    b = xp.shape[0] if b is None else b
+    _check(_lib().woq_qgemm_int4o(ctypes.byref(w), _ptr(xp), b, _ptr(y), y.shape[1], _stream(stream)),
+           "woq_qgemm_int4o")
+    return y
+
+
+# ------------------------------------------------- device-resident weights
+
+class DeviceInt8:
+    """Device layout of one or more INT8 linears stacked along N (one launch).
+
+    ``parts`` is a list of (q int8 [N_i, K], scale) from woq_quantize_int8."""
+
+    def __init__(self, parts, device="cuda"):
+        import torch
+        K = parts[0][0].shape[1]
+        assert all(q.shape[1] == K for q, _ in parts) and len(parts) <= MAX_SEGMENTS
+        q = np.concatenate([p[0] for p in parts], axis=0) if len(parts) > 1 else parts[0][0]
+        self.N, self.K = q.shape
+        self.codes = torch.from_numpy(woq_layout_int8(q)).to(device)
+        self.desc = Int8W()
+        self.desc.codes = self.codes.data_ptr()
+        self.desc.N, self.desc.K, self.desc.nseg = self.N, K, len(parts)
+        end = 0
+        self.segments = []
+        for i, (qi, s) in enumerate(parts):
+            end += qi.shape[0]
+            self.desc.seg_end[i] = end
+            self.desc.seg_scale[i] = float(s)
+            self.segments.append((end - qi.shape[0], end))
+
+    @property
+    def nbytes(self):
+        return int(self.codes.numel())
+
+
+class DeviceInt4o:
+    """Device layout of one or more outlier-INT4 linears of one input space
+    stacked along N.  ``parts`` is a list of (packed, scales, w_out) from
+    woq_quantize_int4o sharing the geometry ``g``."""
+
+    def __init__(self, parts, g: Int4oGeom, device="cuda"):
+        import torch
+        packed = np.concatenate([p[0] for p in parts]) if len(parts) > 1 else parts[0][0]
+        scales = np.concatenate([p[1] for p in parts]) if len(parts) > 1 else parts[0][1]
+        w_out = np.concatenate([p[2] for p in parts]) if len(parts) > 1 else parts[0][2]
+        self.N = packed.shape[0]
+        self.geom = g
+        dc, ds, dw = woq_layout_int4o(packed, scales, w_out, g)
+        self.codes = torch.from_numpy(dc).to(device)
+        self.scales = torch.from_numpy(ds.view(np.int16)).to(device)
+        self.w_out = torch.from_numpy(dw.view(np.int16)).to(device) if dw.size else None
+        self.desc = Int4oW()
+        self.desc.codes = self.codes.data_ptr()
+        self.desc.scales = self.scales.data_ptr()
+        self.desc.w_out = self.w_out.data_ptr() if self.w_out is not None else None
+        self.desc.N = self.N
+        self.desc.geom = g
+        self.segments = []
+        end = 0
+        for p in parts:
+            self.segments.append((end, end + p[0].shape[0]))
+            end += p[0].shape[0]
+
+
+# ------------------------------------------------------------- stack runner
+
+class Stack:
+    """Owns a woq_stack built from a list of StackStep (weights stay owned by
+    the caller, who must keep them alive)."""
+
+    def __init__(self, steps, max_b: int):
+        self.steps = (StackStep * len(steps))(*steps)
+        self.n = len(steps)
+        h = c_void_p()
+        _check(_lib().woq_stack_create(self.steps, self.n, max_b, ctypes.byref(h)), "woq_stack_create")
+        self.handle = h
+
+    @staticmethod
+    def _ptrs(tensors):
+        return (c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+    def bind(self, inputs, outputs):
+        """Fix the input/output slot tensors (keeps references)."""
+        self._in, self._out = list(inputs), list(outputs)
+        self._pin, self._pout = self._ptrs(self._in), self._ptrs(self._out)
+
+    def run(self, b: int, stream=None):
+        _check(_lib().woq_stack_run(self.handle, self._pin, self._pout, b, _stream(stream)), "woq_stack_run")
+
+    def time(self, b: int, iters: int, stream=None):
+        step_ms = (c_float * max(1, self.n))()
+        pass_ms = c_float()
+        _check(_lib().woq_stack_time(self.handle, self._pin, self._pout, b, _stream(stream), iters, step_ms,
+                                     ctypes.byref(pass_ms)), "woq_stack_time")
+        return [step_ms[i] for i in range(self.n)], pass_ms.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _check(_lib().woq_stack_destroy(self.handle), "woq_stack_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def step_int4o(dev: "DeviceInt4o", perm_dev, in_slot: int, out_slot: int) -> StackStep:
+    st = StackStep()
+    st.fmt, st.in_slot, st.out_slot = FMT_INT4O, in_slot, out_slot
+    st.w4 = dev.desc
+    st.perm = perm_dev.data_ptr()
+    return st
+
+
+def step_int8(dev: "DeviceInt8", in_slot: int, out_slot: int) -> StackStep:
+    st = StackStep()
+    st.fmt, st.in_slot, st.out_slot = FMT_INT8, in_slot, out_slot
+    st.w8 = dev.desc
+    return st
