@@ -46,7 +46,11 @@ def int8_case(W_parts, x):
     run the kernel, and return (y_gpu, y_oracle)."""
     parts = [woq.woq_quantize_int8(W) for W in W_parts]
     dw = woq.DeviceInt8(parts)
-    xd = _dev(x)
+    # the ABI wants a leading dimension that is a multiple of 8 fp16 values
+    K = x.shape[1]
+    xpad = np.zeros((x.shape[0], -(-K // 8) * 8), np.float16)
+    xpad[:, :K] = x
+    xd = _dev(xpad)
     y = _empty16(x.shape[0], dw.N)
     woq.woq_qgemv_int8(dw.desc, xd, y)
     ref = np.concatenate([O.linear_int8(*O.quantize_int8(W), x) for W in W_parts], axis=1)

@@ -426,7 +426,7 @@ void launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
 
 int check_int4o_w(const woq_int4o_w* w) {
     if (!w || w->N < 0 || !woq::int4o_geom_valid(&w->geom)) return WOQ_EINVAL;
-    if (w->N > 0 && (!w->codes || !w->scales || (w->geom.n_out8 && !w->w_out))) return WOQ_EINVAL;
+    if (w->N > 0 && ((w->geom.G4 && (!w->codes || !w->scales)) || (w->geom.n_out8 && !w->w_out))) return WOQ_EINVAL;
     if (!woq::aligned16(w->codes) || !woq::aligned16(w->w_out) || (((uintptr_t)w->scales) & 7u)) return WOQ_EALIGN;
     if (w->N > (int64_t)INT32_MAX - 64 || w->geom.xp_len > (int64_t)INT32_MAX / 64) return WOQ_EUNSUPPORTED;
     return WOQ_OK;

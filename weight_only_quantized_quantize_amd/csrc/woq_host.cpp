@@ -353,7 +353,7 @@ int woq_int4o_dev_sizes(int64_t N, const woq_int4o_geom* g, int64_t* codes_bytes
 int woq_layout_int4o(const uint8_t* packed, const uint16_t* scales, const uint16_t* w_out, int64_t N,
                      const woq_int4o_geom* g, uint8_t* dev_codes, uint16_t* dev_scales, uint16_t* dev_wout) {
     if (N < 0 || !woq::int4o_geom_valid(g)) return WOQ_EINVAL;
-    if (!dev_codes || !dev_scales || (g->n_out8 && !dev_wout)) return WOQ_EINVAL;
+    if ((g->G4 && (!dev_codes || !dev_scales)) || (g->n_out8 && !dev_wout)) return WOQ_EINVAL;
     if (N > 0 && ((g->G && (!packed || !scales)) || (g->n_out && !w_out))) return WOQ_EINVAL;
     const int64_t N4 = woq::round_up(N, 4), G = g->G, G4 = g->G4, half = g->K_pad / 2;
     parallel_for(
