@@ -56,6 +56,7 @@ extern "C" {
 #define WOQ_EHIP         (-4)  /* a HIP call failed; woq_last_hip_error() gives its code */
 #define WOQ_EUNSUPPORTED (-5)  /* valid request that this build does not implement */
 #define WOQ_ERANGE       (-6)  /* value not representable: non-finite weight, fp16 scale overflow */
+#define WOQ_ETIMEOUT     (-7)  /* a fused stack run gave up waiting at a step boundary */
 
 #define WOQ_ABI_VERSION 1
 
@@ -286,6 +287,32 @@ int woq_stack_run(woq_stack* st, const uint16_t* const* inputs, uint16_t* const*
  */
 int woq_stack_time(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
                    void* stream, int32_t iters, float* step_ms, float* pass_ms);
+
+/*
+ * The same pass as woq_stack_run in ONE persistent kernel launch: every
+ * workgroup stays resident (cooperative launch), steps run in order, and a
+ * device-side barrier separates consecutive steps, so no step starts its
+ * products before every workgroup has finished the previous step.  Each step
+ * stages its activations (gathered through the permutation for INT4O) in LDS.
+ * Supports INT8 with b <= 8 and INT4O with b <= 7; other cases return
+ * WOQ_EUNSUPPORTED (use woq_stack_run).  The barrier counters live in the
+ * runner and are reset by the kernel itself before it exits, so consecutive
+ * runs on one stream need no host action.  Runs of one runner must not
+ * overlap (same stream, or synchronise).  A barrier that waits longer than a
+ * fixed bound makes every workgroup exit early; woq_stack_check reports it.
+ */
+int woq_stack_run_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                        void* stream);
+
+/* Synchronise `stream`; WOQ_ETIMEOUT if a fused run since the last check gave
+ * up at a barrier (the flag is cleared), WOQ_OK otherwise. */
+int woq_stack_check(woq_stack* st, void* stream);
+
+/* woq_stack_run_fused repeated `iters` times, each launch bracketed by a pair
+ * of HIP events on `stream`; *pass_ms = mean launch duration.  Synchronises,
+ * then reports like woq_stack_check. */
+int woq_stack_time_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                         void* stream, int32_t iters, float* pass_ms);
 
 /* Release the runner and its workspace (after the stream has finished). */
 int woq_stack_destroy(woq_stack* st);

@@ -1,0 +1,153 @@
+"""GPU tests of the layer-stack runner (per-launch and fused persistent pass).
+
+Both passes use the same per-quad arithmetic, so their outputs must agree bit
+for bit; both are also checked against the oracle, whose weights and
+permutations are computed by the oracle itself from the same seeded inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from weight_only_quantized_quantize_amd import woq
+from weight_only_quantized_quantize_amd.stack import GROUPS, ResidentStack
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _case(*a):
+    print("case:", *a, flush=True)
+
+
+def build(spec, layers=None):
+    return ResidentStack(spec, lambda l, lin, out: synth.weight(spec, l, lin, out=out),
+                         lambda s: synth.profile(spec, s), layers=layers)
+
+
+def io(spec, rs, b):
+    import torch
+    ins, outs = [], []
+    for layer in range(rs.n_layers):
+        for names, inp in GROUPS:
+            ins.append(torch.from_numpy(synth.decode_input(spec, layer, inp, b)).cuda())
+            outs.append(torch.full((b, sum(spec.linear(n).N for n in names)), 7.0, dtype=torch.float16,
+                                   device="cuda"))
+    return ins, outs
+
+
+def oracle_perms(spec):
+    perms = {}
+    for space in synth.SPACES:
+        K = spec.space_width(space)
+        cs = np.zeros(K)
+        for layer in range(spec.layers):
+            for lin in spec.linears():
+                if lin.space == space:
+                    cs += O.column_abs_sum(synth.weight(spec, layer, lin))
+        perms[space] = O.global_perm(K, O.select_outliers(O.outlier_scores(cs, synth.profile(spec, space)),
+                                                          O.n_outliers(K)))
+    return perms
+
+
+def oracle_group(spec, perms, layer, names, inp, b, rows=None):
+    x = synth.decode_input(spec, layer, inp, b)
+    ys = []
+    for n in names:
+        lin = spec.linear(n)
+        W = synth.weight(spec, layer, lin)
+        if spec.fmt == "int4o":
+            perm = perms[lin.space]
+            n_out = O.n_outliers(lin.K)
+            c, s, wo = O.quantize_int4o(W if rows is None else W[rows[n]], perm, n_out)
+            x_bg, x_out = O.permute_split(x, perm, n_out)
+            ys.append(O.linear_int4o(c, s, wo, x_bg, x_out))
+        else:
+            q, s = O.quantize_int8(W, rows=None if rows is None else rows[n])
+            ys.append(O.linear_int8(q, s, x))
+    return np.concatenate(ys, axis=1)
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg,b", [(2, 1), (2, 3), (2, 7), (3, 1), (3, 4), (3, 8)])
+def test_small_stack_fused_equals_launches_and_oracle(gpu_lib, cfg, b):
+    _case("small stack", cfg, b)
+    spec = synth.small_stack_spec(cfg, layers=3, batches=(b,))
+    rs = build(spec)
+    ins, outs = io(spec, rs, b)
+    runner = rs.make_runner(b)
+    runner.bind(ins, outs)
+    runner.run(b)
+    ref_launch = [host(t).copy() for t in outs]
+    for t in outs:
+        t.fill_(7.0)
+    for _ in range(3):                       # repeated runs: the barrier counters reset themselves
+        runner.run_fused(b)
+    runner.check()
+    fused = [host(t) for t in outs]
+    for i, (a, f) in enumerate(zip(ref_launch, fused)):
+        np.testing.assert_array_equal(a.view(np.uint16), f.view(np.uint16), err_msg=f"step {i}")
+    perms = oracle_perms(spec) if spec.fmt == "int4o" else None
+    for layer in range(spec.layers):
+        for gi, (names, inp) in enumerate(GROUPS):
+            ref = oracle_group(spec, perms, layer, names, inp, b)
+            err = O.normwise_rel_err(fused[4 * layer + gi].astype(np.float64), ref)
+            print(f"layer {layer} {'|'.join(names)}: {err:.3e}", flush=True)
+            assert err <= TOL
+
+
+def test_config2_stack_fused_full_size(gpu_lib):
+    """The 3B-shaped INT4O stack at full size, batch 1: the fused pass equals the
+    per-launch pass bit for bit on every output, and sampled rows of layers 0 and
+    27 match the oracle (the permutations are the planted sets, which selection
+    recovers)."""
+    spec = synth.stack_spec(2)
+    _case("config 2 full stack")
+    rs = build(spec)
+    for sp in synth.SPACES:
+        K = spec.space_width(sp)
+        np.testing.assert_array_equal(np.sort(rs.perm_host[sp][-O.n_outliers(K):]), synth.planted_set(spec, sp))
+    ins, outs = io(spec, rs, 1)
+    runner = rs.make_runner(1)
+    runner.bind(ins, outs)
+    runner.run(1)
+    ref_launch = [host(t).copy() for t in outs]
+    runner.run_fused(1)
+    runner.check()
+    for i, t in enumerate(outs):
+        np.testing.assert_array_equal(ref_launch[i].view(np.uint16), host(t).view(np.uint16), err_msg=f"step {i}")
+    perms = {sp: O.global_perm(spec.space_width(sp), synth.planted_set(spec, sp)) for sp in synth.SPACES}
+    rng = np.random.default_rng(2)
+    for layer in (0, spec.layers - 1):
+        for gi, (names, inp) in enumerate(GROUPS):
+            rows = {n: np.sort(rng.choice(spec.linear(n).N, 16, replace=False)) for n in names}
+            ref = oracle_group(spec, perms, layer, names, inp, 1, rows)
+            offs, cols = 0, []
+            for n in names:
+                cols.extend(offs + rows[n])
+                offs += spec.linear(n).N
+            got = host(outs[4 * layer + gi])[:, cols].astype(np.float64)
+            err = O.normwise_rel_err(got, ref)
+            print(f"layer {layer} {'|'.join(names)}: {err:.3e}", flush=True)
+            assert err <= TOL
+
+
+def test_fused_unsupported_batch_falls_back(gpu_lib):
+    spec = synth.small_stack_spec(2, layers=1, batches=(8,))
+    rs = build(spec)
+    ins, outs = io(spec, rs, 8)
+    runner = rs.make_runner(8)
+    runner.bind(ins, outs)
+    with pytest.raises(woq.WoqError) as e:
+        runner.run_fused(8)
+    assert e.value.status == woq.WOQ_EUNSUPPORTED
+    runner.run(8)                          # the per-launch pass takes the matrix-core kernel
+    perms = oracle_perms(spec)
+    ref = oracle_group(spec, perms, 0, ("q", "k", "v"), 0, 8)
+    assert O.normwise_rel_err(host(outs[0]).astype(np.float64), ref) <= TOL

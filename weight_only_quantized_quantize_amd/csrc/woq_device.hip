@@ -24,6 +24,7 @@
 // partial products added into one FP16 output).
 #include <hip/hip_runtime.h>
 
+#include "woq_gemv.cuh"
 #include "woq_internal.h"
 
 namespace woq {
@@ -35,55 +36,7 @@ extern "C" int woq_last_hip_error(void) { return woq::g_last_hip_error; }
 
 namespace {
 
-typedef _Float16 f16;
-typedef f16 h2 __attribute__((ext_vector_type(2)));
-typedef f16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
-__device__ __forceinline__ float h_to_f(uint16_t v) { return (float)__builtin_bit_cast(f16, v); }
-__device__ __forceinline__ uint16_t f_to_h(float v) { return __builtin_bit_cast(uint16_t, (f16)v); }
-
-__device__ __forceinline__ float dot2(h2 a, h2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// Streamed 16-byte load: weight bytes are read exactly once, so they are
-// marked non-temporal and do not push the shared activations out of cache.
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// fp16 pairs from an INT4O device dword (see woq_layout_int4o): returns the
-// two unscaled pairs (channels 4e+0,1 and 4e+2,3 of the half-chunk) and the
-// two pairs that carry 16 x code (channels 8+4e+0,1 and 8+4e+2,3).
-struct Int4Pairs {
-    h2 lo0, lo1, hi0, hi1;
-};
-__device__ __forceinline__ Int4Pairs int4_pairs(uint32_t w) {
-    const h2 off_lo = {(f16)1032.0f, (f16)1032.0f};   // 1024 + 8
-    const h2 off_hi = {(f16)1152.0f, (f16)1152.0f};   // 1024 + 16 * 8
-    uint32_t s = w >> 8;
-    Int4Pairs p;
-    p.lo0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - off_lo;
-    p.lo1 = as_h2((s & 0x000F000Fu) | 0x64006400u) - off_lo;
-    p.hi0 = as_h2((w & 0x00F000F0u) | 0x64006400u) - off_hi;
-    p.hi1 = as_h2((s & 0x00F000F0u) | 0x64006400u) - off_hi;
-    return p;
-}
-
-// fp16 pairs (channels 0,1 and 2,3) of an INT8 device dword (offset binary).
-__device__ __forceinline__ void int8_pairs(uint32_t w, h2& a, h2& b) {
-    const h2 off = {(f16)1152.0f, (f16)1152.0f};      // 1024 + 128
-    a = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00050004u)) - off;
-    b = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00070006u)) - off;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
+using namespace woqk;
 
 // ------------------------------------------------------------ permute/split
 
@@ -119,87 +72,10 @@ __global__ __launch_bounds__(64) void qgemv_int4o_valu(Int4oArgs a) {
     const int lane = threadIdx.x;
     const int quad = blockIdx.x;
     const int CPR = a.G4 * 4;
-    const uint4* w0 = a.codes + (int64_t)quad * 4 * CPR;
     float acc[4][B];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-
-#pragma unroll 2
-    for (int cc = lane; cc < CPR; cc += 64) {
-        uint4 w[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = load_stream(w0 + r * CPR + cc);
-        const uint2 sc = a.scales[(int64_t)quad * a.G4 + (cc >> 2)];
-        uint4 xv[B][4];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const uint4* xs = reinterpret_cast<const uint4*>(a.xp + (int64_t)b * a.xp_len + 32 * cc);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xv[b][j] = xs[j];
-        }
-        const float s[4] = {h_to_f((uint16_t)(sc.x & 0xFFFF)), h_to_f((uint16_t)(sc.x >> 16)),
-                            h_to_f((uint16_t)(sc.y & 0xFFFF)), h_to_f((uint16_t)(sc.y >> 16))};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
-            Int4Pairs p[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d]);
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                // x pairs of channels 0..15 (xv[b][0..1]) and 16..31 (xv[b][2..3])
-                const uint32_t xw[16] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
-                                         xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w,
-                                         xv[b][2].x, xv[b][2].y, xv[b][2].z, xv[b][2].w,
-                                         xv[b][3].x, xv[b][3].y, xv[b][3].z, xv[b][3].w};
-                float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-                for (int P = 0; P < 2; ++P) {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const Int4Pairs& q = p[2 * P + e];
-                        lo = dot2(q.lo0, as_h2(xw[8 * P + 2 * e + 0]), lo);
-                        lo = dot2(q.lo1, as_h2(xw[8 * P + 2 * e + 1]), lo);
-                        hi = dot2(q.hi0, as_h2(xw[8 * P + 4 + 2 * e + 0]), hi);
-                        hi = dot2(q.hi1, as_h2(xw[8 * P + 4 + 2 * e + 1]), hi);
-                    }
-                }
-                acc[r][b] = fmaf(s[r], fmaf(hi, 0.0625f, lo), acc[r][b]);
-            }
-        }
-    }
-
-    // FP16 outlier columns: 8 per 16-byte chunk
-    const uint16_t* xo_base = a.xp + 128 * a.G4;
-    for (int oc = lane; oc < a.no8; oc += 64) {
-        uint4 wo[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wo[r] = a.wout[((int64_t)quad * 4 + r) * a.no8 + oc];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const uint4 xo = *reinterpret_cast<const uint4*>(xo_base + (int64_t)b * a.xp_len + 8 * oc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float t = acc[r][b];
-                t = dot2(as_h2(wo[r].x), as_h2(xo.x), t);
-                t = dot2(as_h2(wo[r].y), as_h2(xo.y), t);
-                t = dot2(as_h2(wo[r].z), as_h2(xo.z), t);
-                t = dot2(as_h2(wo[r].w), as_h2(xo.w), t);
-                acc[r][b] = t;
-            }
-        }
-    }
-
-    float out = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            float v = wave_sum(acc[r][b]);
-            if (lane == r * B + b) out = v;
-        }
+    int4o_quad<B>(a.codes + (int64_t)quad * 4 * CPR, CPR, a.scales + (int64_t)quad * a.G4,
+                  a.wout + (int64_t)quad * 4 * a.no8, a.no8, a.xp, a.xp_len, 128 * a.G4, lane, acc);
+    const float out = quad_reduce<B>(acc, lane);
     if (lane < 4 * B) {
         const int r = lane / B, b = lane % B;
         const int n = quad * 4 + r;
@@ -225,11 +101,7 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
     const uint4* w0 = a.codes + (int64_t)quad * 4 * a.CPR;
     const int nchunks = (a.K + 15) >> 4;   // chunks that hold real columns
     float acc[4][B];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-
+    zero_acc(acc);
 #pragma unroll 2
     for (int cc = lane; cc < nchunks; cc += 64) {
         uint4 w[4];
@@ -247,40 +119,21 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
         } else {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                uint16_t t[16];
+                uint32_t t[8];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) t[j] = (k0 + j < a.K) ? a.x[(int64_t)b * a.ldx + k0 + j] : (uint16_t)0;
-                xv[b][0] = make_uint4(t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16));
-                xv[b][1] = make_uint4(t[8] | (t[9] << 16), t[10] | (t[11] << 16), t[12] | (t[13] << 16),
-                                      t[14] | (t[15] << 16));
+                for (int j = 0; j < 8; ++j) {
+                    const int k = k0 + 2 * j;
+                    const uint32_t lo = (k < a.K) ? a.x[(int64_t)b * a.ldx + k] : 0u;
+                    const uint32_t hi = (k + 1 < a.K) ? a.x[(int64_t)b * a.ldx + k + 1] : 0u;
+                    t[j] = lo | (hi << 16);
+                }
+                xv[b][0] = make_uint4(t[0], t[1], t[2], t[3]);
+                xv[b][1] = make_uint4(t[4], t[5], t[6], t[7]);
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
-            h2 q[8];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) int8_pairs(wd[d], q[2 * d], q[2 * d + 1]);
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const uint32_t xw[8] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
-                                        xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w};
-                float t = acc[r][b];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) t = dot2(q[j], as_h2(xw[j]), t);
-                acc[r][b] = t;
-            }
-        }
+        int8_chunk<B>(w, xv, acc);
     }
-
-    float out = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            float v = wave_sum(acc[r][b]);
-            if (lane == r * B + b) out = v;
-        }
+    const float out = quad_reduce<B>(acc, lane);
     if (lane < 4 * B) {
         const int r = lane / B, b = lane % B;
         const int n = quad * 4 + r;

@@ -1,15 +1,155 @@
 // Decode-stack runner: drives a sequence of quantised linears on one stream.
 //
 // A decode step walks the layers in order; within a layer, linears that read
-// the same activation (q|k|v, gate|up) are stacked along N into one launch.
-// Each INT4O step first gathers its input through the input space's global
-// permutation into the runner's workspace, then launches the product.
+// the same activation (q|k|v, gate|up) are stacked along N into one product.
+//
+// Two ways to run a pass:
+//  * woq_stack_run: one launch per permutation and per product, stream-ordered.
+//  * woq_stack_run_fused: one persistent launch for the whole pass.  On this
+//    hardware a dependent launch costs several microseconds, comparable to the
+//    time it takes to stream one decode linear, so the fused pass keeps every
+//    workgroup resident and separates steps with a device-side barrier.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
 #include <new>
 #include <vector>
 
+#include "woq_gemv.cuh"
 #include "woq_internal.h"
+
+namespace {
+
+using namespace woqk;
+
+// A step as the persistent kernel sees it (device memory, read-only).
+struct DevStep {
+    const uint4* codes;
+    const uint2* scales;     // INT4O
+    const uint4* wout;       // INT4O
+    const int32_t* perm;     // INT4O
+    const uint16_t* x;
+    uint16_t* y;
+    int fmt, N, CPR, nchunks, G4, no8, xlen, K, K_bg, n_out, ldx, ldy, nseg;
+    int seg_end[WOQ_MAX_SEGMENTS];
+    float seg_scale[WOQ_MAX_SEGMENTS];
+};
+
+// Barrier state: one 128-byte line per counter.
+constexpr int SYNC_LINE = 16;                 // uint64 per line
+constexpr int SYNC_GROUPS = 8;
+constexpr int SYNC_TOP = 0, SYNC_GROUP0 = 1, SYNC_DEPART = 1 + SYNC_GROUPS, SYNC_ERR = 2 + SYNC_GROUPS;
+constexpr int SYNC_WORDS = (3 + SYNC_GROUPS) * SYNC_LINE;
+constexpr int FUSED_THREADS = 512;
+// polls of s_sleep(2) before a barrier is declared stuck (far above any step)
+constexpr unsigned SPIN_LIMIT = 1u << 24;
+
+typedef unsigned long long u64;
+
+__device__ __forceinline__ u64 ld_relaxed(u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_relaxed(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ u64 add_relaxed(u64* p, u64 v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrive at barrier j (1-based) and wait until every workgroup has arrived.
+// Two levels: workgroups count into one of ng group counters, the last arrival
+// of a group bumps the top counter, everyone polls the top counter.  The
+// steps order computation only (no step reads another step's outputs), so the
+// counters need no memory fences.  Returns false if the wait gave up.
+__device__ bool grid_barrier(u64* sync, unsigned ng, u64 j) {
+    const unsigned P = gridDim.x;
+    const unsigned g = blockIdx.x % ng;
+    const u64 gsize = P / ng + (g < P % ng ? 1 : 0);
+    u64* top = sync + SYNC_TOP * SYNC_LINE;
+    u64* grp = sync + (SYNC_GROUP0 + g) * SYNC_LINE;
+    u64* err = sync + SYNC_ERR * SYNC_LINE;
+    const u64 old = add_relaxed(grp, 1ull);
+    if (old + 1 == j * gsize) add_relaxed(top, 1ull);
+    unsigned n = 0;
+    while (ld_relaxed(top) < j * ng) {
+        if (ld_relaxed(err)) return false;
+        __builtin_amdgcn_s_sleep(2);
+        if (++n > SPIN_LIMIT) {
+            st_relaxed(err, 1ull);
+            return false;
+        }
+    }
+    return true;
+}
+
+template <int B>
+__global__ __launch_bounds__(FUSED_THREADS) void stack_fused(const DevStep* __restrict__ steps, int nsteps, u64* sync) {
+    extern __shared__ __align__(16) uint16_t xs[];   // [B][xlen] staged activations
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nwv = blockDim.x >> 6;
+    const int gw = blockIdx.x * nwv + (tid >> 6);
+    const int NW = gridDim.x * nwv;
+    const unsigned ng = gridDim.x < (unsigned)SYNC_GROUPS ? gridDim.x : (unsigned)SYNC_GROUPS;
+    bool ok = true;
+    for (int si = 0; si < nsteps && ok; ++si) {
+        const DevStep& st = steps[si];
+        const int fmt = st.fmt, xlen = st.xlen;
+        // stage activations in LDS (zero-padded; INT4O gathered through perm)
+        if (fmt == WOQ_FMT_INT4O) {
+            const int bg = 128 * st.G4;
+            for (int b = 0; b < B; ++b)
+                for (int k = tid; k < xlen; k += blockDim.x) {
+                    int src = -1;
+                    if (k < st.K_bg) src = st.perm[k];
+                    else if (k >= bg && k - bg < st.n_out) src = st.perm[st.K_bg + (k - bg)];
+                    xs[b * xlen + k] = ((unsigned)src < (unsigned)st.K) ? st.x[(int64_t)b * st.ldx + src] : (uint16_t)0;
+                }
+        } else {
+            for (int b = 0; b < B; ++b)
+                for (int k = tid; k < xlen; k += blockDim.x)
+                    xs[b * xlen + k] = (k < st.K) ? st.x[(int64_t)b * st.ldx + k] : (uint16_t)0;
+        }
+        __syncthreads();
+        const int quads = (st.N + 3) >> 2;
+        for (int q = gw; q < quads; q += NW) {
+            float acc[4][B];
+            float scale = 1.0f;
+            if (fmt == WOQ_FMT_INT4O) {
+                int4o_quad<B>(st.codes + (int64_t)q * 4 * st.CPR, st.CPR, st.scales + (int64_t)q * st.G4,
+                              st.wout + (int64_t)q * 4 * st.no8, st.no8, xs, xlen, 128 * st.G4, lane, acc);
+            } else {
+                int8_quad_padded<B>(st.codes + (int64_t)q * 4 * st.CPR, st.CPR, st.nchunks, xs, xlen, lane, acc);
+            }
+            const float out = quad_reduce<B>(acc, lane);
+            if (lane < 4 * B) {
+                const int r = lane / B, b = lane % B;
+                const int n = 4 * q + r;
+                if (n < st.N) {
+                    if (fmt == WOQ_FMT_INT8) {
+                        scale = st.seg_scale[st.nseg - 1];
+                        for (int i = st.nseg - 1; i >= 0; --i)
+                            if (n < st.seg_end[i]) scale = st.seg_scale[i];
+                    }
+                    st.y[(int64_t)b * st.ldy + n] = f_to_h(out * scale);
+                }
+            }
+        }
+        __syncthreads();  // LDS is rewritten by the next step
+        if (si + 1 < nsteps) {
+            int stuck = 0;
+            if (tid == 0) stuck = grid_barrier(sync, ng, (u64)(si + 1)) ? 0 : 1;
+            ok = __syncthreads_or(stuck) == 0;
+        }
+    }
+    // The last workgroup to leave resets the counters for the next run; by
+    // then every workgroup has passed its last barrier poll.
+    if (tid == 0) {
+        u64* depart = sync + SYNC_DEPART * SYNC_LINE;
+        if (add_relaxed(depart, 1ull) + 1 == gridDim.x) {
+            st_relaxed(sync + SYNC_TOP * SYNC_LINE, 0ull);
+            for (int g = 0; g < SYNC_GROUPS; ++g) st_relaxed(sync + (SYNC_GROUP0 + g) * SYNC_LINE, 0ull);
+            st_relaxed(depart, 0ull);
+        }
+    }
+}
+
+}  // namespace
 
 struct woq_stack {
     std::vector<woq_stack_step> steps;
@@ -17,45 +157,22 @@ struct woq_stack {
     int64_t xp_elems = 0;      // per workspace row
     uint16_t* xp = nullptr;    // [max_b][xp_elems]
     int device = 0;
+    // fused pass
+    DevStep* dsteps = nullptr;             // device step table
+    std::vector<DevStep> hsteps;           // host copy (pointers of the last bound inputs/outputs)
+    u64* sync = nullptr;
+    int max_xlen = 0;
+    int grid = 0;
+    bool fused_ok = true;                  // every step supported by the fused kernel
 };
 
-extern "C" {
-
-int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b, woq_stack** out) {
-    if (!out || n_steps < 0 || (n_steps > 0 && !steps) || max_b < 1 || max_b > 64) return WOQ_EINVAL;
-    *out = nullptr;
-    int64_t xp_elems = 8;
-    int max_slot = 0;
-    for (int i = 0; i < n_steps; ++i) {
-        const woq_stack_step& s = steps[i];
-        if (s.in_slot < 0 || s.out_slot < 0) return WOQ_EINVAL;
-        max_slot = std::max(max_slot, std::max(s.in_slot, s.out_slot));
-        if (s.fmt == WOQ_FMT_INT4O) {
-            if (!woq::int4o_geom_valid(&s.w4.geom) || !s.perm) return WOQ_EINVAL;
-            xp_elems = std::max(xp_elems, s.w4.geom.xp_len);
-        } else if (s.fmt == WOQ_FMT_INT8) {
-            if (max_b > 8) return WOQ_EUNSUPPORTED;
-        } else {
-            return WOQ_EINVAL;
-        }
-    }
-    woq_stack* st = new (std::nothrow) woq_stack;
-    if (!st) return WOQ_ENOMEM;
-    st->steps.assign(steps, steps + n_steps);
-    st->max_b = max_b;
-    st->xp_elems = xp_elems;
-    hipError_t e = hipGetDevice(&st->device);
-    if (e == hipSuccess) e = hipMalloc((void**)&st->xp, (size_t)(max_b * xp_elems * 2));
-    if (e != hipSuccess) {
-        woq::set_hip_error((int)e);
-        delete st;
-        return e == hipErrorOutOfMemory ? WOQ_ENOMEM : WOQ_EHIP;
-    }
-    *out = st;
-    return WOQ_OK;
-}
-
 namespace {
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return WOQ_OK;
+    woq::set_hip_error((int)e);
+    return e == hipErrorOutOfMemory ? WOQ_ENOMEM : WOQ_EHIP;
+}
 
 // One pass over the steps; ev (2 per step) brackets each product launch.
 int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b, void* stream,
@@ -81,7 +198,165 @@ int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outp
     return WOQ_OK;
 }
 
+template <int B>
+const void* fused_kernel() {
+    return reinterpret_cast<const void*>(&stack_fused<B>);
+}
+
+const void* fused_kernel_for(int64_t b) {
+    switch (b) {
+        case 1: return fused_kernel<1>();
+        case 2: return fused_kernel<2>();
+        case 3: return fused_kernel<3>();
+        case 4: return fused_kernel<4>();
+        case 5: return fused_kernel<5>();
+        case 6: return fused_kernel<6>();
+        case 7: return fused_kernel<7>();
+        default: return fused_kernel<8>();
+    }
+}
+
+// Upload the step table if the bound inputs/outputs changed.
+int bind_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, void* stream) {
+    bool changed = false;
+    for (size_t i = 0; i < st->steps.size(); ++i) {
+        const woq_stack_step& s = st->steps[i];
+        DevStep& d = st->hsteps[i];
+        if (d.x != inputs[s.in_slot] || d.y != outputs[s.out_slot]) {
+            d.x = inputs[s.in_slot];
+            d.y = outputs[s.out_slot];
+            changed = true;
+        }
+    }
+    if (!changed) return WOQ_OK;
+    // the previous table may still be in use by queued runs on this stream
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess)
+        e = hipMemcpy(st->dsteps, st->hsteps.data(), sizeof(DevStep) * st->hsteps.size(), hipMemcpyHostToDevice);
+    return hip_status(e);
+}
+
+int launch_fused(woq_stack* st, int64_t b, void* stream) {
+    const int nsteps = (int)st->steps.size();
+    size_t lds = (size_t)b * st->max_xlen * 2;
+    void* args[] = {&st->dsteps, (void*)&nsteps, &st->sync};
+    hipError_t e = hipLaunchCooperativeKernel(fused_kernel_for(b), dim3(st->grid), dim3(FUSED_THREADS), args,
+                                              (unsigned)lds, (hipStream_t)stream);
+    return hip_status(e);
+}
+
+int prepare_fused(woq_stack* st, int64_t b) {
+    if (!st->fused_ok) return WOQ_EUNSUPPORTED;
+    for (const woq_stack_step& s : st->steps)
+        if ((s.fmt == WOQ_FMT_INT4O && b > 7) || b > 8) return WOQ_EUNSUPPORTED;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, st->device);
+    if (e != hipSuccess) return hip_status(e);
+    const size_t lds = (size_t)b * st->max_xlen * 2;
+    if (lds > prop.sharedMemPerBlock) return WOQ_EUNSUPPORTED;
+    const void* k = fused_kernel_for(b);
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, FUSED_THREADS, lds);
+    if (e != hipSuccess) return hip_status(e);
+    if (per_cu < 1) return WOQ_EUNSUPPORTED;
+    st->grid = prop.multiProcessorCount;   // one resident workgroup per compute unit
+    return WOQ_OK;
+}
+
 }  // namespace
+
+extern "C" {
+
+int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b, woq_stack** out) {
+    if (!out || n_steps < 0 || (n_steps > 0 && !steps) || max_b < 1 || max_b > 64) return WOQ_EINVAL;
+    *out = nullptr;
+    int64_t xp_elems = 8;
+    int max_slot = 0;
+    for (int i = 0; i < n_steps; ++i) {
+        const woq_stack_step& s = steps[i];
+        if (s.in_slot < 0 || s.out_slot < 0) return WOQ_EINVAL;
+        max_slot = std::max(max_slot, std::max(s.in_slot, s.out_slot));
+        if (s.fmt == WOQ_FMT_INT4O) {
+            if (!woq::int4o_geom_valid(&s.w4.geom) || !s.perm) return WOQ_EINVAL;
+            xp_elems = std::max(xp_elems, s.w4.geom.xp_len);
+        } else if (s.fmt == WOQ_FMT_INT8) {
+            if (max_b > 8) return WOQ_EUNSUPPORTED;
+            if (s.w8.nseg < 1 || s.w8.nseg > WOQ_MAX_SEGMENTS || s.w8.K < 1) return WOQ_EINVAL;
+        } else {
+            return WOQ_EINVAL;
+        }
+    }
+    woq_stack* st = new (std::nothrow) woq_stack;
+    if (!st) return WOQ_ENOMEM;
+    st->steps.assign(steps, steps + n_steps);
+    st->max_b = max_b;
+    st->xp_elems = xp_elems;
+    // host step table of the fused pass
+    st->hsteps.resize(n_steps);
+    for (int i = 0; i < n_steps; ++i) {
+        const woq_stack_step& s = steps[i];
+        DevStep d;
+        std::memset(&d, 0, sizeof d);
+        d.fmt = s.fmt;
+        if (s.fmt == WOQ_FMT_INT4O) {
+            const woq_int4o_geom& g = s.w4.geom;
+            d.codes = (const uint4*)s.w4.codes;
+            d.scales = (const uint2*)s.w4.scales;
+            d.wout = (const uint4*)s.w4.w_out;
+            d.perm = s.perm;
+            d.N = (int)s.w4.N;
+            d.CPR = (int)(4 * g.G4);
+            d.G4 = (int)g.G4;
+            d.no8 = (int)(g.n_out8 / 8);
+            d.xlen = (int)g.xp_len;
+            d.K = (int)g.K;
+            d.K_bg = (int)g.K_bg;
+            d.n_out = (int)g.n_out;
+            d.ldx = (int)g.K;
+            d.ldy = (int)s.w4.N;
+            if (!woq::aligned16(s.w4.codes) || !woq::aligned16(s.w4.w_out) || ((uintptr_t)s.w4.scales & 7u))
+                st->fused_ok = false;
+        } else {
+            d.codes = (const uint4*)s.w8.codes;
+            d.N = (int)s.w8.N;
+            d.K = (int)s.w8.K;
+            d.CPR = (int)(woq::round_up(s.w8.K, 64) / 16);
+            d.nchunks = (int)woq::ceil_div(s.w8.K, 16);
+            d.xlen = 16 * d.nchunks;
+            d.ldx = (int)s.w8.K;
+            d.ldy = (int)s.w8.N;
+            d.nseg = s.w8.nseg;
+            for (int j = 0; j < WOQ_MAX_SEGMENTS; ++j) {
+                d.seg_end[j] = j < s.w8.nseg ? (int)s.w8.seg_end[j] : (int)s.w8.N;
+                d.seg_scale[j] = j < s.w8.nseg ? s.w8.seg_scale[j] : 0.0f;
+            }
+            if (!woq::aligned16(s.w8.codes)) st->fused_ok = false;
+        }
+        st->max_xlen = std::max(st->max_xlen, d.xlen);
+        st->hsteps[i] = d;
+    }
+    hipError_t e = hipGetDevice(&st->device);
+    if (e == hipSuccess) e = hipMalloc((void**)&st->xp, (size_t)(max_b * xp_elems * 2));
+    if (e == hipSuccess && n_steps > 0) e = hipMalloc((void**)&st->dsteps, sizeof(DevStep) * n_steps);
+    if (e == hipSuccess) e = hipMalloc((void**)&st->sync, sizeof(u64) * SYNC_WORDS);
+    if (e == hipSuccess) e = hipMemset(st->sync, 0, sizeof(u64) * SYNC_WORDS);
+    if (e == hipSuccess && n_steps > 0)
+        e = hipMemcpy(st->dsteps, st->hsteps.data(), sizeof(DevStep) * n_steps, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        int rc = hip_status(e);
+        hipFree(st->xp);
+        hipFree(st->dsteps);
+        hipFree(st->sync);
+        delete st;
+        return rc;
+    }
+    *out = st;
+    return WOQ_OK;
+}
 
 int woq_stack_run(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b, void* stream) {
     if (!st || !inputs || !outputs || b < 1 || b > st->max_b) return WOQ_EINVAL;
@@ -127,23 +402,82 @@ int woq_stack_time(woq_stack* st, const uint16_t* const* inputs, uint16_t* const
     for (auto& x : ev)
         if (x) hipEventDestroy(x);
     if (rc) return rc;
-    if (e != hipSuccess) {
-        woq::set_hip_error((int)e);
-        return WOQ_EHIP;
+    return hip_status(e);
+}
+
+int woq_stack_run_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                        void* stream) {
+    if (!st || !inputs || !outputs || b < 1 || b > st->max_b) return WOQ_EINVAL;
+    if (st->steps.empty()) return WOQ_OK;
+    int rc = prepare_fused(st, b);
+    if (rc) return rc;
+    rc = bind_fused(st, inputs, outputs, stream);
+    if (rc) return rc;
+    return launch_fused(st, b, stream);
+}
+
+int woq_stack_check(woq_stack* st, void* stream) {
+    if (!st) return WOQ_EINVAL;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    u64 err = 0;
+    e = hipMemcpy(&err, st->sync + SYNC_ERR * SYNC_LINE, sizeof err, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    if (err) {
+        // a run gave up: clear every counter (no kernel of this runner is in flight now)
+        e = hipMemset(st->sync, 0, sizeof(u64) * SYNC_WORDS);
+        if (e != hipSuccess) return hip_status(e);
+        return WOQ_ETIMEOUT;
     }
     return WOQ_OK;
+}
+
+int woq_stack_time_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                         void* stream, int32_t iters, float* pass_ms) {
+    if (!st || !inputs || !outputs || b < 1 || b > st->max_b || iters < 1 || !pass_ms) return WOQ_EINVAL;
+    int rc = prepare_fused(st, b);
+    if (rc) return rc;
+    rc = bind_fused(st, inputs, outputs, stream);
+    if (rc) return rc;
+    hipStream_t hs = (hipStream_t)stream;
+    std::vector<hipEvent_t> ev(2 * (size_t)iters, nullptr);
+    hipError_t e = hipSuccess;
+    for (auto& x : ev)
+        if (e == hipSuccess) e = hipEventCreate(&x);
+    for (int it = 0; it < iters && e == hipSuccess && rc == WOQ_OK; ++it) {
+        e = hipEventRecord(ev[2 * it], hs);
+        if (e == hipSuccess) rc = launch_fused(st, b, stream);
+        if (e == hipSuccess && rc == WOQ_OK) e = hipEventRecord(ev[2 * it + 1], hs);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    double total = 0.0;
+    for (int it = 0; it < iters && e == hipSuccess && rc == WOQ_OK; ++it) {
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, ev[2 * it], ev[2 * it + 1]);
+        total += ms;
+    }
+    for (auto& x : ev)
+        if (x) hipEventDestroy(x);
+    if (rc) return rc;
+    if (e != hipSuccess) return hip_status(e);
+    *pass_ms = (float)(total / iters);
+    return woq_stack_check(st, stream);
 }
 
 int woq_stack_destroy(woq_stack* st) {
     if (!st) return WOQ_OK;
     hipError_t e = hipSuccess;
     if (st->xp) e = hipFree(st->xp);
-    delete st;
-    if (e != hipSuccess) {
-        woq::set_hip_error((int)e);
-        return WOQ_EHIP;
+    if (st->dsteps) {
+        hipError_t e2 = hipFree(st->dsteps);
+        if (e == hipSuccess) e = e2;
     }
-    return WOQ_OK;
+    if (st->sync) {
+        hipError_t e2 = hipFree(st->sync);
+        if (e == hipSuccess) e = e2;
+    }
+    delete st;
+    return hip_status(e);
 }
 
 }  // extern "C"

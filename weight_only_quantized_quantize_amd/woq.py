@@ -18,7 +18,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwoq.so")
 
-WOQ_OK, WOQ_EINVAL, WOQ_EALIGN, WOQ_ENOMEM, WOQ_EHIP, WOQ_EUNSUPPORTED, WOQ_ERANGE = 0, -1, -2, -3, -4, -5, -6
+WOQ_OK, WOQ_EINVAL, WOQ_EALIGN, WOQ_ENOMEM, WOQ_EHIP, WOQ_EUNSUPPORTED, WOQ_ERANGE, WOQ_ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
 MAX_SEGMENTS = 8
 
 
@@ -81,6 +81,10 @@ _SIGS = {
     "woq_stack_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
     "woq_stack_time": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
                                POINTER(c_float), POINTER(c_float)]),
+    "woq_stack_run_fused": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
+    "woq_stack_check": (c_int, [c_void_p, c_void_p]),
+    "woq_stack_time_fused": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
+                                     POINTER(c_float)]),
     "woq_stack_destroy": (c_int, [c_void_p]),
 }
 
@@ -355,6 +359,19 @@ class Stack:
 
     def run(self, b: int, stream=None):
         _check(_lib().woq_stack_run(self.handle, self._pin, self._pout, b, _stream(stream)), "woq_stack_run")
+
+    def run_fused(self, b: int, stream=None):
+        _check(_lib().woq_stack_run_fused(self.handle, self._pin, self._pout, b, _stream(stream)),
+               "woq_stack_run_fused")
+
+    def check(self, stream=None):
+        _check(_lib().woq_stack_check(self.handle, _stream(stream)), "woq_stack_check")
+
+    def time_fused(self, b: int, iters: int, stream=None) -> float:
+        pass_ms = c_float()
+        _check(_lib().woq_stack_time_fused(self.handle, self._pin, self._pout, b, _stream(stream), iters,
+                                           ctypes.byref(pass_ms)), "woq_stack_time_fused")
+        return pass_ms.value
 
     def time(self, b: int, iters: int, stream=None):
         step_ms = (c_float * max(1, self.n))()
