@@ -97,7 +97,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4])
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="resident layers (default: all)")
-    ap.add_argument("--mode", choices=["fused", "launch"], default="fused",
+    ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
                     help="fused: one persistent launch per step; launch: one launch per permutation and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -46,11 +46,11 @@ __global__ void permute_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, co
     const uint16_t* xr = x + r * ldx;
     for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < xp_len; k += gridDim.x * blockDim.x) {
         int src = -1;
-        if (k < K_bg) src = perm[k];
-        else if (k >= bg_len && k - bg_len < n_out) src = perm[K_bg + (k - bg_len)];
+        if (k < K_bg) src = *gptr(perm + k);
+        else if (k >= bg_len && k - bg_len < n_out) src = *gptr(perm + K_bg + (k - bg_len));
         // an index outside [0, K) cannot come from a valid permutation; read 0
-        uint16_t v = ((unsigned)src < (unsigned)K) ? xr[src] : (uint16_t)0;
-        xp[r * xp_len + k] = v;
+        uint16_t v = ((unsigned)src < (unsigned)K) ? *gptr(xr + src) : (uint16_t)0;
+        *gptr(xp + r * xp_len + k) = v;
     }
 }
 
@@ -69,18 +69,27 @@ struct Int4oArgs {
 // chunks (a chunk = 32 background channels of one group).
 template <int B>
 __global__ __launch_bounds__(64) void qgemv_int4o_valu(Int4oArgs a) {
+    constexpr int U = B <= 4 ? 4 : 2;
     const int lane = threadIdx.x;
-    const int quad = blockIdx.x;
-    const int CPR = a.G4 * 4;
-    float acc[4][B];
-    int4o_quad<B>(a.codes + (int64_t)quad * 4 * CPR, CPR, a.scales + (int64_t)quad * a.G4,
-                  a.wout + (int64_t)quad * 4 * a.no8, a.no8, a.xp, a.xp_len, 128 * a.G4, lane, acc);
-    const float out = quad_reduce<B>(acc, lane);
-    if (lane < 4 * B) {
-        const int r = lane / B, b = lane % B;
-        const int n = quad * 4 + r;
-        if (n < a.N) a.y[(int64_t)b * a.ldy + n] = f_to_h(out);
-    }
+    QuadTask t;
+    t.codes = a.codes;
+    t.scales = a.scales;
+    t.wout = a.wout;
+    t.CPR = 4 * a.G4;
+    t.no8 = a.no8;
+    t.nchunks = t.CPR + t.no8;
+    t.IT = (t.nchunks + 63) >> 6;
+    t.q0 = blockIdx.x;
+    t.qstride = 1;
+    t.nq = 1;
+    Slots<U> slots;
+    prefetch_items<true, U>(t, lane, slots);
+    stream_task<true, B, U>(t, slots, (gx_ptr)a.xp, a.xp_len, 128 * a.G4, lane, U, [&](int q, float out) {
+        if (lane < 4 * B) {
+            const int r = lane / B, b = lane % B, n = 4 * q + r;
+            if (n < a.N) *gptr(a.y + (int64_t)b * a.ldy + n) = f_to_h(out);
+        }
+    });
 }
 
 // --------------------------------------------------------- INT8, batch <= 8
@@ -106,15 +115,15 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
     for (int cc = lane; cc < nchunks; cc += 64) {
         uint4 w[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = load_stream(w0 + r * a.CPR + cc);
+        for (int r = 0; r < 4; ++r) w[r] = gload_nt(w0 + r * a.CPR + cc);
         uint4 xv[B][2];
         const int k0 = 16 * cc;
         if (k0 + 16 <= a.K) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                const uint4* xs = reinterpret_cast<const uint4*>(a.x + (int64_t)b * a.ldx + k0);
-                xv[b][0] = xs[0];
-                xv[b][1] = xs[1];
+                const gx_ptr xs = (gx_ptr)(a.x + (int64_t)b * a.ldx + k0);
+                xv[b][0] = load_x16(xs);
+                xv[b][1] = load_x16(xs + 8);
             }
         } else {
 #pragma unroll
@@ -123,8 +132,8 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int k = k0 + 2 * j;
-                    const uint32_t lo = (k < a.K) ? a.x[(int64_t)b * a.ldx + k] : 0u;
-                    const uint32_t hi = (k + 1 < a.K) ? a.x[(int64_t)b * a.ldx + k + 1] : 0u;
+                    const uint32_t lo = (k < a.K) ? *gptr(a.x + (int64_t)b * a.ldx + k) : 0u;
+                    const uint32_t hi = (k + 1 < a.K) ? *gptr(a.x + (int64_t)b * a.ldx + k + 1) : 0u;
                     t[j] = lo | (hi << 16);
                 }
                 xv[b][0] = make_uint4(t[0], t[1], t[2], t[3]);
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
             float s = a.seg_scale[a.nseg - 1];
             for (int i = a.nseg - 1; i >= 0; --i)
                 if (n < a.seg_end[i]) s = a.seg_scale[i];
-            a.y[(int64_t)b * a.ldy + n] = f_to_h(out * s);
+            *gptr(a.y + (int64_t)b * a.ldy + n) = f_to_h(out * s);
         }
     }
 }
@@ -175,11 +184,12 @@ __global__ __launch_bounds__(256) void qgemm_int4o_mfma(Int4oArgs a, int b) {
     for (int t = 0; t < NBT; ++t) acc[t] = (f4){0.f, 0.f, 0.f, 0.f};
 
     for (int g = wave; g < a.G4; g += 4) {
-        uint4 w = row_ok ? load_stream(wrow + 4 * g + c) : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+        uint4 w = row_ok ? gload_nt(wrow + 4 * g + c) : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
         const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        const uint32_t bias = bias_reg();
         Int4Pairs p[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d]);
+        for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d], bias);
         // A operands of the four k-steps (8 fp16 each)
         h8 A[4];
 #pragma unroll
@@ -195,16 +205,16 @@ __global__ __launch_bounds__(256) void qgemm_int4o_mfma(Int4oArgs a, int b) {
         for (int i = 0; i < 4; ++i) {
             const int rr = 4 * c + i;      // D row held by this lane
             const int q = quad0 + (rr >> 2);
-            s[i] = (q * 4 < N4) ? h_to_f(reinterpret_cast<const uint16_t*>(a.scales)[((int64_t)q * a.G4 + g) * 4 + (rr & 3)]) : 0.0f;
+            s[i] = (q * 4 < N4) ? h_to_f(*gptr(reinterpret_cast<const uint16_t*>(a.scales) + ((int64_t)q * a.G4 + g) * 4 + (rr & 3))) : 0.0f;
         }
 #pragma unroll
         for (int t = 0; t < NBT; ++t) {
             const int col = t * 16 + m;    // batch column of the B operand
             h8 Bv[4];
             if (col < b) {
-                const uint4* xs = reinterpret_cast<const uint4*>(a.xp + (int64_t)col * a.xp_len + 128 * g + 32 * c);
+                const gx_ptr xs = (gx_ptr)(a.xp + (int64_t)col * a.xp_len + 128 * g + 32 * c);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Bv[j] = __builtin_bit_cast(h8, xs[j]);
+                for (int j = 0; j < 4; ++j) Bv[j] = __builtin_bit_cast(h8, load_x16(xs + 8 * j));
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Bv[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
@@ -226,13 +236,13 @@ __global__ __launch_bounds__(256) void qgemm_int4o_mfma(Int4oArgs a, int b) {
         const int col0 = 32 * st + 8 * c;
         h8 Av = (h8){0, 0, 0, 0, 0, 0, 0, 0};
         if (row_ok && col0 < n_o8)
-            Av = __builtin_bit_cast(h8, a.wout[(int64_t)row * a.no8 + (col0 >> 3)]);
+            Av = __builtin_bit_cast(h8, gload_u4(a.wout + (int64_t)row * a.no8 + (col0 >> 3)));
 #pragma unroll
         for (int t = 0; t < NBT; ++t) {
             const int bc = t * 16 + m;
             h8 Bv = (h8){0, 0, 0, 0, 0, 0, 0, 0};
             if (bc < b && col0 < n_o8)
-                Bv = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(xo_base + (int64_t)bc * a.xp_len + col0));
+                Bv = __builtin_bit_cast(h8, load_x16((gx_ptr)(xo_base + (int64_t)bc * a.xp_len + col0)));
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Bv, acc[t], 0, 0, 0);
         }
     }
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(256) void qgemm_int4o_mfma(Int4oArgs a, int b) {
         const int n = blockIdx.x * 16 + rr;
         if (bc < b && n < a.N) {
             float v = red[0][t][rr][col] + red[1][t][rr][col] + red[2][t][rr][col] + red[3][t][rr][col];
-            a.y[(int64_t)bc * a.ldy + n] = f_to_h(v);
+            *gptr(a.y + (int64_t)bc * a.ldy + n) = f_to_h(v);
         }
     }
 }

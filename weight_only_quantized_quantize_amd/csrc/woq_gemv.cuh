@@ -20,17 +20,54 @@ typedef f16 h2 __attribute__((ext_vector_type(2)));
 typedef f16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Address-space-qualified pointers.  Loads through generic pointers become
+// FLAT instructions, which count against the LDS wait counter as well and so
+// serialise LDS waits behind every outstanding weight load.
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+typedef __attribute__((address_space(3))) const u32x4 l_u32x4;
+typedef __attribute__((address_space(1))) const uint16_t* gx_ptr;   // activations in global memory
+typedef __attribute__((address_space(3))) const uint16_t* lx_ptr;   // activations staged in LDS
+
+// The same pointer in the global address space (for loads and stores that
+// must not become FLAT instructions).
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gptr(T* p) {
+    return (__attribute__((address_space(1))) T*)p;
+}
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ float h_to_f(uint16_t v) { return (float)__builtin_bit_cast(f16, v); }
 __device__ __forceinline__ uint16_t f_to_h(float v) { return __builtin_bit_cast(uint16_t, (f16)v); }
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
 
-// Streamed 16-byte load: weight bytes are read exactly once, so they are
-// marked non-temporal and do not push the shared activations out of cache.
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+
+// 16 bytes of activations (8 fp16), 16-byte aligned.
+__device__ __forceinline__ uint4 load_x16(gx_ptr p) { return as_uint4(*(g_u32x4*)p); }
+__device__ __forceinline__ uint4 load_x16(lx_ptr p) { return as_uint4(*(l_u32x4*)p); }
+// 16 and 8 bytes from global memory (cached).
+__device__ __forceinline__ uint4 gload_u4(const uint4* p) { return as_uint4(*(g_u32x4*)p); }
+__device__ __forceinline__ uint2 gload_u2(const uint2* p) {
+    u32x2 v = *(g_u32x2*)p;
+    return make_uint2(v[0], v[1]);
+}
+
+// Streamed 16-byte weight load: weight bytes are read exactly once, so they
+// are marked non-temporal and do not push the shared activations out of cache.
+__device__ __forceinline__ uint4 gload_nt(const uint4* p) {
+    return as_uint4(__builtin_nontemporal_load((g_u32x4*)p));
+}
+
+// The fp16 exponent bias 0x64006400 is kept in a VGPR: VOP3 instructions on
+// this target take no literal operands, and with the bias in a register each
+// pair costs a single v_and_or_b32 (mask from an SGPR) instead of an and + or.
+__device__ __forceinline__ uint32_t bias_reg() {
+    uint32_t v = 0x64006400u;
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 // fp16 pairs from an INT4O device dword (layout: see woq_layout_int4o):
@@ -39,15 +76,15 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 struct Int4Pairs {
     h2 lo0, lo1, hi0, hi1;
 };
-__device__ __forceinline__ Int4Pairs int4_pairs(uint32_t w) {
+__device__ __forceinline__ Int4Pairs int4_pairs(uint32_t w, uint32_t bias) {
     const h2 off_lo = {(f16)1032.0f, (f16)1032.0f};   // 1024 + 8
     const h2 off_hi = {(f16)1152.0f, (f16)1152.0f};   // 1024 + 16 * 8
     uint32_t s = w >> 8;
     Int4Pairs p;
-    p.lo0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - off_lo;
-    p.lo1 = as_h2((s & 0x000F000Fu) | 0x64006400u) - off_lo;
-    p.hi0 = as_h2((w & 0x00F000F0u) | 0x64006400u) - off_hi;
-    p.hi1 = as_h2((s & 0x00F000F0u) | 0x64006400u) - off_hi;
+    p.lo0 = as_h2((w & 0x000F000Fu) | bias) - off_lo;
+    p.lo1 = as_h2((s & 0x000F000Fu) | bias) - off_lo;
+    p.hi0 = as_h2((w & 0x00F000F0u) | bias) - off_hi;
+    p.hi1 = as_h2((s & 0x00F000F0u) | bias) - off_hi;
     return p;
 }
 
@@ -56,12 +93,6 @@ __device__ __forceinline__ void int8_pairs(uint32_t w, h2& a, h2& b) {
     const h2 off = {(f16)1152.0f, (f16)1152.0f};      // 1024 + 128
     a = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00050004u)) - off;
     b = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00070006u)) - off;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
 }
 
 template <int B>
@@ -73,25 +104,19 @@ __device__ __forceinline__ void zero_acc(float (&acc)[4][B]) {
 }
 
 // Dot products of one INT4O chunk (four rows, 32 channels) with B activation
-// rows; x points at channel 32 * cc of activation row 0, rows xs apart.
+// rows xv (32 fp16 each).
 template <int B>
-__device__ __forceinline__ void int4o_chunk(const uint4 (&w)[4], uint2 sc, const uint16_t* x, int xs,
+__device__ __forceinline__ void int4o_chunk(const uint4 (&w)[4], uint2 sc, const uint4 (&xv)[B][4],
                                             float (&acc)[4][B]) {
-    uint4 xv[B][4];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        const uint4* p = reinterpret_cast<const uint4*>(x + b * xs);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xv[b][j] = p[j];
-    }
     const float s[4] = {h_to_f((uint16_t)(sc.x & 0xFFFF)), h_to_f((uint16_t)(sc.x >> 16)),
                         h_to_f((uint16_t)(sc.y & 0xFFFF)), h_to_f((uint16_t)(sc.y >> 16))};
+    const uint32_t bias = bias_reg();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
         Int4Pairs p[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d]);
+        for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d], bias);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             const uint32_t xw[16] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
@@ -111,43 +136,6 @@ __device__ __forceinline__ void int4o_chunk(const uint4 (&w)[4], uint2 sc, const
                 }
             }
             acc[r][b] = fmaf(s[r], fmaf(hi, 0.0625f, lo), acc[r][b]);
-        }
-    }
-}
-
-// One quad of an INT4O linear: codes w0 = the quad's first row ([4][CPR]
-// chunks), sc = the quad's scales ([G4] x 4 fp16), xp = permuted activations
-// (row stride xs, background then outliers at 128 * G4), wo = the quad's
-// outlier columns ([4][no8] chunks of 8 fp16).
-template <int B>
-__device__ __forceinline__ void int4o_quad(const uint4* __restrict__ w0, int CPR, const uint2* __restrict__ sc,
-                                           const uint4* __restrict__ wo, int no8, const uint16_t* xp, int xs,
-                                           int bg_len, int lane, float (&acc)[4][B]) {
-    zero_acc(acc);
-#pragma unroll 2
-    for (int cc = lane; cc < CPR; cc += 64) {
-        uint4 w[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = load_stream(w0 + r * CPR + cc);
-        int4o_chunk<B>(w, sc[cc >> 2], xp + 32 * cc, xs, acc);
-    }
-    const uint16_t* xo = xp + bg_len;
-    for (int oc = lane; oc < no8; oc += 64) {
-        uint4 o[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = wo[r * no8 + oc];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(xo + b * xs + 8 * oc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float t = acc[r][b];
-                t = dot2(as_h2(o[r].x), as_h2(xv.x), t);
-                t = dot2(as_h2(o[r].y), as_h2(xv.y), t);
-                t = dot2(as_h2(o[r].z), as_h2(xv.z), t);
-                t = dot2(as_h2(o[r].w), as_h2(xv.w), t);
-                acc[r][b] = t;
-            }
         }
     }
 }
@@ -173,26 +161,25 @@ __device__ __forceinline__ void int8_chunk(const uint4 (&w)[4], const uint4 (&xv
     }
 }
 
-// One quad of an INT8 linear whose activations are zero-padded to a whole
-// number of chunks (row stride xs), e.g. staged in LDS.
-template <int B>
-__device__ __forceinline__ void int8_quad_padded(const uint4* __restrict__ w0, int CPR, int nchunks, const uint16_t* x,
-                                                 int xs, int lane, float (&acc)[4][B]) {
-    zero_acc(acc);
-#pragma unroll 2
-    for (int cc = lane; cc < nchunks; cc += 64) {
-        uint4 w[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = load_stream(w0 + r * CPR + cc);
-        uint4 xv[B][2];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const uint4* p = reinterpret_cast<const uint4*>(x + b * xs + 16 * cc);
-            xv[b][0] = p[0];
-            xv[b][1] = p[1];
-        }
-        int8_chunk<B>(w, xv, acc);
-    }
+// Sum of v over the 64 lanes of the wave, returned to every lane.  Within each
+// 16-lane row: DPP exchanges with lane ^ 1, lane ^ 2, the mirrored lane of the
+// 8-lane half row and of the row; the four row sums are then read with
+// v_readlane.  No LDS round trips, so the dependent chain is a few cycles long.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp_move<0x141>(v);   // row_half_mirror
+    v += dpp_move<0x140>(v);   // row_mirror
+    const int iv = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Reduce a quad's accumulators over the wave; lane r * B + b returns the sum
@@ -204,10 +191,160 @@ __device__ __forceinline__ float quad_reduce(float (&acc)[4][B], int lane) {
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            float v = wave_sum(acc[r][b]);
+            const float v = wave_sum_dpp(acc[r][b]);
             if (lane == r * B + b) out = v;
         }
     return out;
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined streaming of a wave's quads.
+//
+// A wave owns quads q0, q0 + qstride, ... (nq of them).  Each quad is a
+// sequence of chunk iterations: iteration i covers chunk c = lane + 64 i of
+// the quad's chunk space.  For INT4O the chunk space is the background chunks
+// [0, CPR) followed by the outlier chunks [CPR, CPR + no8); for INT8 it is the
+// code chunks [0, nchunks).  The wave walks the flat sequence of (quad,
+// iteration) items through a window of U register slots: the loads of item
+// t + U are issued as soon as item t has been consumed, so U items are always
+// in flight.  The first items can be issued early (prefetch) because the
+// weights do not depend on the activations.
+//
+// Loads are issued unconditionally: a lane whose chunk lies outside the chunk
+// space reads a valid dummy address and ignores the result, so no slot
+// register is written on a divergent path (merging such writes would force a
+// wait for the load).
+struct QuadTask {
+    const uint4* codes;      // quad-major rows of CPR chunks
+    const uint2* scales;     // INT4O: [quads][G4] x 4 fp16
+    const uint4* wout;       // INT4O: rows of no8 chunks
+    int CPR, no8, nchunks;   // nchunks: INT8 chunks holding real columns; INT4O: CPR + no8
+    int q0, qstride, nq, IT; // IT: iterations per quad
+};
+
+template <int U>
+struct Slots {
+    uint4 w[U][4];
+    uint2 sc[U];
+};
+
+// Cursor over (quad, iteration) items.
+struct ItemCursor {
+    int j, i;
+    __device__ __forceinline__ void advance(int IT) {
+        if (++i == IT) {
+            i = 0;
+            ++j;
+        }
+    }
+};
+
+template <bool INT4O>
+__device__ __forceinline__ void issue_item(const QuadTask& t, ItemCursor cur, int lane, uint4 (&w)[4], uint2& sc) {
+    const int q = t.q0 + cur.j * t.qstride;
+    const int c = lane + 64 * cur.i;
+    const uint4* base;
+    int rs;
+    if (INT4O) {
+        const bool bg = c < t.CPR;
+        const bool ol = !bg && c < t.CPR + t.no8;
+        const uint4* dummy = t.CPR > 0 ? t.codes : t.wout;
+        base = bg ? t.codes + ((int64_t)q * 4 * t.CPR + c)
+                  : ol ? t.wout + ((int64_t)q * 4 * t.no8 + (c - t.CPR)) : dummy;
+        rs = bg ? t.CPR : ol ? t.no8 : 0;
+        if (t.CPR > 0) sc = gload_u2(t.scales + (bg ? (int64_t)q * (t.CPR >> 2) + (c >> 2) : 0));
+    } else {
+        const bool ok = c < t.nchunks;
+        base = ok ? t.codes + ((int64_t)q * 4 * t.CPR + c) : t.codes;
+        rs = ok ? t.CPR : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = gload_nt(base + r * rs);
+}
+
+// Issue items [from, to) of the window (to <= U), counting from item 0.
+template <bool INT4O, int U>
+__device__ __forceinline__ void prefetch_items(const QuadTask& t, int lane, Slots<U>& s, int from = 0, int to = U) {
+    const int T = t.nq * t.IT;
+    ItemCursor cur = {0, 0};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u >= from && u < to && u < T) issue_item<INT4O>(t, cur, lane, s.w[u], s.sc[u]);
+        cur.advance(t.IT);
+    }
+}
+
+// Consume the item in slot (w, sc): chunk c of the quad; xs holds the
+// activations (row stride xstride) in the chunk space's order, background
+// then, from bg_len on, the outlier channels (INT4O).
+template <bool INT4O, int B, class XPtr>
+__device__ __forceinline__ void consume_item(const QuadTask& t, int c, const uint4 (&w)[4], uint2 sc, XPtr xs,
+                                             int xstride, int bg_len, float (&acc)[4][B]) {
+    if (INT4O) {
+        if (c < t.CPR) {
+            uint4 xv[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) xv[b][k] = load_x16(xs + b * xstride + 32 * c + 8 * k);
+            int4o_chunk<B>(w, sc, xv, acc);
+        } else if (c < t.CPR + t.no8) {
+            const int o = bg_len + 8 * (c - t.CPR);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint4 xv = load_x16(xs + b * xstride + o);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = acc[r][b];
+                    v = dot2(as_h2(w[r].x), as_h2(xv.x), v);
+                    v = dot2(as_h2(w[r].y), as_h2(xv.y), v);
+                    v = dot2(as_h2(w[r].z), as_h2(xv.z), v);
+                    v = dot2(as_h2(w[r].w), as_h2(xv.w), v);
+                    acc[r][b] = v;
+                }
+            }
+        }
+    } else if (c < t.nchunks) {
+        uint4 xv[B][2];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            xv[b][0] = load_x16(xs + b * xstride + 16 * c);
+            xv[b][1] = load_x16(xs + b * xstride + 16 * c + 8);
+        }
+        int8_chunk<B>(w, xv, acc);
+    }
+}
+
+// Stream every item of the task; slots must hold the first `issued` items
+// already issued (prefetch_items); the rest of the window is issued here.
+// emit(quad, out) is called once per quad with the wave-reduced sums (lane
+// r * B + b holds row r, batch row b).
+template <bool INT4O, int B, int U, class XPtr, class Emit>
+__device__ __forceinline__ void stream_task(const QuadTask& t, Slots<U>& s, XPtr xs, int xstride, int bg_len,
+                                            int lane, int issued, Emit&& emit) {
+    const int T = t.nq * t.IT;
+    if (issued < U) prefetch_items<INT4O, U>(t, lane, s, issued, U);
+    float acc[4][B];
+    zero_acc(acc);
+    const int IT = t.IT > 0 ? t.IT : 1;
+    ItemCursor use = {0, 0};
+    ItemCursor nxt = {U / IT, U % IT};   // item U
+    for (int t0 = 0; t0 < T; t0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int item = t0 + u;
+            if (item < T) {
+                consume_item<INT4O, B>(t, lane + 64 * use.i, s.w[u], s.sc[u], xs, xstride, bg_len, acc);
+                if (item + U < T) issue_item<INT4O>(t, nxt, lane, s.w[u], s.sc[u]);
+                nxt.advance(IT);
+                if (use.i == IT - 1) {
+                    emit(t.q0 + use.j * t.qstride, quad_reduce<B>(acc, lane));
+                    zero_acc(acc);
+                }
+                use.advance(IT);
+            }
+        }
+    }
 }
 
 }  // namespace woqk

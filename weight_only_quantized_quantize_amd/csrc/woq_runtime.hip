@@ -37,8 +37,8 @@ struct DevStep {
 
 // Barrier state: one 128-byte line per counter.
 constexpr int SYNC_LINE = 16;                 // uint64 per line
-constexpr int SYNC_GROUPS = 8;
-constexpr int SYNC_TOP = 0, SYNC_GROUP0 = 1, SYNC_DEPART = 1 + SYNC_GROUPS, SYNC_ERR = 2 + SYNC_GROUPS;
+constexpr int SYNC_GROUPS = 16;
+constexpr int SYNC_GROUP0 = 1, SYNC_DEPART = 1 + SYNC_GROUPS, SYNC_ERR = 2 + SYNC_GROUPS;   // line 0 unused
 constexpr int SYNC_WORDS = (3 + SYNC_GROUPS) * SYNC_LINE;
 constexpr int FUSED_THREADS = 512;
 // polls of s_sleep(2) before a barrier is declared stuck (far above any step)
@@ -52,98 +52,190 @@ __device__ __forceinline__ u64 add_relaxed(u64* p, u64 v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Arrive at barrier j (1-based) and wait until every workgroup has arrived.
-// Two levels: workgroups count into one of ng group counters, the last arrival
-// of a group bumps the top counter, everyone polls the top counter.  The
-// steps order computation only (no step reads another step's outputs), so the
-// counters need no memory fences.  Returns false if the wait gave up.
-__device__ bool grid_barrier(u64* sync, unsigned ng, u64 j) {
-    const unsigned P = gridDim.x;
-    const unsigned g = blockIdx.x % ng;
-    const u64 gsize = P / ng + (g < P % ng ? 1 : 0);
-    u64* top = sync + SYNC_TOP * SYNC_LINE;
-    u64* grp = sync + (SYNC_GROUP0 + g) * SYNC_LINE;
-    u64* err = sync + SYNC_ERR * SYNC_LINE;
-    const u64 old = add_relaxed(grp, 1ull);
-    if (old + 1 == j * gsize) add_relaxed(top, 1ull);
-    unsigned n = 0;
-    while (ld_relaxed(top) < j * ng) {
-        if (ld_relaxed(err)) return false;
-        __builtin_amdgcn_s_sleep(2);
-        if (++n > SPIN_LIMIT) {
-            st_relaxed(err, 1ull);
-            return false;
-        }
+// register window of weight items per wave (narrower for wide batches, which
+// need the registers for activations and accumulators)
+template <int B>
+constexpr int prefetch_items_for() { return B <= 4 ? 4 : 2; }
+// Items per wave issued before a step boundary.  The barrier's own atomics
+// queue behind outstanding loads in the memory system, so only about what
+// drains within one barrier latency is issued early (about 1 item per wave,
+// 4 KB: ~7 MB over the chip); the rest of the window follows the barrier.
+constexpr int EARLY_ITEMS = 1;
+constexpr int PREFETCH_SRC = 18;    // staged activation sources per thread resolved before a barrier
+
+__device__ __forceinline__ QuadTask make_task(const DevStep& st, int gw, int NW) {
+    QuadTask t;
+    t.codes = st.codes;
+    t.scales = st.scales;
+    t.wout = st.wout;
+    t.CPR = st.CPR;
+    t.no8 = st.no8;
+    t.nchunks = st.fmt == WOQ_FMT_INT4O ? st.CPR + st.no8 : st.nchunks;
+    t.IT = (t.nchunks + 63) >> 6;
+    const int quads = (st.N + 3) >> 2;
+    t.q0 = gw;
+    t.qstride = NW;
+    t.nq = gw < quads ? (quads - 1 - gw) / NW + 1 : 0;
+    return t;
+}
+
+// Source index in the activation row of staged element k (-1: zero padding).
+__device__ __forceinline__ int stage_src(const DevStep& st, int k) {
+    if (st.fmt == WOQ_FMT_INT4O) {
+        const int bg = 128 * st.G4;
+        int src = -1;
+        if (k < st.K_bg) src = *gptr(st.perm + k);
+        else if (k >= bg && k - bg < st.n_out) src = *gptr(st.perm + st.K_bg + (k - bg));
+        return ((unsigned)src < (unsigned)st.K) ? src : -1;
     }
-    return true;
+    return k < st.K ? k : -1;
+}
+
+// Workgroup control barrier that waits only for this wave's LDS and scalar
+// memory operations, not for its outstanding vector loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+template <int B, int U>
+__device__ __forceinline__ void fused_step(const DevStep& st, const QuadTask& task, Slots<U>& slots,
+                                           const int (&src)[PREFETCH_SRC], uint16_t* xs, int tid, int lane) {
+    const int xlen = st.xlen;
+    // Stage activations.  The loads are unconditional (padding reads element 0
+    // and is replaced by zero afterwards), so they are all in flight at once and
+    // the step waits for one memory round trip.
+    uint16_t v[PREFETCH_SRC][B];
+#pragma unroll
+    for (int i = 0; i < PREFETCH_SRC; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) v[i][b] = *gptr(st.x + (int64_t)b * st.ldx + (src[i] >= 0 ? src[i] : 0));
+#pragma unroll
+    for (int i = 0; i < PREFETCH_SRC; ++i) {
+        const int k = tid + i * FUSED_THREADS;
+        if (k < xlen)
+#pragma unroll
+            for (int b = 0; b < B; ++b) xs[b * xlen + k] = src[i] >= 0 ? v[i][b] : (uint16_t)0;
+    }
+    for (int k = tid + PREFETCH_SRC * FUSED_THREADS; k < xlen; k += FUSED_THREADS) {
+        const int sk = stage_src(st, k);
+        for (int b = 0; b < B; ++b) xs[b * xlen + k] = sk >= 0 ? *gptr(st.x + (int64_t)b * st.ldx + sk) : (uint16_t)0;
+    }
+    lds_barrier();
+    if (st.fmt == WOQ_FMT_INT4O) {
+        stream_task<true, B, U>(task, slots, (lx_ptr)xs, xlen, 128 * st.G4, lane, EARLY_ITEMS, [&](int q, float out) {
+            if (lane < 4 * B) {
+                const int r = lane / B, b = lane % B, n = 4 * q + r;
+                if (n < st.N) *gptr(st.y + (int64_t)b * st.ldy + n) = f_to_h(out);
+            }
+        });
+    } else {
+        stream_task<false, B, U>(task, slots, (lx_ptr)xs, xlen, 0, lane, EARLY_ITEMS, [&](int q, float out) {
+            if (lane < 4 * B) {
+                const int r = lane / B, b = lane % B, n = 4 * q + r;
+                if (n < st.N) {
+                    float scale = st.seg_scale[st.nseg - 1];
+                    for (int i = st.nseg - 1; i >= 0; --i)
+                        if (n < st.seg_end[i]) scale = st.seg_scale[i];
+                    *gptr(st.y + (int64_t)b * st.ldy + n) = f_to_h(out * scale);
+                }
+            }
+        });
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void prefetch_step(const DevStep& st, const QuadTask& task, Slots<U>& slots,
+                                              int (&src)[PREFETCH_SRC], int tid, int lane) {
+    if (st.fmt == WOQ_FMT_INT4O) prefetch_items<true, U>(task, lane, slots, 0, EARLY_ITEMS);
+    else prefetch_items<false, U>(task, lane, slots, 0, EARLY_ITEMS);
+#pragma unroll
+    for (int i = 0; i < PREFETCH_SRC; ++i) {
+        const int k = tid + i * FUSED_THREADS;
+        src[i] = k < st.xlen ? stage_src(st, k) : -1;
+    }
 }
 
 template <int B>
 __global__ __launch_bounds__(FUSED_THREADS) void stack_fused(const DevStep* __restrict__ steps, int nsteps, u64* sync) {
     extern __shared__ __align__(16) uint16_t xs[];   // [B][xlen] staged activations
+    __shared__ int stuck_flag;
+    constexpr int U = prefetch_items_for<B>();
     const int tid = threadIdx.x, lane = tid & 63;
-    const int nwv = blockDim.x >> 6;
-    const int gw = blockIdx.x * nwv + (tid >> 6);
-    const int NW = gridDim.x * nwv;
-    const unsigned ng = gridDim.x < (unsigned)SYNC_GROUPS ? gridDim.x : (unsigned)SYNC_GROUPS;
+    // consecutive quads go to different workgroups first, so a small step
+    // spreads over every compute unit
+    const int gw = (tid >> 6) * gridDim.x + blockIdx.x;
+    const int NW = gridDim.x * (FUSED_THREADS / 64);
+    const unsigned P = gridDim.x;
+    const unsigned ng = P < (unsigned)SYNC_GROUPS ? P : (unsigned)SYNC_GROUPS;
+    const unsigned g = blockIdx.x % ng;
+    u64* grp = sync + (SYNC_GROUP0 + g) * SYNC_LINE;
+    u64* err = sync + SYNC_ERR * SYNC_LINE;
+
+    Slots<U> slots;
+    int src[PREFETCH_SRC];
+    QuadTask task = make_task(steps[0], gw, NW);
+    prefetch_step<U>(steps[0], task, slots, src, tid, lane);
     bool ok = true;
     for (int si = 0; si < nsteps && ok; ++si) {
-        const DevStep& st = steps[si];
-        const int fmt = st.fmt, xlen = st.xlen;
-        // stage activations in LDS (zero-padded; INT4O gathered through perm)
-        if (fmt == WOQ_FMT_INT4O) {
-            const int bg = 128 * st.G4;
-            for (int b = 0; b < B; ++b)
-                for (int k = tid; k < xlen; k += blockDim.x) {
-                    int src = -1;
-                    if (k < st.K_bg) src = st.perm[k];
-                    else if (k >= bg && k - bg < st.n_out) src = st.perm[st.K_bg + (k - bg)];
-                    xs[b * xlen + k] = ((unsigned)src < (unsigned)st.K) ? st.x[(int64_t)b * st.ldx + src] : (uint16_t)0;
-                }
-        } else {
-            for (int b = 0; b < B; ++b)
-                for (int k = tid; k < xlen; k += blockDim.x)
-                    xs[b * xlen + k] = (k < st.K) ? st.x[(int64_t)b * st.ldx + k] : (uint16_t)0;
-        }
-        __syncthreads();
-        const int quads = (st.N + 3) >> 2;
-        for (int q = gw; q < quads; q += NW) {
-            float acc[4][B];
-            float scale = 1.0f;
-            if (fmt == WOQ_FMT_INT4O) {
-                int4o_quad<B>(st.codes + (int64_t)q * 4 * st.CPR, st.CPR, st.scales + (int64_t)q * st.G4,
-                              st.wout + (int64_t)q * 4 * st.no8, st.no8, xs, xlen, 128 * st.G4, lane, acc);
-            } else {
-                int8_quad_padded<B>(st.codes + (int64_t)q * 4 * st.CPR, st.CPR, st.nchunks, xs, xlen, lane, acc);
-            }
-            const float out = quad_reduce<B>(acc, lane);
-            if (lane < 4 * B) {
-                const int r = lane / B, b = lane % B;
-                const int n = 4 * q + r;
-                if (n < st.N) {
-                    if (fmt == WOQ_FMT_INT8) {
-                        scale = st.seg_scale[st.nseg - 1];
-                        for (int i = st.nseg - 1; i >= 0; --i)
-                            if (n < st.seg_end[i]) scale = st.seg_scale[i];
-                    }
-                    st.y[(int64_t)b * st.ldy + n] = f_to_h(out * scale);
-                }
-            }
-        }
-        __syncthreads();  // LDS is rewritten by the next step
+        fused_step<B, U>(steps[si], task, slots, src, xs, tid, lane);
+        // every wave of this workgroup has finished the step's products and its
+        // LDS reads (its output stores may still be in flight: nothing reads them)
+        lds_barrier();
         if (si + 1 < nsteps) {
+            // The last wave arrives and waits; the other waves issue the next
+            // step's weight and index loads first, so those travel while the
+            // workgroups finish.  (The polling wave issues its own loads after
+            // the wait: vector loads return in order, and an earlier prefetch
+            // would hold back every poll.)  Steps only order computation (no step
+            // reads another step's outputs), so the counters are relaxed atomics
+            // without fences.
+            const u64 j = (u64)(si + 1);
+            constexpr int POLLER = FUSED_THREADS - 64;
+            task = make_task(steps[si + 1], gw, NW);
             int stuck = 0;
-            if (tid == 0) stuck = grid_barrier(sync, ng, (u64)(si + 1)) ? 0 : 1;
-            ok = __syncthreads_or(stuck) == 0;
+            if (tid < POLLER) {
+                prefetch_step<U>(steps[si + 1], task, slots, src, tid, lane);
+            } else {
+                // Arrive with a fire-and-forget add to this workgroup's group
+                // counter; lane g then watches group counter g, so the release is
+                // seen one memory round trip after the last arrival.
+                if (tid == POLLER) add_relaxed(grp, 1ull);
+                const unsigned lg = (unsigned)lane;
+                const u64 want = lg < ng ? j * (P / ng + (lg < P % ng ? 1 : 0)) : 0;
+                u64* mine = sync + (SYNC_GROUP0 + (lg < ng ? lg : 0)) * SYNC_LINE;
+                unsigned n = 0;
+                for (;;) {
+                    const u64 have = lg < ng ? ld_relaxed(mine) : 0;
+                    if (__ballot(have < want) == 0) break;
+                    if (ld_relaxed(err)) {
+                        stuck = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++n > SPIN_LIMIT) {
+                        if (tid == POLLER) st_relaxed(err, 1ull);
+                        stuck = 1;
+                        break;
+                    }
+                }
+                prefetch_step<U>(steps[si + 1], task, slots, src, tid, lane);
+            }
+            // Control barrier only: the poller's LDS flag is complete before it
+            // reaches s_barrier, and no wave waits for its outstanding vector
+            // loads (a __syncthreads fence would wait for the whole prefetch).
+            if (tid == POLLER) stuck_flag = stuck;
+            lds_barrier();
+            ok = stuck_flag == 0;
+            lds_barrier();                    // the flag is read before anyone rewrites it
         }
     }
     // The last workgroup to leave resets the counters for the next run; by
     // then every workgroup has passed its last barrier poll.
     if (tid == 0) {
         u64* depart = sync + SYNC_DEPART * SYNC_LINE;
-        if (add_relaxed(depart, 1ull) + 1 == gridDim.x) {
-            st_relaxed(sync + SYNC_TOP * SYNC_LINE, 0ull);
-            for (int g = 0; g < SYNC_GROUPS; ++g) st_relaxed(sync + (SYNC_GROUP0 + g) * SYNC_LINE, 0ull);
+        if (add_relaxed(depart, 1ull) + 1 == P) {
+            for (int gi = 0; gi < SYNC_GROUPS; ++gi) st_relaxed(sync + (SYNC_GROUP0 + gi) * SYNC_LINE, 0ull);
             st_relaxed(depart, 0ull);
         }
     }
