@@ -93,6 +93,22 @@ def test_small_stack_fused_equals_launches_and_oracle(gpu_lib, cfg, b):
     fused = [host(t) for t in outs]
     for i, (a, f) in enumerate(zip(ref_launch, fused)):
         np.testing.assert_array_equal(a.view(np.uint16), f.view(np.uint16), err_msg=f"step {i}")
+    # the public entry points composed by hand give the same bits
+    import torch
+    for layer in range(spec.layers):
+        for gi, (names, inp) in enumerate(GROUPS):
+            dev = rs.layers[layer][gi][2]
+            x = ins[4 * layer + gi]
+            y = torch.empty_like(outs[4 * layer + gi])
+            if spec.fmt == "int4o":
+                g = dev.geom
+                xp = torch.empty(b, g.xp_len, dtype=torch.float16, device="cuda")
+                woq.woq_permute_x(x, rs.perm_dev[spec.linear(names[0]).space], g, xp)
+                woq.woq_qgemv_int4o(dev.desc, xp, y)
+            else:
+                woq.woq_qgemv_int8(dev.desc, x, y)
+            np.testing.assert_array_equal(host(y).view(np.uint16), fused[4 * layer + gi].view(np.uint16),
+                                          err_msg=f"layer {layer} group {gi}")
     perms = oracle_perms(spec) if spec.fmt == "int4o" else None
     for layer in range(spec.layers):
         for gi, (names, inp) in enumerate(GROUPS):
