@@ -38,6 +38,40 @@ def algorithmic_bytes(fmt: str, N: int, K: int, b: int) -> int:
     return (N * K_bg) // 2 + 2 * N * G + 2 * N * n_out + 2 * b * (K + N)
 
 
+TRAFFIC_PROFILES = {
+    # (config, runner, batch) -> committed counter summary of that workload
+    (2, "launch", 1): "profiles/qgemv_int4o_valu__3b_int4o_stack_b1__traffic.md",
+}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("weight_only_quantized_quantize_amd/csrc/woq_gemv.cuh",
+              "weight_only_quantized_quantize_amd/csrc/woq_device.hip"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg: int, mode: str, b: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if there is none for this workload or the kernel sources
+    changed since the counters were taken."""
+    path = TRAFFIC_PROFILES.get((cfg, mode, b))
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    fields = {}
+    with open(os.path.join(ROOT, path)) as fh:
+        for ln in fh:
+            if ":" in ln and ln.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256_16"):
+                k, v = ln.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(spec, b: int, budget_s: float = 12.0):
     """The oracle, untuned, on a bounded sample: the decode products of layer 0
     (and more layers while the budget lasts), scaled to a whole step."""
@@ -198,7 +232,8 @@ def main():
         "decode_tok_s": round(b / (ms_per_step * 1e-3), 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.config, mode, b),
                      "launches_per_step": launches_per_step,
                      "mean_launch_us": round(1e3 * kern_ms / launches_per_step, 3),
                      "mean_algorithmic_bytes_per_launch": kernel_bytes // launches_per_step},

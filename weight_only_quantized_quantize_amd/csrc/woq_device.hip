@@ -27,9 +27,16 @@
 #include "woq_gemv.cuh"
 #include "woq_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace woq {
 static thread_local int g_last_hip_error = 0;
 void set_hip_error(int code) { g_last_hip_error = code; }
+static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+void set_launch_events(void* start, void* stop) {
+    g_ev_start = (hipEvent_t)start;
+    g_ev_stop = (hipEvent_t)stop;
+}
 }  // namespace woq
 
 extern "C" int woq_last_hip_error(void) { return woq::g_last_hip_error; }
@@ -263,6 +270,16 @@ __global__ __launch_bounds__(256) void qgemm_int4o_mfma(Int4oArgs a, int b) {
     }
 }
 
+// Launch a kernel; with timing events set, through hipExtLaunchKernel so the
+// events take the dispatch's own start and end timestamps.
+template <class K, class... A>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, A... args) {
+    void* argv[] = {(void*)&args...};
+    if (woq::g_ev_start)
+        return hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, s, woq::g_ev_start, woq::g_ev_stop, 0);
+    return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, s);
+}
+
 int launch_status(hipError_t e) {
     if (e != hipSuccess) {
         woq::set_hip_error((int)e);
@@ -272,19 +289,19 @@ int launch_status(hipError_t e) {
 }
 
 template <int B>
-void launch_int4o_valu(const Int4oArgs& a, int quads, hipStream_t s) {
-    hipLaunchKernelGGL(qgemv_int4o_valu<B>, dim3(quads), dim3(64), 0, s, a);
+hipError_t launch_int4o_valu(const Int4oArgs& a, int quads, hipStream_t s) {
+    return launch_kernel(qgemv_int4o_valu<B>, dim3(quads), dim3(64), 0, s, a);
 }
 
 template <int B>
-void launch_int8_valu(const Int8Args& a, int quads, hipStream_t s) {
-    hipLaunchKernelGGL(qgemv_int8_valu<B>, dim3(quads), dim3(64), 0, s, a);
+hipError_t launch_int8_valu(const Int8Args& a, int quads, hipStream_t s) {
+    return launch_kernel(qgemv_int8_valu<B>, dim3(quads), dim3(64), 0, s, a);
 }
 
 template <int NBT>
-void launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
+hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(woq::round_up(a.N, 4), 16);
-    hipLaunchKernelGGL(qgemm_int4o_mfma<NBT>, dim3(tiles), dim3(256), 0, s, a, b);
+    return launch_kernel(qgemm_int4o_mfma<NBT>, dim3(tiles), dim3(256), 0, s, a, b);
 }
 
 int check_int4o_w(const woq_int4o_w* w) {
@@ -345,16 +362,17 @@ int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_
     Int4oArgs a = make_int4o_args(w, xp, y, ldy);
     const int quads = (int)woq::ceil_div(w->N, 4);
     hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
     switch (b) {
-        case 1: launch_int4o_valu<1>(a, quads, s); break;
-        case 2: launch_int4o_valu<2>(a, quads, s); break;
-        case 3: launch_int4o_valu<3>(a, quads, s); break;
-        case 4: launch_int4o_valu<4>(a, quads, s); break;
-        case 5: launch_int4o_valu<5>(a, quads, s); break;
-        case 6: launch_int4o_valu<6>(a, quads, s); break;
-        default: launch_int4o_valu<7>(a, quads, s); break;
+        case 1: e = launch_int4o_valu<1>(a, quads, s); break;
+        case 2: e = launch_int4o_valu<2>(a, quads, s); break;
+        case 3: e = launch_int4o_valu<3>(a, quads, s); break;
+        case 4: e = launch_int4o_valu<4>(a, quads, s); break;
+        case 5: e = launch_int4o_valu<5>(a, quads, s); break;
+        case 6: e = launch_int4o_valu<6>(a, quads, s); break;
+        default: e = launch_int4o_valu<7>(a, quads, s); break;
     }
-    return launch_status(hipGetLastError());
+    return launch_status(e);
 }
 
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy, void* stream) {
@@ -364,13 +382,14 @@ int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_
     Int4oArgs a = make_int4o_args(w, xp, y, ldy);
     hipStream_t s = (hipStream_t)stream;
     const int nbt = (int)woq::ceil_div(b, 16);
+    hipError_t e;
     switch (nbt) {
-        case 1: launch_int4o_mfma<1>(a, (int)b, s); break;
-        case 2: launch_int4o_mfma<2>(a, (int)b, s); break;
-        case 3: launch_int4o_mfma<3>(a, (int)b, s); break;
-        default: launch_int4o_mfma<4>(a, (int)b, s); break;
+        case 1: e = launch_int4o_mfma<1>(a, (int)b, s); break;
+        case 2: e = launch_int4o_mfma<2>(a, (int)b, s); break;
+        case 3: e = launch_int4o_mfma<3>(a, (int)b, s); break;
+        default: e = launch_int4o_mfma<4>(a, (int)b, s); break;
     }
-    return launch_status(hipGetLastError());
+    return launch_status(e);
 }
 
 int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t b, uint16_t* y, int64_t ldy,
@@ -402,17 +421,18 @@ int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t 
     }
     const int quads = (int)woq::ceil_div(w->N, 4);
     hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
     switch (b) {
-        case 1: launch_int8_valu<1>(a, quads, s); break;
-        case 2: launch_int8_valu<2>(a, quads, s); break;
-        case 3: launch_int8_valu<3>(a, quads, s); break;
-        case 4: launch_int8_valu<4>(a, quads, s); break;
-        case 5: launch_int8_valu<5>(a, quads, s); break;
-        case 6: launch_int8_valu<6>(a, quads, s); break;
-        case 7: launch_int8_valu<7>(a, quads, s); break;
-        default: launch_int8_valu<8>(a, quads, s); break;
+        case 1: e = launch_int8_valu<1>(a, quads, s); break;
+        case 2: e = launch_int8_valu<2>(a, quads, s); break;
+        case 3: e = launch_int8_valu<3>(a, quads, s); break;
+        case 4: e = launch_int8_valu<4>(a, quads, s); break;
+        case 5: e = launch_int8_valu<5>(a, quads, s); break;
+        case 6: e = launch_int8_valu<6>(a, quads, s); break;
+        case 7: e = launch_int8_valu<7>(a, quads, s); break;
+        default: e = launch_int8_valu<8>(a, quads, s); break;
     }
-    return launch_status(hipGetLastError());
+    return launch_status(e);
 }
 
 }  // extern "C"

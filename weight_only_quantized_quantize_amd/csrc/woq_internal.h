@@ -16,6 +16,11 @@ namespace woq {
 // hipError_t of the last failing HIP call on this thread.
 void set_hip_error(int code);
 
+// Events (hipEvent_t, or null) that the next product launch on this thread
+// records at its own dispatch boundaries (the timestamps a kernel trace
+// reports); set by the runner's timing pass around one launch.
+void set_launch_events(void* start, void* stop);
+
 inline int64_t round_up(int64_t a, int64_t m) { return (a + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t a, int64_t m) { return (a + m - 1) / m; }
 

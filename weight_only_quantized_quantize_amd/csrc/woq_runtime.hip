@@ -278,13 +278,12 @@ int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outp
         if (s.fmt == WOQ_FMT_INT4O) {
             rc = woq_permute_x(x, s.w4.geom.K, s.perm, b, &s.w4.geom, st->xp, stream);
             if (rc) return rc;
-            if (ev) hipEventRecord(ev[2 * i], hs);
-            rc = woq_qgemv_int4o(&s.w4, st->xp, b, y, s.w4.N, stream);
-        } else {
-            if (ev) hipEventRecord(ev[2 * i], hs);
-            rc = woq_qgemv_int8(&s.w8, x, s.w8.K, b, y, s.w8.N, stream);
         }
-        if (ev) hipEventRecord(ev[2 * i + 1], hs);
+        // with events, the product launch records them at its own dispatch boundaries
+        if (ev) woq::set_launch_events(ev[2 * i], ev[2 * i + 1]);
+        if (s.fmt == WOQ_FMT_INT4O) rc = woq_qgemv_int4o(&s.w4, st->xp, b, y, s.w4.N, stream);
+        else rc = woq_qgemv_int8(&s.w8, x, s.w8.K, b, y, s.w8.N, stream);
+        if (ev) woq::set_launch_events(nullptr, nullptr);
         if (rc) return rc;
     }
     return WOQ_OK;
