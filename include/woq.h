@@ -317,6 +317,50 @@ int woq_stack_time_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t*
 /* Release the runner and its workspace (after the stream has finished). */
 int woq_stack_destroy(woq_stack* st);
 
+/* ------------------------------------------------------- streamed pager */
+
+/*
+ * One product of a streamed INT8 layer: its device-layout codes start
+ * code_offset bytes into the layer's block; w gives N, K and the segment
+ * scales (w.codes is ignored).
+ */
+typedef struct {
+    int64_t code_offset;
+    woq_int8_w w;
+} woq_pager_step;
+
+typedef struct woq_pager woq_pager;
+
+/*
+ * Streamed decode over INT8 layers that live in pinned host memory ("Open
+ * Origin - ELG Stream Layer", Key Features 1-3: a block-allocated INT8 pool in
+ * pinned RAM, asynchronous layer paging, double-buffered prefetch of layer N+1
+ * on a secondary stream while layer N computes).  Layer l's block is
+ * layer_bytes[l] bytes at pinned_pool + layer_off[l] (page-locked memory from
+ * hipHostMalloc or an equivalent pinned allocation, owned by the caller, valid
+ * while the pager exists).  steps holds steps_per_layer entries per layer, in
+ * layer order.  The pager allocates two device slots of max(layer_bytes) and
+ * its events; WOQ_ENOMEM if that fails.  1 <= max_b <= 8.
+ */
+int woq_pager_create(const void* pinned_pool, const int64_t* layer_off, const int64_t* layer_bytes,
+                     int32_t n_layers, const woq_pager_step* steps, int32_t steps_per_layer, int64_t max_b,
+                     woq_pager** out);
+
+/*
+ * One streamed pass: on copy_stream, layer l's block is copied into slot
+ * l mod 2 once the products of layer l-2 have finished with that slot; on
+ * compute_stream, layer l's products start once its copy has landed.  Step s
+ * of layer l reads inputs[l * steps_per_layer + s] (fp16 [b, K]) and writes
+ * outputs[l * steps_per_layer + s] (fp16 [b, N]).  The two streams must be
+ * distinct; both are left with work queued (synchronise compute_stream to wait
+ * for the outputs).  Passes of one pager must not overlap.
+ */
+int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                  void* compute_stream, void* copy_stream);
+
+/* Release the slots and events (after both streams have finished). */
+int woq_pager_destroy(woq_pager* p);
+
 #ifdef __cplusplus
 }
 #endif

@@ -253,3 +253,35 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert lib.woq_qgemv_int8(w8, 16, 68, 1, 16, 8, None) == woq.WOQ_EALIGN   # ldx % 8
     assert lib.woq_qgemv_int8(w8, 16, 64, 9, 16, 8, None) == woq.WOQ_EINVAL   # b > 8
     assert lib.woq_permute_x(16, 100, 16, 1, g, 16, None) == woq.WOQ_EINVAL    # ldx < K
+
+
+# -------------------------------------------------------------------- pager
+
+def test_pager_create_validates_before_allocating():
+    """Argument checks of woq_pager_create run before any device call, so
+    they are exercised without a GPU."""
+    import ctypes
+    lib = woq.lib()
+    pool = np.zeros(4096, np.uint8)
+    N, K = 8, 64
+    need = lib.woq_int8_dev_bytes(N, K)
+
+    def create(code_offset, layer_bytes, n=N, nseg=1, seg_end=None, max_b=1):
+        st = woq.PagerStep()
+        st.code_offset = code_offset
+        st.w.N, st.w.K, st.w.nseg = n, K, nseg
+        st.w.seg_end[0] = n if seg_end is None else seg_end
+        st.w.seg_scale[0] = 1.0
+        steps = (woq.PagerStep * 1)(st)
+        off = (ctypes.c_int64 * 1)(0)
+        nb = (ctypes.c_int64 * 1)(layer_bytes)
+        h = ctypes.c_void_p()
+        return lib.woq_pager_create(woq._ptr(pool), off, nb, 1, steps, 1, max_b, ctypes.byref(h))
+
+    assert create(8, 4096) == woq.WOQ_EINVAL                 # codes not 16-byte aligned
+    assert create(4096 - need + 16, 4096) == woq.WOQ_EINVAL  # codes run past the block
+    assert create(0, 4096, seg_end=N - 1) == woq.WOQ_EINVAL   # segments do not cover N
+    assert create(0, 4096, nseg=0) == woq.WOQ_EINVAL
+    assert create(0, 4096, max_b=9) == woq.WOQ_EINVAL
+    assert create(0, 0) == woq.WOQ_EINVAL
+    assert lib.woq_pager_destroy(None) == woq.WOQ_OK

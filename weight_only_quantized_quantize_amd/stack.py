@@ -139,3 +139,57 @@ class ResidentStack:
                     if x is not None:
                         tot += x.numel() * x.element_size()
         return tot
+
+
+class StreamedInt8Stack:
+    """INT8 layers in one pinned host pool, decoded through woq_pager.
+
+    Each layer's block holds the device layouts of its four products (q|k|v,
+    o, gate|up, down) back to back at 256-byte aligned offsets."""
+
+    def __init__(self, spec, weight_fn, threads=None, layers=None, log=None):
+        import torch
+        assert spec.fmt == "int8"
+        self.spec = spec
+        self.n_layers = spec.layers if layers is None else layers
+        threads = threads or min(16, os.cpu_count() or 1)
+        log = log or (lambda *a: None)
+        # block layout (identical for every layer)
+        offs, o = [], 0
+        for names, _ in GROUPS:
+            N = sum(spec.linear(n).N for n in names)
+            K = spec.linear(names[0]).K
+            offs.append(o)
+            o += -(-woq.lib().woq_int8_dev_bytes(N, K) // 256) * 256
+        self.block_bytes = o
+        self.group_offsets = offs
+        self.pool = torch.empty(self.n_layers * o, dtype=torch.uint8, pin_memory=True)
+        pool_np = self.pool.numpy()
+        self.steps = []
+        for l0 in range(0, self.n_layers, 4):
+            ls = range(l0, min(self.n_layers, l0 + 4))
+            log(f"quantising streamed layers {ls.start}..{ls.stop - 1}")
+            jobs = [(layer, lin) for layer in ls for lin in spec.linears()]
+            res = _map_weights(spec, jobs, weight_fn, lambda layer, lin, W: woq.woq_quantize_int8(W), threads)
+            got = {(layer, lin.name): r for (layer, lin), r in zip(jobs, res)}
+            for layer in ls:
+                base = layer * o
+                for gi, (names, _) in enumerate(GROUPS):
+                    parts = [got[(layer, n)] for n in names]
+                    q = np.concatenate([p[0] for p in parts]) if len(parts) > 1 else parts[0][0]
+                    dev = woq.woq_layout_int8(q)
+                    pool_np[base + offs[gi]: base + offs[gi] + dev.size] = dev
+                    st = woq.PagerStep()
+                    st.code_offset = offs[gi]
+                    st.w.N, st.w.K, st.w.nseg = q.shape[0], q.shape[1], len(parts)
+                    end = 0
+                    for i, (qi, sc) in enumerate(parts):
+                        end += qi.shape[0]
+                        st.w.seg_end[i] = end
+                        st.w.seg_scale[i] = float(sc)
+                    self.steps.append(st)
+        self.layer_off = [l * o for l in range(self.n_layers)]
+        self.layer_bytes = [o] * self.n_layers
+
+    def make_pager(self, max_b: int):
+        return woq.Pager(self.pool, self.layer_off, self.layer_bytes, self.steps, len(GROUPS), max_b)

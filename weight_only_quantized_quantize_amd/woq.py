@@ -53,6 +53,10 @@ class StackStep(ctypes.Structure):
                 ("perm", c_void_p)]
 
 
+class PagerStep(ctypes.Structure):
+    _fields_ = [("code_offset", c_int64), ("w", Int8W)]
+
+
 FMT_INT8, FMT_INT4O = 1, 2
 
 _LIB = None
@@ -86,6 +90,10 @@ _SIGS = {
     "woq_stack_time_fused": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
                                      POINTER(c_float)]),
     "woq_stack_destroy": (c_int, [c_void_p]),
+    "woq_pager_create": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int64), c_int32, POINTER(PagerStep), c_int32,
+                                 c_int64, POINTER(c_void_p)]),
+    "woq_pager_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_void_p]),
+    "woq_pager_destroy": (c_int, [c_void_p]),
 }
 
 # symbols the header declares (checked by the CPU tests)
@@ -405,3 +413,40 @@ def step_int8(dev: "DeviceInt8", in_slot: int, out_slot: int) -> StackStep:
     st.fmt, st.in_slot, st.out_slot = FMT_INT8, in_slot, out_slot
     st.w8 = dev.desc
     return st
+
+
+# ------------------------------------------------------------ streamed pager
+
+class Pager:
+    """Owns a woq_pager over a caller-owned pinned pool (kept referenced)."""
+
+    def __init__(self, pool, layer_off, layer_bytes, steps, steps_per_layer: int, max_b: int):
+        self.pool = pool
+        self.off = (c_int64 * len(layer_off))(*layer_off)
+        self.bytes = (c_int64 * len(layer_bytes))(*layer_bytes)
+        self.steps = (PagerStep * len(steps))(*steps)
+        self.n = len(steps)
+        h = c_void_p()
+        _check(_lib().woq_pager_create(_ptr(pool), self.off, self.bytes, len(layer_off), self.steps, steps_per_layer,
+                                       max_b, ctypes.byref(h)), "woq_pager_create")
+        self.handle = h
+
+    def bind(self, inputs, outputs):
+        self._in, self._out = list(inputs), list(outputs)
+        self._pin = (c_void_p * len(self._in))(*[t.data_ptr() for t in self._in])
+        self._pout = (c_void_p * len(self._out))(*[t.data_ptr() for t in self._out])
+
+    def run(self, b: int, compute_stream, copy_stream):
+        _check(_lib().woq_pager_run(self.handle, self._pin, self._pout, b, _stream(compute_stream),
+                                    _stream(copy_stream)), "woq_pager_run")
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _check(_lib().woq_pager_destroy(self.handle), "woq_pager_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
