@@ -234,6 +234,27 @@ int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t 
 int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
                     int64_t ldy, void* stream);
 
+/*
+ * Positions of the input channels in the permuted, padded activation row of
+ * woq_permute_x: pos[j] = k such that xp[r, k] = x[r, j] (host function).
+ * pos holds round_up(K, 8) entries; entries K.. are 0xFFFF.  WOQ_EINVAL if
+ * perm is not a permutation of [0, K); WOQ_EUNSUPPORTED if xp_len > 65535.
+ */
+int woq_perm_positions(const int32_t* perm, const woq_int4o_geom* g, uint16_t* pos);
+
+/*
+ * woq_permute_x and woq_qgemv_int4o in one launch, with the same result bit
+ * for bit: x is read in its natural channel order (fp16 [b, ldx], 16-byte
+ * aligned, ldx a multiple of 8 and >= K) and scattered through pos (device
+ * copy of woq_perm_positions, 16-byte aligned) into the permuted, split row,
+ * held in on-chip memory while the weights stream.  WOQ_EUNSUPPORTED unless
+ * woq_qgemv_int4o_x_supported(g, b) (1 <= b <= 7 and the staged row, b *
+ * xp_len fp16 values, fits 64 KB); callers then use the two-call form.
+ */
+int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, const uint16_t* pos,
+                      int64_t b, uint16_t* y, int64_t ldy, void* stream);
+int woq_qgemv_int4o_x_supported(const woq_int4o_geom* g, int64_t b);
+
 /* The matrix-core (MFMA) kernel of woq_qgemv_int4o for any 1 <= b <= 64. */
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
                     int64_t ldy, void* stream);
@@ -265,13 +286,20 @@ typedef struct woq_stack woq_stack;
  * OTF-LLM runner that drives the model through the fused kernels).  The step
  * array is copied; the weights it points to stay owned by the caller.  The
  * runner owns an activation workspace for batches up to max_b (allocated on
- * the current device here).  WOQ_ENOMEM if that allocation fails.
+ * the current device here) and, for each distinct INT4O permutation, a device
+ * channel-position table (woq_perm_positions), built here from the
+ * permutation's device copy, which must therefore hold its values already.
+ * WOQ_EINVAL if a permutation is not one; WOQ_ENOMEM if an allocation fails.
  */
 int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b, woq_stack** out);
 
 /*
- * Run every step once: for each step, permute its input (INT4O) and launch
- * its product, all on `stream`.  inputs[slot] are fp16 [b, K of the step]
+ * Run every step once, in order, on `stream`: an INT4O step is one
+ * woq_qgemv_int4o_x launch where that form supports the case (b <= 7, K a
+ * multiple of 8, 16-byte aligned input, N <= 16384; beyond that width the
+ * separate permutation is faster), otherwise woq_permute_x followed by
+ * woq_qgemv_int4o; an INT8 step is one woq_qgemv_int8 launch.  Both INT4O
+ * forms give the same bits.  inputs[slot] are fp16 [b, K of the step]
  * activations (rows contiguous), outputs[slot] fp16 [b, N of the step].
  * 1 <= b <= max_b.  Asynchronous; the caller synchronises.
  */

@@ -62,13 +62,35 @@ def int4o_parts(W_list, perm, n_out):
 
 
 def int4o_run(parts, g, perm, x, force_mfma=False):
+    """Permute + product through the two public calls; where the one-launch
+    form (permutation folded into the product) supports the case, it must give
+    the same bits."""
     dw = woq.DeviceInt4o(parts, g)
     xd = _dev(x)
     xp = _empty16(x.shape[0], g.xp_len)
     woq.woq_permute_x(xd, _dev(perm), g, xp)
     y = _empty16(x.shape[0], dw.N)
     (woq.woq_qgemm_int4o if force_mfma else woq.woq_qgemv_int4o)(dw.desc, xp, y)
-    return _host(y).astype(np.float64), _host(xp)
+    y_host = _host(y)
+    b = x.shape[0]
+    if not force_mfma and woq.woq_qgemv_int4o_x_supported(g, b):
+        y1 = one_launch(dw, g, perm, x)
+        np.testing.assert_array_equal(y1.view(np.uint16), y_host.view(np.uint16),
+                                      err_msg="one-launch permutation+product differs from the two-call form")
+    return y_host.astype(np.float64), _host(xp)
+
+
+def one_launch(dw, g, perm, x, ldx=None):
+    """woq_qgemv_int4o_x on x stored with leading dimension ldx (>= K, multiple of 8)."""
+    b, K = x.shape
+    ldx = ldx or -(-K // 8) * 8
+    xpad = np.full((b, ldx), np.float16(3.0), np.float16)     # padding must not leak into the result
+    xpad[:, :K] = x
+    pos = _dev(woq.woq_perm_positions(perm, g))
+    y = _empty16(b, dw.N)
+    y.fill_(7.0)
+    woq.woq_qgemv_int4o_x(dw.desc, _dev(xpad), pos, y, ldx=ldx)
+    return _host(y)
 
 
 def int4o_ref(W_list, perm, n_out, x):
@@ -242,6 +264,41 @@ def test_int4o_full_shapes_sampled(gpu_lib, cfg):
             y, _ = int4o_run([part], g, perm, x[:b])
             x_bg, x_out = O.permute_split(x[:b], perm, g.n_out)
             check(y[:, rows], O.linear_int4o(c, s, wo, x_bg, x_out), f"cfg{cfg} {lin.name} b={b}")
+
+
+@pytest.mark.parametrize("N,K,b,ldx", [(1, 8, 1, 8), (5, 300, 3, 320), (4100, 1000, 2, 1000 + 24),
+                                       (16500, 3072, 1, 3072), (33, 8192, 3, 8192), (17, 28672, 1, 28672 + 8)])
+def test_int4o_one_launch_matches_oracle(gpu_lib, N, K, b, ldx):
+    """The permutation folded into the product, including row strides above K,
+    several quads per wave (N >= 16384) and the largest supported row."""
+    _print_case("int4o one launch", N, K, b, ldx)
+    rng = np.random.default_rng(N + 7 * K + b)
+    g = woq.woq_int4o_geometry(K)
+    assert woq.woq_qgemv_int4o_x_supported(g, b)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    parts = int4o_parts([W], perm, g.n_out)
+    dw = woq.DeviceInt4o(parts, g)
+    y = one_launch(dw, g, perm, x, ldx).astype(np.float64)
+    check(y, int4o_ref([W], perm, g.n_out, x), f"one launch {N}x{K} b={b}")
+
+
+def test_int4o_one_launch_rejects_unsupported(gpu_lib):
+    g = woq.woq_int4o_geometry(28672)
+    rng = np.random.default_rng(1)
+    perm = O.global_perm(28672, np.sort(rng.choice(28672, g.n_out, replace=False)))
+    W = (rng.standard_normal((4, 28672)) * 0.02).astype(np.float32)
+    dw = woq.DeviceInt4o(int4o_parts([W], perm, g.n_out), g)
+    x = _dev(np.zeros((2, 28672), np.float16))
+    pos = _dev(woq.woq_perm_positions(perm, g))
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_qgemv_int4o_x(dw.desc, x, pos, _empty16(2, 4))
+    assert e.value.status == woq.WOQ_EUNSUPPORTED
 
 
 def test_batch_prefix_invariant(gpu_lib):

@@ -285,3 +285,45 @@ def test_pager_create_validates_before_allocating():
     assert create(0, 4096, max_b=9) == woq.WOQ_EINVAL
     assert create(0, 0) == woq.WOQ_EINVAL
     assert lib.woq_pager_destroy(None) == woq.WOQ_OK
+
+
+# ------------------------------------------------- permutation positions
+
+@pytest.mark.parametrize("K", [8, 130, 1000, 3072])
+def test_perm_positions_invert_the_oracle_split(K):
+    """xp (the oracle's permute/split, padded as the device row) at pos[j] is
+    x[j] for every channel; table padding is 0xFFFF."""
+    rng = np.random.default_rng(K)
+    n_out = O.n_outliers(K)
+    perm = O.global_perm(K, O.select_outliers(rng.random(K), n_out)).astype(np.int32)
+    g = woq.woq_int4o_geometry(K)
+    pos = woq.woq_perm_positions(perm, g)
+    x = rng.standard_normal((2, K)).astype(np.float16)
+    x_bg, x_out = O.permute_split(x, perm, n_out)
+    xp = np.zeros((2, g.xp_len))
+    xp[:, :x_bg.shape[1]] = x_bg          # background, zero-padded to whole groups
+    xp[:, 128 * g.G4:128 * g.G4 + n_out] = x_out
+    assert pos.shape == (-(-K // 8) * 8,)
+    np.testing.assert_array_equal(xp[:, pos[:K].astype(np.int64)], x)
+    assert np.all(pos[K:] == 0xFFFF)
+    assert len(set(pos[:K].tolist())) == K
+
+
+def test_perm_positions_rejects_non_permutations():
+    K = 64
+    g = woq.woq_int4o_geometry(K)
+    perm = np.arange(K, dtype=np.int32)
+    perm[5] = 6
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_perm_positions(perm, g)
+    assert e.value.status == woq.WOQ_EINVAL
+    perm[5] = K
+    with pytest.raises(woq.WoqError):
+        woq.woq_perm_positions(perm, g)
+    big = woq.woq_int4o_geometry(70000)
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_perm_positions(np.arange(70000, dtype=np.int32), big)
+    assert e.value.status == woq.WOQ_EUNSUPPORTED
+    assert woq.woq_qgemv_int4o_x_supported(woq.woq_int4o_geometry(28672), 1)
+    assert not woq.woq_qgemv_int4o_x_supported(woq.woq_int4o_geometry(28672), 2)
+    assert not woq.woq_qgemv_int4o_x_supported(woq.woq_int4o_geometry(3072), 8)

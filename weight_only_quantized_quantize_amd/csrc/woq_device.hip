@@ -99,6 +99,110 @@ __global__ __launch_bounds__(64) void qgemv_int4o_valu(Int4oArgs a) {
     });
 }
 
+// ------------------------------- INT4O, batch <= 7, permutation in the kernel
+
+// The activation permutation and split folded into the product: a workgroup
+// of GX_WAVES waves reads the activations in their natural channel order
+// (coalesced 16-byte loads of 8 channels, together with the 8 channels'
+// positions in the permuted row) and scatters them into LDS, where they form
+// the permuted, zero-padded row that the waves' quads then read.  The weight
+// loads of every wave are issued right after the activation loads, so the
+// staging costs no extra memory round trip.
+constexpr int GX_WAVES = 4;
+constexpr int GX_THREADS = 64 * GX_WAVES;
+constexpr int GX_LDS_BYTES = 64 * 1024;
+
+struct Int4oGxArgs {
+    Int4oArgs p;             // p.xp unused
+    const uint16_t* x;       // [b][ldx], natural channel order
+    const uint16_t* pos;     // [round_up(K, 8)] position of each channel in the permuted row (0xFFFF: none)
+    int K, K_bg, n_out, ldx, qpw;   // qpw: quads per wave
+};
+
+// Write 8 channels (one 16-byte chunk per batch row) to their positions in
+// the staged row; positions outside the row (table padding) are skipped.
+template <int B>
+__device__ __forceinline__ void gx_scatter(uint16_t* xs, int xp_len, const uint4 (&xv)[B], uint4 pv) {
+    const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int p = (int)((pw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+        if (p < xp_len) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint32_t xw[4] = {xv[b].x, xv[b].y, xv[b].z, xv[b].w};
+                xs[b * xp_len + p] = (uint16_t)(xw[j >> 1] >> (16 * (j & 1)));
+            }
+        }
+    }
+}
+
+template <int B>
+__global__ __launch_bounds__(GX_THREADS) void qgemv_int4o_gx(Int4oGxArgs a) {
+    extern __shared__ __align__(16) uint16_t xs[];   // [B][xp_len]
+    constexpr int U = B <= 4 ? 4 : 2;
+    constexpr int SC = B == 1 ? 4 : B == 2 ? 2 : 1;   // activation chunks per thread per pass
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int xp_len = a.p.xp_len, bg_len = 128 * a.p.G4;
+    const int quads = (a.p.N + 3) >> 2;
+    // quads base + wave, base + wave + GX_WAVES, ... (qpw of them, within N)
+    const int base = blockIdx.x * GX_WAVES * a.qpw;
+    const int q0 = base + wave;
+    const int last = min(quads, base + GX_WAVES * a.qpw);
+    QuadTask t;
+    t.codes = a.p.codes;
+    t.scales = a.p.scales;
+    t.wout = a.p.wout;
+    t.CPR = 4 * a.p.G4;
+    t.no8 = a.p.no8;
+    t.nchunks = t.CPR + t.no8;
+    t.IT = (t.nchunks + 63) >> 6;
+    t.q0 = q0 < last ? q0 : 0;              // a wave without quads streams quad 0's first item and ignores it
+    t.qstride = GX_WAVES;
+    t.nq = q0 < last ? (last - 1 - q0) / GX_WAVES + 1 : 0;
+
+    const int nc = (a.K + 7) >> 3;          // 8-channel activation chunks
+    const g_u32x4* xg = (const g_u32x4*)a.x;
+    const g_u32x4* pg = (const g_u32x4*)a.pos;
+    const int ldx16 = a.ldx >> 3;
+    // first pass of activation loads (unconditional; out-of-range chunks reload chunk 0)
+    uint4 xv[SC][B], pv[SC];
+#pragma unroll
+    for (int i = 0; i < SC; ++i) {
+        const int c = tid + i * GX_THREADS;
+        const int cc = c < nc ? c : 0;
+        pv[i] = as_uint4(pg[cc]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) xv[i][b] = as_uint4(xg[b * ldx16 + cc]);
+    }
+    Slots<U> slots;
+    prefetch_items_fixed<true, U>(t, lane, slots);
+    // padding of the permuted row: [K_bg, bg_len) and [bg_len + n_out, xp_len)
+    for (int k = a.K_bg + tid; k < bg_len; k += GX_THREADS)
+#pragma unroll
+        for (int b = 0; b < B; ++b) xs[b * xp_len + k] = 0;
+    for (int k = bg_len + a.n_out + tid; k < xp_len; k += GX_THREADS)
+#pragma unroll
+        for (int b = 0; b < B; ++b) xs[b * xp_len + k] = 0;
+#pragma unroll
+    for (int i = 0; i < SC; ++i)
+        if (tid + i * GX_THREADS < nc) gx_scatter<B>(xs, xp_len, xv[i], pv[i]);
+    for (int c = tid + SC * GX_THREADS; c < nc; c += GX_THREADS) {
+        uint4 xv1[B];
+        const uint4 pv1 = as_uint4(pg[c]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) xv1[b] = as_uint4(xg[b * ldx16 + c]);
+        gx_scatter<B>(xs, xp_len, xv1, pv1);
+    }
+    lds_barrier();
+    stream_task<true, B, U>(t, slots, (lx_ptr)xs, xp_len, bg_len, lane, U, [&](int q, float out) {
+        if (lane < 4 * B) {
+            const int r = lane / B, b = lane % B, n = 4 * q + r;
+            if (n < a.p.N) *gptr(a.p.y + (int64_t)b * a.p.ldy + n) = f_to_h(out);
+        }
+    });
+}
+
 // --------------------------------------------------------- INT8, batch <= 8
 
 struct Int8Args {
@@ -294,6 +398,14 @@ hipError_t launch_int4o_valu(const Int4oArgs& a, int quads, hipStream_t s) {
 }
 
 template <int B>
+hipError_t launch_int4o_gx(const Int4oGxArgs& a, hipStream_t s) {
+    const int quads = (int)woq::ceil_div(a.p.N, 4);
+    const int grid = (int)woq::ceil_div(quads, (int64_t)GX_WAVES * a.qpw);
+    const size_t lds = (size_t)B * a.p.xp_len * sizeof(uint16_t);
+    return launch_kernel(qgemv_int4o_gx<B>, dim3(grid), dim3(GX_THREADS), lds, s, a);
+}
+
+template <int B>
 hipError_t launch_int8_valu(const Int8Args& a, int quads, hipStream_t s) {
     return launch_kernel(qgemv_int8_valu<B>, dim3(quads), dim3(64), 0, s, a);
 }
@@ -373,6 +485,47 @@ int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_
         default: e = launch_int4o_valu<7>(a, quads, s); break;
     }
     return launch_status(e);
+}
+
+int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, const uint16_t* pos, int64_t b,
+                      uint16_t* y, int64_t ldy, void* stream) {
+    int st = check_int4o_w(w);
+    if (st) return st;
+    const woq_int4o_geom& g = w->geom;
+    if (b < 0 || ldx < g.K || ldy < w->N || ldx > INT32_MAX || ldy > INT32_MAX) return WOQ_EINVAL;
+    if (b == 0 || w->N == 0) return WOQ_OK;
+    if (!x || !pos || !y) return WOQ_EINVAL;
+    if (!woq::aligned16(x) || !woq::aligned16(pos) || (ldx & 7) || ((uintptr_t)y & 1u)) return WOQ_EALIGN;
+    if (!woq_qgemv_int4o_x_supported(&g, b)) return WOQ_EUNSUPPORTED;
+    Int4oGxArgs a;
+    a.p = make_int4o_args(w, nullptr, y, ldy);
+    a.x = x;
+    a.pos = pos;
+    a.K = (int)g.K;
+    a.K_bg = (int)g.K_bg;
+    a.n_out = (int)g.n_out;
+    a.ldx = (int)ldx;
+    // one quad per wave: more quads per workgroup would stage the activations
+    // fewer times but leaves fewer waves to keep loads in flight, which costs
+    // more (measured on the 70B-shaped products)
+    a.qpw = 1;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (b) {
+        case 1: e = launch_int4o_gx<1>(a, s); break;
+        case 2: e = launch_int4o_gx<2>(a, s); break;
+        case 3: e = launch_int4o_gx<3>(a, s); break;
+        case 4: e = launch_int4o_gx<4>(a, s); break;
+        case 5: e = launch_int4o_gx<5>(a, s); break;
+        case 6: e = launch_int4o_gx<6>(a, s); break;
+        default: e = launch_int4o_gx<7>(a, s); break;
+    }
+    return launch_status(e);
+}
+
+int woq_qgemv_int4o_x_supported(const woq_int4o_geom* g, int64_t b) {
+    if (!g || b < 1 || b > 7) return 0;
+    return g->xp_len <= 65535 && b * g->xp_len * 2 <= GX_LDS_BYTES;
 }
 
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy, void* stream) {

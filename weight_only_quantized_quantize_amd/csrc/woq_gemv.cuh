@@ -262,6 +262,29 @@ __device__ __forceinline__ void issue_item(const QuadTask& t, ItemCursor cur, in
     for (int r = 0; r < 4; ++r) w[r] = gload_nt(base + r * rs);
 }
 
+// Issue all U slots of the window unconditionally: slots past the task's last
+// item reload item 0 (results ignored), so the number of loads in flight is
+// the same on every path and later waits can count them exactly.  The task
+// must have an item 0 at a valid address (q0 a real quad).
+template <bool INT4O, int U>
+__device__ __forceinline__ void prefetch_items_fixed(const QuadTask& t, int lane, Slots<U>& s) {
+    const int T = t.nq * t.IT;
+    ItemCursor cur = {0, 0};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const ItemCursor c = u < T ? cur : ItemCursor{0, 0};
+        issue_item<INT4O>(t, c, lane, s.w[u], s.sc[u]);
+        cur.advance(t.IT);
+    }
+}
+
+// Workgroup control barrier that waits only for this wave's LDS and scalar
+// memory operations, not for its outstanding vector loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
 // Issue items [from, to) of the window (to <= U), counting from item 0.
 template <bool INT4O, int U>
 __device__ __forceinline__ void prefetch_items(const QuadTask& t, int lane, Slots<U>& s, int from = 0, int to = U) {

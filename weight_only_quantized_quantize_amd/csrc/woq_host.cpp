@@ -417,4 +417,20 @@ int woq_layout_int4o_inverse(const uint8_t* dev_codes, const uint16_t* dev_scale
     return WOQ_OK;
 }
 
+int woq_perm_positions(const int32_t* perm, const woq_int4o_geom* g, uint16_t* pos) {
+    if (!perm || !pos || !woq::int4o_geom_valid(g)) return WOQ_EINVAL;
+    if (g->xp_len > 65535) return WOQ_EUNSUPPORTED;
+    const int64_t K = g->K, K8 = woq::round_up(K, 8), bg = 128 * g->G4;
+    for (int64_t j = 0; j < K8; ++j) pos[j] = 0xFFFF;
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t j = perm[k];
+        if (j < 0 || j >= K || pos[j] != 0xFFFF) {
+            for (int64_t i = 0; i < K8; ++i) pos[i] = 0xFFFF;
+            return WOQ_EINVAL;
+        }
+        pos[j] = (uint16_t)(k < g->K_bg ? k : bg + (k - g->K_bg));
+    }
+    return WOQ_OK;
+}
+
 }  // extern "C"

@@ -91,13 +91,6 @@ __device__ __forceinline__ int stage_src(const DevStep& st, int k) {
     return k < st.K ? k : -1;
 }
 
-// Workgroup control barrier that waits only for this wave's LDS and scalar
-// memory operations, not for its outstanding vector loads and stores.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-}
-
 template <int B, int U>
 __device__ __forceinline__ void fused_step(const DevStep& st, const QuadTask& task, Slots<U>& slots,
                                            const int (&src)[PREFETCH_SRC], uint16_t* xs, int tid, int lane) {
@@ -249,6 +242,11 @@ struct woq_stack {
     int64_t xp_elems = 0;      // per workspace row
     uint16_t* xp = nullptr;    // [max_b][xp_elems]
     int device = 0;
+    // INT4O: device channel-position table of each step's permutation (null
+    // where the row is too long for 16-bit positions); one table per distinct
+    // permutation, owned here
+    std::vector<const uint16_t*> pos;
+    std::vector<uint16_t*> pos_owned;
     // fused pass
     DevStep* dsteps = nullptr;             // device step table
     std::vector<DevStep> hsteps;           // host copy (pointers of the last bound inputs/outputs)
@@ -266,6 +264,53 @@ int hip_status(hipError_t e) {
     return e == hipErrorOutOfMemory ? WOQ_ENOMEM : WOQ_EHIP;
 }
 
+void free_stack(woq_stack* st) {
+    if (st->xp) (void)hipFree(st->xp);
+    if (st->dsteps) (void)hipFree(st->dsteps);
+    if (st->sync) (void)hipFree(st->sync);
+    for (uint16_t* p : st->pos_owned) (void)hipFree(p);
+    delete st;
+}
+
+// Channel-position tables of the INT4O steps' permutations (read back from
+// the device once; an invalid permutation is rejected here).
+int make_positions(woq_stack* st) {
+    st->pos.assign(st->steps.size(), nullptr);
+    for (size_t i = 0; i < st->steps.size(); ++i) {
+        const woq_stack_step& s = st->steps[i];
+        if (s.fmt != WOQ_FMT_INT4O || s.w4.geom.xp_len > 65535) continue;
+        for (size_t j = 0; j < i && !st->pos[i]; ++j) {
+            const woq_stack_step& t = st->steps[j];
+            if (st->pos[j] && t.perm == s.perm && t.w4.geom.K == s.w4.geom.K && t.w4.geom.n_out == s.w4.geom.n_out)
+                st->pos[i] = st->pos[j];
+        }
+        if (st->pos[i]) continue;
+        const int64_t K = s.w4.geom.K, K8 = woq::round_up(K, 8);
+        std::vector<int32_t> perm((size_t)K);
+        std::vector<uint16_t> pos((size_t)K8);
+        hipError_t e = hipMemcpy(perm.data(), s.perm, sizeof(int32_t) * K, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_status(e);
+        int rc = woq_perm_positions(perm.data(), &s.w4.geom, pos.data());
+        if (rc) return rc;
+        uint16_t* d = nullptr;
+        e = hipMalloc((void**)&d, sizeof(uint16_t) * K8);
+        if (e != hipSuccess) return hip_status(e);
+        st->pos_owned.push_back(d);
+        e = hipMemcpy(d, pos.data(), sizeof(uint16_t) * K8, hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_status(e);
+        st->pos[i] = d;
+    }
+    return WOQ_OK;
+}
+
+// Largest N for which a step folds its permutation into the product.  Every
+// workgroup of that kernel stages the whole activation row (16 output rows per
+// workgroup), so its extra traffic grows with N; measured on MI355X, the
+// folded form is faster up to the 3B gate|up width (16384 rows at K = 3072)
+// and the 70B down projection (8192 rows at K = 28672), and slower than a
+// separate permutation launch for the 70B gate|up product (57344 rows).
+constexpr int64_t ONE_LAUNCH_MAX_N = 16384;
+
 // One pass over the steps; ev (2 per step) brackets each product launch.
 int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b, void* stream,
              hipEvent_t* ev) {
@@ -275,6 +320,15 @@ int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outp
         const uint16_t* x = inputs[s.in_slot];
         uint16_t* y = outputs[s.out_slot];
         int rc;
+        if (s.fmt == WOQ_FMT_INT4O && st->pos[i] && s.w4.N <= ONE_LAUNCH_MAX_N &&
+            woq_qgemv_int4o_x_supported(&s.w4.geom, b) && (s.w4.geom.K & 7) == 0 && woq::aligned16(x)) {
+            // permutation folded into the product: one launch
+            if (ev) woq::set_launch_events(ev[2 * i], ev[2 * i + 1]);
+            rc = woq_qgemv_int4o_x(&s.w4, x, s.w4.geom.K, st->pos[i], b, y, s.w4.N, stream);
+            if (ev) woq::set_launch_events(nullptr, nullptr);
+            if (rc) return rc;
+            continue;
+        }
         if (s.fmt == WOQ_FMT_INT4O) {
             rc = woq_permute_x(x, s.w4.geom.K, s.perm, b, &s.w4.geom, st->xp, stream);
             if (rc) return rc;
@@ -437,12 +491,10 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
     if (e == hipSuccess) e = hipMemset(st->sync, 0, sizeof(u64) * SYNC_WORDS);
     if (e == hipSuccess && n_steps > 0)
         e = hipMemcpy(st->dsteps, st->hsteps.data(), sizeof(DevStep) * n_steps, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        int rc = hip_status(e);
-        hipFree(st->xp);
-        hipFree(st->dsteps);
-        hipFree(st->sync);
-        delete st;
+    int rc = hip_status(e);
+    if (rc == WOQ_OK) rc = make_positions(st);
+    if (rc != WOQ_OK) {
+        free_stack(st);
         return rc;
     }
     *out = st;
@@ -558,15 +610,15 @@ int woq_stack_time_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t*
 int woq_stack_destroy(woq_stack* st) {
     if (!st) return WOQ_OK;
     hipError_t e = hipSuccess;
-    if (st->xp) e = hipFree(st->xp);
-    if (st->dsteps) {
-        hipError_t e2 = hipFree(st->dsteps);
+    auto release = [&](void* p) {
+        if (!p) return;
+        hipError_t e2 = hipFree(p);
         if (e == hipSuccess) e = e2;
-    }
-    if (st->sync) {
-        hipError_t e2 = hipFree(st->sync);
-        if (e == hipSuccess) e = e2;
-    }
+    };
+    release(st->xp);
+    release(st->dsteps);
+    release(st->sync);
+    for (uint16_t* p : st->pos_owned) release(p);
     delete st;
     return hip_status(e);
 }

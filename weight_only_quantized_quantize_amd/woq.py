@@ -81,6 +81,10 @@ _SIGS = {
     "woq_qgemv_int8": (c_int, [POINTER(Int8W), c_void_p, c_int64, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_qgemv_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_qgemm_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
+    "woq_perm_positions": (c_int, [c_void_p, POINTER(Int4oGeom), c_void_p]),
+    "woq_qgemv_int4o_x": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                  c_void_p]),
+    "woq_qgemv_int4o_x_supported": (c_int, [POINTER(Int4oGeom), c_int64]),
     "woq_stack_create": (c_int, [POINTER(StackStep), c_int32, c_int64, POINTER(c_void_p)]),
     "woq_stack_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
     "woq_stack_time": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
@@ -274,6 +278,24 @@ def woq_qgemv_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
     b = xp.shape[0] if b is None else b
     _check(_lib().woq_qgemv_int4o(ctypes.byref(w), _ptr(xp), b, _ptr(y), y.shape[1], _stream(stream)),
            "woq_qgemv_int4o")
+    return y
+
+
+def woq_perm_positions(perm: np.ndarray, g: Int4oGeom) -> np.ndarray:
+    perm = np.ascontiguousarray(perm, np.int32)
+    pos = np.empty(-(-g.K // 8) * 8, np.uint16)
+    _check(_lib().woq_perm_positions(_ptr(perm), ctypes.byref(g), _ptr(pos)), "woq_perm_positions")
+    return pos
+
+
+def woq_qgemv_int4o_x_supported(g: Int4oGeom, b: int) -> bool:
+    return bool(_lib().woq_qgemv_int4o_x_supported(ctypes.byref(g), b))
+
+
+def woq_qgemv_int4o_x(w: Int4oW, x, pos_dev, y, stream=None, b: int | None = None, ldx: int | None = None):
+    b = x.shape[0] if b is None else b
+    _check(_lib().woq_qgemv_int4o_x(ctypes.byref(w), _ptr(x), ldx or x.shape[1], _ptr(pos_dev), b, _ptr(y),
+                                    y.shape[1], _stream(stream)), "woq_qgemv_int4o_x")
     return y
 
 
