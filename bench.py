@@ -207,7 +207,7 @@ def main():
         # product kernels: a second pass of K steps with HIP events around each product launch
         step_ms, _ = runner.time(b, args.steps, stream)
         kern_ms = sum(step_ms)
-        kname = ("qgemv_int4o_valu" if b < 8 else "qgemm_int4o_mfma") if spec.fmt == "int4o" else "qgemv_int8_valu"
+        kname = ("qgemv_int4o_tile" if b <= 4 else "qgemm_int4o_mfma") if spec.fmt == "int4o" else "qgemv_int8_valu"
         launches_per_step = len(shapes)
         kernel_bytes = step_bytes
     ms_per_step = wall * 1e3 / args.steps
@@ -230,7 +230,7 @@ def main():
                    "format": spec.fmt, "layers": L, "hidden": spec.hidden, "intermediate": spec.inter,
                    "q_heads": spec.q_heads, "kv_heads": spec.kv_heads, "head_dim": spec.head_dim,
                    "batch": b, "runner": mode,
-                   "launches_per_step": 1 if mode == "fused" else (2 * len(shapes) if spec.fmt == "int4o" else len(shapes)),
+                   "launches_per_step": 1 if mode == "fused" else runner.launches(b),
                    "algorithmic_bytes_per_step": step_bytes},
         "decode_tok_s": round(b / (ms_per_step * 1e-3), 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

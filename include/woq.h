@@ -153,15 +153,19 @@ int woq_layout_int8(const int8_t* q, int64_t N, int64_t K, uint8_t* dev);
 int woq_layout_int8_inverse(const uint8_t* dev, int64_t N, int64_t K, int8_t* q);
 
 /*
- * INT4O device layout (N4 = N rounded up to 4):
- *   codes  : N4 rows of 64 * G4 bytes.  Row n holds, for each group g and each
- *            32-channel chunk c of the group, 16 bytes: the codes of background
- *            channels 128g + 32c + 16P + t (P = 0, 1; t = 0..15) as offset-binary
+ * INT4O device layout, in tiles of 16 rows (N16 = N rounded up to 16; padding
+ * rows hold code 0, scale 0 and zero outlier weights):
+ *   codes  : for each tile, group g (0 .. G4-1) and 32-channel chunk c (0..3)
+ *            of the group, 256 bytes: 16 bytes per row of the tile, row-minor.
+ *            The 16 bytes of (row, g, c) hold the codes of background channels
+ *            128g + 32c + 16P + t (P = 0, 1; t = 0..15) as offset-binary
  *            nibbles (code + 8), dword e (0, 1) of half P holding, at nibble
  *            positions 0,4,2,6 the channels t = 4e+0..4e+3 and at positions
- *            1,5,3,7 the channels t = 8+4e+0..8+4e+3.  Padding holds code 0.
- *   scales : [N4/4][G4][4] fp16 - the four rows of a quad side by side per group.
- *   w_out  : [N4, n_out8] fp16, zero-padded.
+ *            1,5,3,7 the channels t = 8+4e+0..8+4e+3.  A (tile, group) block is
+ *            1 KB; a row's codes are 64 * G4 bytes.
+ *   scales : [N16/16][G4][16] fp16 - the 16 rows of a tile side by side per group.
+ *   w_out  : [N16/16][n_out8/8][16] chunks of 8 fp16 (the outlier weights of
+ *            channels 8i .. 8i+7 of each row, row-minor within a tile), zero-padded.
  * Byte sizes from woq_int4o_dev_sizes.  The inverse reproduces the canonical
  * arrays bit for bit.
  */
@@ -228,8 +232,10 @@ int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t 
  * with fp32 accumulation ("On-The-Fly Weight Synthesizer (OTF-LLM Engine)",
  * architecture diagram: the outlier GEMM and the fused background GEMM added
  * into one FP16 output).  xp from woq_permute_x (fp16 [b, xp_len]); y fp16
- * [b, ldy], ldy >= N.  b <= 7 runs the vector-ALU kernel, b >= 8 the matrix-core
- * kernel (woq_qgemm_int4o).  1 <= b <= 64 (b = 0 is a no-op).
+ * [b, ldy], ldy >= N.  The vector-ALU kernel runs for b <= 2, and for b <= 4
+ * when N < 6144, if b * xp_len fp16 values fit in 62 KB of LDS; otherwise the
+ * matrix-core kernel (woq_qgemm_int4o) runs - on MI355X the faster of the two
+ * in each case.  1 <= b <= 64 (b = 0 is a no-op).
  */
 int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
                     int64_t ldy, void* stream);
@@ -247,9 +253,11 @@ int woq_perm_positions(const int32_t* perm, const woq_int4o_geom* g, uint16_t* p
  * for bit: x is read in its natural channel order (fp16 [b, ldx], 16-byte
  * aligned, ldx a multiple of 8 and >= K) and scattered through pos (device
  * copy of woq_perm_positions, 16-byte aligned) into the permuted, split row,
- * held in on-chip memory while the weights stream.  WOQ_EUNSUPPORTED unless
- * woq_qgemv_int4o_x_supported(g, b) (1 <= b <= 7 and the staged row, b *
- * xp_len fp16 values, fits 64 KB); callers then use the two-call form.
+ * held in on-chip memory while the weights stream; this is the vector-ALU
+ * kernel of woq_qgemv_int4o at any 1 <= b <= 4.  WOQ_EUNSUPPORTED unless
+ * woq_qgemv_int4o_x_supported(g, b) (1 <= b <= 4, xp_len <= 65535 and the
+ * staged row, b * xp_len fp16 values, fits 62 KB); callers then use the
+ * two-call form.
  */
 int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, const uint16_t* pos,
                       int64_t b, uint16_t* y, int64_t ldy, void* stream);
@@ -295,16 +303,24 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
 
 /*
  * Run every step once, in order, on `stream`: an INT4O step is one
- * woq_qgemv_int4o_x launch where that form supports the case (b <= 7, K a
- * multiple of 8, 16-byte aligned input, N <= 16384; beyond that width the
- * separate permutation is faster), otherwise woq_permute_x followed by
- * woq_qgemv_int4o; an INT8 step is one woq_qgemv_int8 launch.  Both INT4O
- * forms give the same bits.  inputs[slot] are fp16 [b, K of the step]
+ * woq_qgemv_int4o_x launch where folding the permutation into the product is
+ * the faster form (the vector kernel serves the batch, K is a multiple of 8,
+ * the input 16-byte aligned, N <= 16384 and b * xp_len <= 8704), otherwise
+ * woq_permute_x followed by woq_qgemv_int4o; an INT8 step is one
+ * woq_qgemv_int8 launch.  Both INT4O forms give the same bits.
+ * inputs[slot] are fp16 [b, K of the step]
  * activations (rows contiguous), outputs[slot] fp16 [b, N of the step].
  * 1 <= b <= max_b.  Asynchronous; the caller synchronises.
  */
 int woq_stack_run(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
                   void* stream);
+
+/*
+ * Kernel launches of one woq_stack_run pass at batch b (a folded INT4O step
+ * or an INT8 step is one launch, a permute-then-product INT4O step two),
+ * assuming 16-byte aligned inputs.
+ */
+int woq_stack_launches(const woq_stack* st, int64_t b, int32_t* launches);
 
 /*
  * woq_stack_run repeated `iters` times with a pair of HIP events recorded on
@@ -321,9 +337,9 @@ int woq_stack_time(woq_stack* st, const uint16_t* const* inputs, uint16_t* const
  * workgroup stays resident (cooperative launch), steps run in order, and a
  * device-side barrier separates consecutive steps, so no step starts its
  * products before every workgroup has finished the previous step.  Each step
- * stages its activations (gathered through the permutation for INT4O) in LDS.
- * Supports INT8 with b <= 8 and INT4O with b <= 7; other cases return
- * WOQ_EUNSUPPORTED (use woq_stack_run).  The barrier counters live in the
+ * stages its activations in LDS.  Supports stacks of INT8 steps with b <= 8;
+ * a stack with an INT4O step, or a larger batch, returns WOQ_EUNSUPPORTED (use
+ * woq_stack_run, which is also the faster pass on MI355X).  The barrier counters live in the
  * runner and are reset by the kernel itself before it exits, so consecutive
  * runs on one stream need no host action.  Runs of one runner must not
  * overlap (same stream, or synchronise).  A barrier that waits longer than a

@@ -270,7 +270,8 @@ def test_int4o_full_shapes_sampled(gpu_lib, cfg):
                                        (16500, 3072, 1, 3072), (33, 8192, 3, 8192), (17, 28672, 1, 28672 + 8)])
 def test_int4o_one_launch_matches_oracle(gpu_lib, N, K, b, ldx):
     """The permutation folded into the product, including row strides above K,
-    several quads per wave (N >= 16384) and the largest supported row."""
+    every tile/split plan of the vector kernel (N from 1 to 16500 rows) and the
+    largest supported row."""
     _print_case("int4o one launch", N, K, b, ldx)
     rng = np.random.default_rng(N + 7 * K + b)
     g = woq.woq_int4o_geometry(K)

@@ -1,8 +1,11 @@
-"""GPU tests of the layer-stack runner (per-launch and fused persistent pass).
+"""GPU tests of the layer-stack runner (per-launch pass, and the fused
+persistent pass of INT8 stacks).
 
-Both passes use the same per-quad arithmetic, so their outputs must agree bit
-for bit; both are also checked against the oracle, whose weights and
-permutations are computed by the oracle itself from the same seeded inputs.
+The runner's launches are the public entry points, so its outputs must equal
+those entry points composed by hand bit for bit; the fused INT8 pass uses the
+same per-quad arithmetic and must agree bit for bit too.  Everything is also
+checked against the oracle, whose weights and permutations are computed by the
+oracle itself from the same seeded inputs.
 """
 import numpy as np
 import pytest
@@ -76,23 +79,28 @@ def host(t):
 
 
 @pytest.mark.parametrize("cfg,b", [(2, 1), (2, 3), (2, 7), (3, 1), (3, 4), (3, 8)])
-def test_small_stack_fused_equals_launches_and_oracle(gpu_lib, cfg, b):
+def test_small_stack_runner_equals_entry_points_and_oracle(gpu_lib, cfg, b):
     _case("small stack", cfg, b)
     spec = synth.small_stack_spec(cfg, layers=3, batches=(b,))
     rs = build(spec)
     ins, outs = io(spec, rs, b)
     runner = rs.make_runner(b)
     runner.bind(ins, outs)
-    runner.run(b)
+    for _ in range(2):
+        runner.run(b)
     ref_launch = [host(t).copy() for t in outs]
-    for t in outs:
-        t.fill_(7.0)
-    for _ in range(3):                       # repeated runs: the barrier counters reset themselves
-        runner.run_fused(b)
-    runner.check()
-    fused = [host(t) for t in outs]
-    for i, (a, f) in enumerate(zip(ref_launch, fused)):
-        np.testing.assert_array_equal(a.view(np.uint16), f.view(np.uint16), err_msg=f"step {i}")
+    if spec.fmt == "int8":
+        for t in outs:
+            t.fill_(7.0)
+        for _ in range(3):                       # repeated runs: the barrier counters reset themselves
+            runner.run_fused(b)
+        runner.check()
+        for i, (a, t) in enumerate(zip(ref_launch, outs)):
+            np.testing.assert_array_equal(a.view(np.uint16), host(t).view(np.uint16), err_msg=f"fused step {i}")
+    else:
+        with pytest.raises(woq.WoqError) as e:   # the persistent pass streams INT8 only
+            runner.run_fused(b)
+        assert e.value.status == woq.WOQ_EUNSUPPORTED
     # the public entry points composed by hand give the same bits
     import torch
     for layer in range(spec.layers):
@@ -107,22 +115,23 @@ def test_small_stack_fused_equals_launches_and_oracle(gpu_lib, cfg, b):
                 woq.woq_qgemv_int4o(dev.desc, xp, y)
             else:
                 woq.woq_qgemv_int8(dev.desc, x, y)
-            np.testing.assert_array_equal(host(y).view(np.uint16), fused[4 * layer + gi].view(np.uint16),
+            np.testing.assert_array_equal(host(y).view(np.uint16), ref_launch[4 * layer + gi].view(np.uint16),
                                           err_msg=f"layer {layer} group {gi}")
     perms = oracle_perms(spec) if spec.fmt == "int4o" else None
     for layer in range(spec.layers):
         for gi, (names, inp) in enumerate(GROUPS):
             ref = oracle_group(spec, perms, layer, names, inp, b)
-            err = O.normwise_rel_err(fused[4 * layer + gi].astype(np.float64), ref)
+            err = O.normwise_rel_err(ref_launch[4 * layer + gi].astype(np.float64), ref)
             print(f"layer {layer} {'|'.join(names)}: {err:.3e}", flush=True)
             assert err <= TOL
 
 
-def test_config2_stack_fused_full_size(gpu_lib):
-    """The 3B-shaped INT4O stack at full size, batch 1: the fused pass equals the
-    per-launch pass bit for bit on every output, and sampled rows of layers 0 and
-    27 match the oracle (the permutations are the planted sets, which selection
-    recovers)."""
+def test_config2_stack_full_size(gpu_lib):
+    """The 3B-shaped INT4O stack at full size, batch 1: every output equals the
+    two-call form (permute, then product) bit for bit, and sampled rows of
+    layers 0 and 27 match the oracle (the permutations are the planted sets,
+    which selection recovers)."""
+    import torch
     spec = synth.stack_spec(2)
     _case("config 2 full stack")
     rs = build(spec)
@@ -133,11 +142,17 @@ def test_config2_stack_fused_full_size(gpu_lib):
     runner = rs.make_runner(1)
     runner.bind(ins, outs)
     runner.run(1)
-    ref_launch = [host(t).copy() for t in outs]
-    runner.run_fused(1)
-    runner.check()
-    for i, t in enumerate(outs):
-        np.testing.assert_array_equal(ref_launch[i].view(np.uint16), host(t).view(np.uint16), err_msg=f"step {i}")
+    got = [host(t).copy() for t in outs]
+    for layer in range(spec.layers):
+        for gi, (names, inp) in enumerate(GROUPS):
+            dev = rs.layers[layer][gi][2]
+            g = dev.geom
+            xp = torch.empty(1, g.xp_len, dtype=torch.float16, device="cuda")
+            woq.woq_permute_x(ins[4 * layer + gi], rs.perm_dev[spec.linear(names[0]).space], g, xp)
+            y = torch.empty_like(outs[4 * layer + gi])
+            woq.woq_qgemv_int4o(dev.desc, xp, y)
+            np.testing.assert_array_equal(host(y).view(np.uint16), got[4 * layer + gi].view(np.uint16),
+                                          err_msg=f"layer {layer} group {gi}")
     perms = {sp: O.global_perm(spec.space_width(sp), synth.planted_set(spec, sp)) for sp in synth.SPACES}
     rng = np.random.default_rng(2)
     for layer in (0, spec.layers - 1):
@@ -148,8 +163,7 @@ def test_config2_stack_fused_full_size(gpu_lib):
             for n in names:
                 cols.extend(offs + rows[n])
                 offs += spec.linear(n).N
-            got = host(outs[4 * layer + gi])[:, cols].astype(np.float64)
-            err = O.normwise_rel_err(got, ref)
+            err = O.normwise_rel_err(got[4 * layer + gi][:, cols].astype(np.float64), ref)
             print(f"layer {layer} {'|'.join(names)}: {err:.3e}", flush=True)
             assert err <= TOL
 
@@ -167,3 +181,14 @@ def test_fused_unsupported_batch_falls_back(gpu_lib):
     perms = oracle_perms(spec)
     ref = oracle_group(spec, perms, 0, ("q", "k", "v"), 0, 8)
     assert O.normwise_rel_err(host(outs[0]).astype(np.float64), ref) <= TOL
+
+
+def test_runner_launch_count(gpu_lib):
+    """One launch per folded INT4O step (small widths, b <= 2), two where the
+    permutation runs separately (b = 8, matrix-core kernel), one per INT8 step."""
+    spec = synth.small_stack_spec(2, layers=2, batches=(8,))
+    runner = build(spec).make_runner(8)
+    assert runner.launches(1) == 4 * spec.layers
+    assert runner.launches(8) == 8 * spec.layers
+    spec8 = synth.small_stack_spec(3, layers=2, batches=(4,))
+    assert build(spec8).make_runner(4).launches(4) == 4 * spec8.layers

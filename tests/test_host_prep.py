@@ -186,8 +186,8 @@ def test_int4o_layout_roundtrip(N, K, n_out):
     perm = O.global_perm(K, np.sort(rng.choice(K, g.n_out, replace=False)))
     packed, scales, w_out = woq.woq_quantize_int4o(W, perm, g.n_out)
     dc, ds, dw = woq.woq_layout_int4o(packed, scales, w_out, g)
-    N4 = -(-N // 4) * 4
-    assert dc.size == N4 * 64 * g.G4 and ds.size == N4 * g.G4 and dw.size == N4 * g.n_out8
+    N16 = -(-N // 16) * 16
+    assert dc.size == N16 * 64 * g.G4 and ds.size == N16 * g.G4 and dw.size == N16 * g.n_out8
     p2, s2, w2 = woq.woq_layout_int4o_inverse(dc, ds, dw, N, g)
     np.testing.assert_array_equal(p2, packed)
     np.testing.assert_array_equal(s2.view(np.uint16), scales.view(np.uint16))
@@ -209,7 +209,37 @@ def test_int4o_device_nibble_placement():
         pos = (lo_pos if t < 8 else hi_pos)[j]
         nib = (int(dw[2 * P + e]) >> (4 * pos)) & 0xF
         assert nib == codes[0, c] + 8, c
-    assert np.all(dc[16:] == 0x88)          # rows 1..3 and the other chunks: code 0
+    assert np.all(dc[16:] == 0x88)          # rows 1..15 and the other chunks: code 0
+
+
+def test_int4o_device_tile_placement():
+    """Tiles of 16 rows: chunk (row r, group g, chunk c) at byte
+    ((r // 16 * G4 + g) * 4 + c) * 256 + (r % 16) * 16; scale (r, g) at
+    (r // 16 * G4 + g) * 16 + r % 16; outlier weight (r, i) in the 8-wide chunk
+    ((r // 16 * no8 + i // 8) * 16 + r % 16) at element i % 8."""
+    N, K, n_out = 20, 300, 3
+    g = woq.woq_int4o_geometry(K, n_out)
+    assert (g.G, g.G4, g.n_out8) == (3, 4, 8)
+    codes = np.zeros((N, g.K_pad), np.int8)
+    r, gi, c, t = 17, 1, 2, 5                  # channel 128*1 + 32*2 + 5 of row 17
+    codes[r, 128 * gi + 32 * c + t] = -6
+    packed = O.pack_int4(codes)
+    scales = np.zeros((N, g.G), np.float16)
+    scales[r, 2] = np.float16(0.5)
+    w_out = np.zeros((N, n_out), np.float16)
+    w_out[r, 2] = np.float16(-3.0)
+    dc, ds, dw = woq.woq_layout_int4o(packed, scales, w_out, g)
+    off = ((r // 16 * g.G4 + gi) * 4 + c) * 256 + (r % 16) * 16
+    chunk = dc[off:off + 16].view(np.uint32)
+    e, j = (t // 4, t % 4)
+    assert (int(chunk[e]) >> (4 * [0, 4, 2, 6][j])) & 0xF == -6 + 8
+    others = np.delete(dc, np.arange(off, off + 16))
+    assert np.all(others == 0x88)
+    assert ds[(r // 16 * g.G4 + 2) * 16 + r % 16] == np.float16(0.5).view(np.uint16)
+    assert np.count_nonzero(ds) == 1
+    no8 = g.n_out8 // 8
+    assert dw[((r // 16 * no8 + 0) * 16 + r % 16) * 8 + 2] == np.float16(-3.0).view(np.uint16)
+    assert np.count_nonzero(dw) == 1
 
 
 def test_geometry_of_configs():

@@ -61,68 +61,31 @@ __global__ void permute_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, co
     }
 }
 
-// ------------------------------------------------------- INT4O, batch <= 7
+// ---------------------------------------------------- INT4O, vector ALU (b <= 4)
 
 struct Int4oArgs {
-    const uint4* codes;     // [N4][4*G4] chunks of 16 bytes
-    const uint2* scales;    // [N4/4][G4] x 4 fp16
-    const uint4* wout;      // [N4][n_out8/8] chunks of 8 fp16
-    const uint16_t* xp;     // [b][xp_len]
+    const uint4* codes;     // [tiles][G4][4 chunks][16 rows] x 16 bytes
+    const uint16_t* scales; // [tiles][G4][16] fp16
+    const uint4* wout;      // [tiles][no8][16] chunks of 8 fp16
+    const uint16_t* xp;     // [b][xp_len] permuted, split activations
     uint16_t* y;            // [b][ldy]
     int N, G4, no8, xp_len, ldy;
 };
 
-// One wave per quad of four output rows; lanes stride over the rows' 16-byte
-// chunks (a chunk = 32 background channels of one group).
-template <int B>
-__global__ __launch_bounds__(64) void qgemv_int4o_valu(Int4oArgs a) {
-    constexpr int U = B <= 4 ? 4 : 2;
-    const int lane = threadIdx.x;
-    QuadTask t;
-    t.codes = a.codes;
-    t.scales = a.scales;
-    t.wout = a.wout;
-    t.CPR = 4 * a.G4;
-    t.no8 = a.no8;
-    t.nchunks = t.CPR + t.no8;
-    t.IT = (t.nchunks + 63) >> 6;
-    t.q0 = blockIdx.x;
-    t.qstride = 1;
-    t.nq = 1;
-    Slots<U> slots;
-    prefetch_items<true, U>(t, lane, slots);
-    stream_task<true, B, U>(t, slots, (gx_ptr)a.xp, a.xp_len, 128 * a.G4, lane, U, [&](int q, float out) {
-        if (lane < 4 * B) {
-            const int r = lane / B, b = lane % B, n = 4 * q + r;
-            if (n < a.N) *gptr(a.y + (int64_t)b * a.ldy + n) = f_to_h(out);
-        }
-    });
-}
-
-// ------------------------------- INT4O, batch <= 7, permutation in the kernel
-
-// The activation permutation and split folded into the product: a workgroup
-// of GX_WAVES waves reads the activations in their natural channel order
-// (coalesced 16-byte loads of 8 channels, together with the 8 channels'
-// positions in the permuted row) and scatters them into LDS, where they form
-// the permuted, zero-padded row that the waves' quads then read.  The weight
-// loads of every wave are issued right after the activation loads, so the
-// staging costs no extra memory round trip.
-constexpr int GX_WAVES = 4;
-constexpr int GX_THREADS = 64 * GX_WAVES;
-constexpr int GX_LDS_BYTES = 64 * 1024;
-
-struct Int4oGxArgs {
-    Int4oArgs p;             // p.xp unused
-    const uint16_t* x;       // [b][ldx], natural channel order
-    const uint16_t* pos;     // [round_up(K, 8)] position of each channel in the permuted row (0xFFFF: none)
-    int K, K_bg, n_out, ldx, qpw;   // qpw: quads per wave
+// Activations in their natural channel order and the position of every
+// channel in the permuted row (the permutation folded into the product).
+struct GatherArgs {
+    const uint16_t* x;      // [b][ldx]
+    const uint16_t* pos;    // [round_up(K, 8)], 0xFFFF: no position
+    int K, K_bg, n_out, ldx;
 };
+
+constexpr int TILE_WINDOW = 8;              // groups of weights in flight per wave
 
 // Write 8 channels (one 16-byte chunk per batch row) to their positions in
 // the staged row; positions outside the row (table padding) are skipped.
 template <int B>
-__device__ __forceinline__ void gx_scatter(uint16_t* xs, int xp_len, const uint4 (&xv)[B], uint4 pv) {
+__device__ __forceinline__ void scatter8(uint16_t* xs, int xp_len, const uint4 (&xv)[B], uint4 pv) {
     const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -137,70 +100,174 @@ __device__ __forceinline__ void gx_scatter(uint16_t* xs, int xp_len, const uint4
     }
 }
 
-template <int B>
-__global__ __launch_bounds__(GX_THREADS) void qgemv_int4o_gx(Int4oGxArgs a) {
+// A workgroup of T x S waves owns T tiles of 16 rows; the S waves of a tile
+// take the groups g = s, s + S, ... of every row.  Lane l holds row l & 15 of
+// its tile and chunk c = l >> 4 (32 channels) of each of its groups, so a
+// wave's weight load is one contiguous kilobyte (a tile's group block), and
+// the 16 lanes of a chunk read the same activations (an LDS broadcast).  The
+// activation rows are staged in LDS once per workgroup - copied from the
+// permuted row, or (GATHER) scattered from the natural-order row through the
+// channel-position table - while the first TILE_WINDOW groups of weights are
+// already in flight.  Weights and scales stream through a window of register
+// slots refilled unconditionally (past the last group the refill rereads it),
+// so every wait on a slot counts loads exactly.  Lane sums meet over the four
+// chunks with cross-lane shuffles and over the S waves in LDS, in a fixed
+// order.
+template <int B, int T, int S, bool GATHER>
+__global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, GatherArgs ga) {
     extern __shared__ __align__(16) uint16_t xs[];   // [B][xp_len]
-    constexpr int U = B <= 4 ? 4 : 2;
-    constexpr int SC = B == 1 ? 4 : B == 2 ? 2 : 1;   // activation chunks per thread per pass
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int xp_len = a.p.xp_len, bg_len = 128 * a.p.G4;
-    const int quads = (a.p.N + 3) >> 2;
-    // quads base + wave, base + wave + GX_WAVES, ... (qpw of them, within N)
-    const int base = blockIdx.x * GX_WAVES * a.qpw;
-    const int q0 = base + wave;
-    const int last = min(quads, base + GX_WAVES * a.qpw);
-    QuadTask t;
-    t.codes = a.p.codes;
-    t.scales = a.p.scales;
-    t.wout = a.p.wout;
-    t.CPR = 4 * a.p.G4;
-    t.no8 = a.p.no8;
-    t.nchunks = t.CPR + t.no8;
-    t.IT = (t.nchunks + 63) >> 6;
-    t.q0 = q0 < last ? q0 : 0;              // a wave without quads streams quad 0's first item and ignores it
-    t.qstride = GX_WAVES;
-    t.nq = q0 < last ? (last - 1 - q0) / GX_WAVES + 1 : 0;
+    __shared__ float red[S > 1 ? T * S : 1][B][16];
+    constexpr int W = T * S, NT = 64 * W, P = TILE_WINDOW;
+    constexpr int SC = 4;                            // staged pieces per thread issued before the weights
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tile = wave / S, s = wave % S;
+    const int m = lane & 15, c = lane >> 4;
+    const int tiles = (a.N + 15) >> 4;
+    const int t16 = blockIdx.x * T + tile;
+    const bool tile_ok = t16 < tiles;
+    const int tb = tile_ok ? t16 : 0;
+    const int G4 = a.G4, xp_len = a.xp_len, bg_len = 128 * G4;
 
-    const int nc = (a.K + 7) >> 3;          // 8-channel activation chunks
-    const g_u32x4* xg = (const g_u32x4*)a.x;
-    const g_u32x4* pg = (const g_u32x4*)a.pos;
-    const int ldx16 = a.ldx >> 3;
-    // first pass of activation loads (unconditional; out-of-range chunks reload chunk 0)
-    uint4 xv[SC][B], pv[SC];
+    // 1. activation loads (16-byte pieces; unconditional, out-of-range pieces reread piece 0)
+    uint4 pv[SC];
+    uint4 xv[SC][GATHER ? B : 1];
+    const int npieces = GATHER ? (ga.K + 7) >> 3 : B * xp_len / 8;
+    const int ldx16 = GATHER ? ga.ldx >> 3 : 0;
 #pragma unroll
     for (int i = 0; i < SC; ++i) {
-        const int c = tid + i * GX_THREADS;
-        const int cc = c < nc ? c : 0;
-        pv[i] = as_uint4(pg[cc]);
+        const int p = tid + i * NT;
+        const int pp = p < npieces ? p : 0;
+        if (GATHER) {
+            pv[i] = as_uint4(((const g_u32x4*)ga.pos)[pp]);
 #pragma unroll
-        for (int b = 0; b < B; ++b) xv[i][b] = as_uint4(xg[b * ldx16 + cc]);
+            for (int b = 0; b < B; ++b) xv[i][b] = as_uint4(((const g_u32x4*)ga.x)[b * ldx16 + pp]);
+        } else {
+            xv[i][0] = as_uint4(((const g_u32x4*)a.xp)[pp]);
+        }
     }
-    Slots<U> slots;
-    prefetch_items_fixed<true, U>(t, lane, slots);
-    // padding of the permuted row: [K_bg, bg_len) and [bg_len + n_out, xp_len)
-    for (int k = a.K_bg + tid; k < bg_len; k += GX_THREADS)
+
+    // 2. weight window: this wave's groups s, s + S, ... (J of them)
+    const int J = G4 > s ? (G4 - 1 - s) / S + 1 : 0;
+    const uint4* wb = a.codes + (int64_t)tb * G4 * 64 + c * 16 + m;
+    const uint16_t* sb = a.scales + (int64_t)tb * G4 * 16 + m;
+    uint4 wq[P];
+    uint32_t sq[P];
+    if (J > 0) {
 #pragma unroll
-        for (int b = 0; b < B; ++b) xs[b * xp_len + k] = 0;
-    for (int k = bg_len + a.n_out + tid; k < xp_len; k += GX_THREADS)
+        for (int u = 0; u < P; ++u) {
+            const int g = s + S * (u < J ? u : J - 1);
+            wq[u] = gload_nt(wb + (int64_t)g * 64);
+            sq[u] = *gptr(sb + g * 16);
+        }
+    }
+
+    // 3. activations into LDS
 #pragma unroll
-        for (int b = 0; b < B; ++b) xs[b * xp_len + k] = 0;
+    for (int i = 0; i < SC; ++i) {
+        const int p = tid + i * NT;
+        if (p < npieces) {
+            if (GATHER) {
+                uint4 x1[B];
 #pragma unroll
-    for (int i = 0; i < SC; ++i)
-        if (tid + i * GX_THREADS < nc) gx_scatter<B>(xs, xp_len, xv[i], pv[i]);
-    for (int c = tid + SC * GX_THREADS; c < nc; c += GX_THREADS) {
-        uint4 xv1[B];
-        const uint4 pv1 = as_uint4(pg[c]);
+                for (int b = 0; b < B; ++b) x1[b] = xv[i][b];
+                scatter8<B>(xs, xp_len, x1, pv[i]);
+            } else {
+                *(__attribute__((address_space(3))) u32x4*)&xs[8 * p] =
+                    (u32x4){xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w};
+            }
+        }
+    }
+    for (int p = tid + SC * NT; p < npieces; p += NT) {
+        if (GATHER) {
+            uint4 x1[B];
+            const uint4 p1 = as_uint4(((const g_u32x4*)ga.pos)[p]);
 #pragma unroll
-        for (int b = 0; b < B; ++b) xv1[b] = as_uint4(xg[b * ldx16 + c]);
-        gx_scatter<B>(xs, xp_len, xv1, pv1);
+            for (int b = 0; b < B; ++b) x1[b] = as_uint4(((const g_u32x4*)ga.x)[b * ldx16 + p]);
+            scatter8<B>(xs, xp_len, x1, p1);
+        } else {
+            const uint4 v = as_uint4(((const g_u32x4*)a.xp)[p]);
+            *(__attribute__((address_space(3))) u32x4*)&xs[8 * p] = (u32x4){v.x, v.y, v.z, v.w};
+        }
+    }
+    if (GATHER) {
+        // padding of the permuted row: [K_bg, bg_len) and [bg_len + n_out, xp_len)
+        for (int k = ga.K_bg + tid; k < bg_len; k += NT)
+#pragma unroll
+            for (int b = 0; b < B; ++b) xs[b * xp_len + k] = 0;
+        for (int k = bg_len + ga.n_out + tid; k < xp_len; k += NT)
+#pragma unroll
+            for (int b = 0; b < B; ++b) xs[b * xp_len + k] = 0;
     }
     lds_barrier();
-    stream_task<true, B, U>(t, slots, (lx_ptr)xs, xp_len, bg_len, lane, U, [&](int q, float out) {
-        if (lane < 4 * B) {
-            const int r = lane / B, b = lane % B, n = 4 * q + r;
-            if (n < a.p.N) *gptr(a.p.y + (int64_t)b * a.p.ldy + n) = f_to_h(out);
+
+    // 4. background groups
+    const lx_ptr xl = (lx_ptr)xs;
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    for (int j0 = 0; j0 < J; j0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int j = j0 + u;
+            const uint4 w = wq[u];
+            const float sc = h_to_f((uint16_t)sq[u]);
+            const int gn = s + S * (j + P < J ? j + P : J - 1);
+            wq[u] = gload_nt(wb + (int64_t)gn * 64);
+            sq[u] = *gptr(sb + gn * 16);
+            if (j < J) {
+                const int g = s + S * j;
+                uint4 xg[B][4];
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) xg[b][q] = load_x16(xl + b * xp_len + 128 * g + 32 * c + 8 * q);
+                int4o_row_chunk<B>(w, sc, xg, acc);
+            }
         }
-    });
+    }
+
+    // 5. FP16 outlier columns: step st covers outlier chunks 4 st .. 4 st + 3 (lane chunk c)
+    const uint4* ob = a.wout + (int64_t)tb * a.no8 * 16 + m;
+    for (int st = s; 32 * st < 8 * a.no8; st += S) {
+        const int i8 = 4 * st + c;
+        const bool in = i8 < a.no8;
+        const uint4 wo = gload_u4(ob + (int64_t)(in ? i8 : 0) * 16);
+        if (in) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint4 xo = load_x16(xl + b * xp_len + bg_len + 8 * i8);
+                float v = acc[b];
+                v = dot2(as_h2(wo.x), as_h2(xo.x), v);
+                v = dot2(as_h2(wo.y), as_h2(xo.y), v);
+                v = dot2(as_h2(wo.z), as_h2(xo.z), v);
+                v = dot2(as_h2(wo.w), as_h2(xo.w), v);
+                acc[b] = v;
+            }
+        }
+    }
+
+    // 6. sums over the four chunk lanes, then over the S waves of the tile
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = sum_over_chunks(acc[b]);
+    if (S > 1) {
+        if (c == 0)
+#pragma unroll
+            for (int b = 0; b < B; ++b) red[wave][b][m] = acc[b];
+        __syncthreads();
+        if (s == 0 && c == 0)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                float v = acc[b];
+                for (int p = 1; p < S; ++p) v += red[wave + p][b][m];
+                acc[b] = v;
+            }
+    }
+    if (s == 0 && c == 0 && tile_ok) {
+        const int n = t16 * 16 + m;
+        if (n < a.N)
+#pragma unroll
+            for (int b = 0; b < B; ++b) *gptr(a.y + (int64_t)b * a.ldy + n) = f_to_h(acc[b]);
+    }
 }
 
 // --------------------------------------------------------- INT8, batch <= 8
@@ -268,108 +335,227 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
 
 // ------------------------------------------------ INT4O, matrix cores (b >= 8)
 
-// A workgroup of four waves owns 16 output rows; wave w takes the groups
-// g = w, w + 4, ...  Lane l holds row l & 15 of the 16-row tile and the
-// 16-byte chunk l >> 4 of each group (32 channels) - exactly the A operand of
-// v_mfma_f32_16x16x32_f16 for four k-steps: the unscaled pairs feed steps 0
-// and 2, the pairs that carry 16 x code feed steps 1 and 3 into a second
-// accumulator that is divided by 16 before the group scale is applied.  The B
-// operand (activations, batch column l & 15) is read from memory in the same
-// channel order.  Partial sums of the four waves meet in LDS.
-template <int NBT>
-__global__ __launch_bounds__(256) void qgemm_int4o_mfma(Int4oArgs a, int b) {
-    __shared__ float red[4][NBT][16][17];
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+// A workgroup of T x S waves owns T tiles of 16 output rows; the S waves of a
+// tile split the groups of every K chunk (CH groups) between them.  Lane l
+// holds row l & 15 of its tile and the 16-byte chunk l >> 4 of each group (32
+// channels) - exactly the A operand of v_mfma_f32_16x16x32_f16 for four
+// k-steps: the unscaled pairs feed steps 0 and 2, the pairs that carry
+// 16 x code feed steps 1 and 3 into a second accumulator that is divided by
+// 16 before the group scale is applied.
+//
+// The B operand (activations, batch column l & 15) is read from LDS.  The
+// workgroup stages each K chunk of the permuted activations (all b columns)
+// once for its T tiles, two chunks ahead of use: the loads of chunk k + 2 are
+// issued when chunk k starts, held in registers, and written to LDS at the end
+// of chunk k + 1, so they return in the shadow of the weight stream instead of
+// stalling it.  Each wave streams its weights and scales through a window of
+// P register slots that runs ahead across chunk boundaries.  Every load is
+// unconditional (clamped to a valid address, results unused), so the number
+// of loads in flight is the same on every path and each wait is exact.
+// Partial sums of the S waves of a tile meet in LDS.
+template <int NBT, int T, int S>
+__global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int b) {
+    constexpr int W = T * S;
+    constexpr int CHB = NBT <= 2 ? 4 : 2;             // chunk size bound by the LDS of wide batches
+    constexpr int CH = S > CHB ? S : CHB;             // groups per chunk
+    constexpr int KC = CH / S;                        // groups per wave per chunk
+    constexpr int P = NBT == 1 ? 8 : 4;               // weight window (groups), whole chunks
+    static_assert(P % KC == 0, "window must hold whole chunks");
+    constexpr int UNR = P / KC < 2 ? 2 : P / KC;      // chunks per unrolled loop body (even)
+    static_assert(UNR % 2 == 0 && UNR % (P / KC) == 0, "unroll");
+    constexpr int COLS = 16 * NBT;                    // batch columns of the B operand
+    constexpr int XS = CH * 128 + 8;                  // LDS column stride (fp16), padded against bank conflicts
+    constexpr int PPC = CH * 16;                      // 16-byte pieces of one column per chunk
+    constexpr int NPT = (COLS * PPC + 64 * W - 1) / (64 * W);   // staged pieces per thread (b = COLS)
+    constexpr int RED = 4 * W * NBT * 16 * 17;
+    constexpr int XSB = 2 * 2 * COLS * XS;
+    __shared__ __align__(16) uint16_t lds[(XSB > RED ? XSB : RED) / 2];
+    uint16_t (*xs)[COLS][XS] = reinterpret_cast<uint16_t (*)[COLS][XS]>(lds);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int tile = wave / S, s = wave % S;
     const int m = lane & 15;           // row within the tile (A) / batch column (B)
     const int c = lane >> 4;           // 32-channel chunk of the group / k-block
-    const int row = blockIdx.x * 16 + m;
-    const int N4 = (a.N + 3) & ~3;
-    const bool row_ok = row < N4;
-    const int CPR = a.G4 * 4;
-    const uint4* wrow = a.codes + (int64_t)row * CPR;
-    const int quad0 = blockIdx.x * 4;  // first quad of the tile
+    const int tiles = (a.N + 15) >> 4;
+    const int t16 = blockIdx.x * T + tile;
+    const bool tile_ok = t16 < tiles;
+    const int tb = tile_ok ? t16 : 0;
+    const int trow0 = t16 * 16;
+    const int G4 = a.G4, xp_len = a.xp_len;
+    const int nchunks = (G4 + CH - 1) / CH;
+    const int bgl = 128 * G4;
 
     f4 acc[NBT];
 #pragma unroll
     for (int t = 0; t < NBT; ++t) acc[t] = (f4){0.f, 0.f, 0.f, 0.f};
 
-    for (int g = wave; g < a.G4; g += 4) {
-        uint4 w = row_ok ? gload_nt(wrow + 4 * g + c) : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-        const uint32_t bias = bias_reg();
-        Int4Pairs p[4];
+    // columns b .. COLS-1 of both buffers hold zeros for the whole kernel
+    for (int e = tid; e < 2 * COLS * XS; e += 64 * W) {
+        const int col = (e / XS) % COLS;
+        if (col >= b) lds[e] = 0;
+    }
+
+    // staging: piece p of chunk k -> column p / PPC, channels 8 (p % PPC) of the chunk
+    uint4 stg[2][NPT];
+    auto stage_load = [&](uint4 (&r)[NPT], int k) {
+        const int kk = k < nchunks ? k : 0;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d], bias);
-        // A operands of the four k-steps (8 fp16 each)
-        h8 A[4];
-#pragma unroll
-        for (int P = 0; P < 2; ++P) {
-            const Int4Pairs& e0 = p[2 * P];
-            const Int4Pairs& e1 = p[2 * P + 1];
-            A[2 * P + 0] = (h8){e0.lo0[0], e0.lo0[1], e0.lo1[0], e0.lo1[1], e1.lo0[0], e1.lo0[1], e1.lo1[0], e1.lo1[1]};
-            A[2 * P + 1] = (h8){e0.hi0[0], e0.hi0[1], e0.hi1[0], e0.hi1[1], e1.hi0[0], e1.hi0[1], e1.hi1[0], e1.hi1[1]};
+        for (int i = 0; i < NPT; ++i) {
+            const int p = tid + i * 64 * W;
+            const int col = p / PPC, ch = kk * CH * 128 + 8 * (p % PPC);
+            const bool ok = col < b && ch < bgl;
+            r[i] = load_x16((gx_ptr)(a.xp + (ok ? (int64_t)col * xp_len + ch : 0)));
         }
-        // per-row scales of this group for the four D rows this lane holds
-        float s[4];
+    };
+    auto stage_store = [&](const uint4 (&r)[NPT], int buf, int k) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * c + i;      // D row held by this lane
-            const int q = quad0 + (rr >> 2);
-            s[i] = (q * 4 < N4) ? h_to_f(*gptr(reinterpret_cast<const uint16_t*>(a.scales) + ((int64_t)q * a.G4 + g) * 4 + (rr & 3))) : 0.0f;
-        }
-#pragma unroll
-        for (int t = 0; t < NBT; ++t) {
-            const int col = t * 16 + m;    // batch column of the B operand
-            h8 Bv[4];
+        for (int i = 0; i < NPT; ++i) {
+            const int p = tid + i * 64 * W;
+            const int col = p / PPC, off = p % PPC;
             if (col < b) {
-                const gx_ptr xs = (gx_ptr)(a.xp + (int64_t)col * a.xp_len + 128 * g + 32 * c);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Bv[j] = __builtin_bit_cast(h8, load_x16(xs + 8 * j));
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Bv[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+                const bool ok = k * CH * 128 + 8 * off < bgl;   // past the last group: zeros
+                *(__attribute__((address_space(3))) u32x4*)&xs[buf][col][8 * off] =
+                    ok ? (u32x4){r[i].x, r[i].y, r[i].z, r[i].w} : (u32x4){0u, 0u, 0u, 0u};
             }
-            f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
-            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], Bv[0], lo, 0, 0, 0);
-            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], Bv[1], hi, 0, 0, 0);
-            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], Bv[2], lo, 0, 0, 0);
-            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], Bv[3], hi, 0, 0, 0);
+        }
+    };
+
+    // this wave's groups: in chunk k, k*CH + s*KC + kk (kk < KC); j counts them
+    const int full = G4 / CH, rem = G4 - full * CH;
+    const int J = full * KC + min(max(rem - s * KC, 0), KC);
+    auto group_of = [&](int j) { return (j / KC) * CH + s * KC + (j % KC); };
+    // tile layout: lane (m, c) reads 16 bytes of the tile's 1 KB block of group g,
+    // and the scales of D rows 4c .. 4c + 3 (8 contiguous bytes)
+    const uint4* wld = a.codes + (int64_t)tb * G4 * 64 + c * 16 + m;
+    const uint2* sld = reinterpret_cast<const uint2*>(a.scales) + (int64_t)tb * G4 * 4 + c;
+
+    uint4 wq[P];
+    uint2 sc[P];
+    if (nchunks > 0) {                 // G4 > 0: group 0 exists
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(s[i], fmaf(hi[i], 0.0625f, lo[i]), acc[t][i]);
+        for (int u = 0; u < P; ++u) {
+            const int g = u < J ? group_of(u) : 0;
+            wq[u] = gload_nt(wld + (int64_t)g * 64);
+            sc[u] = gload_u2(sld + g * 4);
+        }
+        stage_load(stg[0], 0);
+        stage_load(stg[1], 1);
+        stage_store(stg[0], 0, 0);
+    }
+    __syncthreads();
+    const uint32_t bias = bias_reg();
+    for (int k0 = 0; k0 < nchunks; k0 += UNR) {
+#pragma unroll
+        for (int cb = 0; cb < UNR; ++cb) {
+            const int k = k0 + cb;     // k & 1 == cb & 1
+            if (k < nchunks) {
+                stage_load(stg[cb & 1], k + 2);          // chunk k's registers are free again
+#pragma unroll
+                for (int kk = 0; kk < KC; ++kk) {
+                    const int u = (cb * KC + kk) % P;
+                    const int j = k * KC + kk;
+                    const int g = k * CH + s * KC + kk;
+                    const bool gv = g < G4;
+                    const uint32_t wd[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
+                    const float sf[4] = {h_to_f((uint16_t)(sc[u].x & 0xFFFF)), h_to_f((uint16_t)(sc[u].x >> 16)),
+                                         h_to_f((uint16_t)(sc[u].y & 0xFFFF)), h_to_f((uint16_t)(sc[u].y >> 16))};
+                    const int gn = j + P < J ? group_of(j + P) : 0;
+                    wq[u] = gload_nt(wld + (int64_t)gn * 64);
+                    sc[u] = gload_u2(sld + gn * 4);
+                    Int4Pairs pr[4];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) pr[d] = int4_pairs(wd[d], bias);
+                    h8 A[4];
+#pragma unroll
+                    for (int Pp = 0; Pp < 2; ++Pp) {
+                        const Int4Pairs& e0 = pr[2 * Pp];
+                        const Int4Pairs& e1 = pr[2 * Pp + 1];
+                        A[2 * Pp + 0] = (h8){e0.lo0[0], e0.lo0[1], e0.lo1[0], e0.lo1[1],
+                                             e1.lo0[0], e1.lo0[1], e1.lo1[0], e1.lo1[1]};
+                        A[2 * Pp + 1] = (h8){e0.hi0[0], e0.hi0[1], e0.hi1[0], e0.hi1[1],
+                                             e1.hi0[0], e1.hi0[1], e1.hi1[0], e1.hi1[1]};
+                    }
+                    const int gl = s * KC + kk;  // group within the chunk
+#pragma unroll
+                    for (int t = 0; t < NBT; ++t) {
+                        const lx_ptr xb = (lx_ptr)&xs[cb & 1][16 * t + m][128 * gl + 32 * c];
+                        h8 Bv[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
+                        f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
+                        lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], Bv[0], lo, 0, 0, 0);
+                        hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], Bv[1], hi, 0, 0, 0);
+                        lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], Bv[2], lo, 0, 0, 0);
+                        hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], Bv[3], hi, 0, 0, 0);
+                        if (gv)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(sf[i], fmaf(hi[i], 0.0625f, lo[i]), acc[t][i]);
+                    }
+                }
+                // chunk k + 1 (loaded during chunk k - 1) into the other buffer, last read in chunk k - 1
+                if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1, k + 1);
+                lds_barrier();
+            }
         }
     }
 
-    // FP16 outlier columns, 32 per k-step, split over the waves
-    const uint16_t* xo_base = a.xp + 128 * a.G4;
+    // FP16 outlier columns, 32 per k-step, split over the S waves of the tile;
+    // up to four k-steps' loads in flight at once
+    const uint16_t* xo_base = a.xp + bgl;
     const int n_o8 = a.no8 * 8;
-    for (int st = wave; st * 32 < n_o8; st += 4) {
-        const int col0 = 32 * st + 8 * c;
-        h8 Av = (h8){0, 0, 0, 0, 0, 0, 0, 0};
-        if (row_ok && col0 < n_o8)
-            Av = __builtin_bit_cast(h8, gload_u4(a.wout + (int64_t)row * a.no8 + (col0 >> 3)));
+    for (int st0 = s; st0 * 32 < n_o8; st0 += 4 * S) {
+        h8 Av[4], Bo[4][NBT];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col0 = 32 * (st0 + q * S) + 8 * c;
+            const bool in = col0 < n_o8;
+            Av[q] = __builtin_bit_cast(h8, gload_u4(a.wout + ((int64_t)tb * a.no8 + (in ? col0 >> 3 : 0)) * 16 + m));
+            if (!in) Av[q] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < NBT; ++t) {
+                const int bc = t * 16 + m;
+                const bool okb = bc < b && in;
+                Bo[q][t] = __builtin_bit_cast(h8, load_x16((gx_ptr)(xo_base + (okb ? (int64_t)bc * xp_len + col0 : 0))));
+                if (!okb) Bo[q][t] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int t = 0; t < NBT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av[q], Bo[q][t], acc[t], 0, 0, 0);
+    }
+
+    // lane (c, m) holds rows 4c .. 4c + 3 of the tile, batch column 16t + m
+    if (S > 1) {
+        typedef float RedTile[NBT][16][17];
+        RedTile* red = reinterpret_cast<RedTile*>(lds);
+        __syncthreads();                               // the staging buffers are dead
+#pragma unroll
+        for (int t = 0; t < NBT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][t][4 * c + i][m] = acc[t][i];
+        __syncthreads();
+        if (s == 0) {
+#pragma unroll
+            for (int t = 0; t < NBT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = acc[t][i];
+                    for (int p = 1; p < S; ++p) v += red[wave + p][t][4 * c + i][m];
+                    acc[t][i] = v;
+                }
+        }
+    }
+    if (s == 0 && tile_ok) {
 #pragma unroll
         for (int t = 0; t < NBT; ++t) {
             const int bc = t * 16 + m;
-            h8 Bv = (h8){0, 0, 0, 0, 0, 0, 0, 0};
-            if (bc < b && col0 < n_o8)
-                Bv = __builtin_bit_cast(h8, load_x16((gx_ptr)(xo_base + (int64_t)bc * a.xp_len + col0)));
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Bv, acc[t], 0, 0, 0);
-        }
-    }
-
 #pragma unroll
-    for (int t = 0; t < NBT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][t][4 * c + i][m] = acc[t][i];
-    __syncthreads();
-    for (int e = threadIdx.x; e < NBT * 256; e += 256) {
-        const int t = e >> 8, rr = (e >> 4) & 15, col = e & 15;
-        const int bc = t * 16 + col;
-        const int n = blockIdx.x * 16 + rr;
-        if (bc < b && n < a.N) {
-            float v = red[0][t][rr][col] + red[1][t][rr][col] + red[2][t][rr][col] + red[3][t][rr][col];
-            *gptr(a.y + (int64_t)bc * a.ldy + n) = f_to_h(v);
+            for (int i = 0; i < 4; ++i) {
+                const int n = trow0 + 4 * c + i;
+                if (bc < b && n < a.N) *gptr(a.y + (int64_t)bc * a.ldy + n) = f_to_h(acc[t][i]);
+            }
         }
     }
 }
@@ -392,17 +578,29 @@ int launch_status(hipError_t e) {
     return WOQ_OK;
 }
 
-template <int B>
-hipError_t launch_int4o_valu(const Int4oArgs& a, int quads, hipStream_t s) {
-    return launch_kernel(qgemv_int4o_valu<B>, dim3(quads), dim3(64), 0, s, a);
+// Tiles per workgroup and waves per tile of the vector kernel (measured on
+// MI355X over the 3B- and 70B-shaped products): narrow products split each
+// tile's groups over four waves so that enough loads are in flight on every
+// compute unit; from 1024 tiles on, two tiles share a workgroup (one staged
+// copy of the activations) and each tile takes two waves.
+template <int B, bool GATHER>
+hipError_t launch_int4o_tile(const Int4oArgs& a, const GatherArgs& ga, hipStream_t s) {
+    const int tiles = (int)woq::ceil_div(a.N, 16);
+    const size_t lds = (size_t)B * a.xp_len * sizeof(uint16_t);
+    if (tiles >= 1024)
+        return launch_kernel(qgemv_int4o_tile<B, 2, 2, GATHER>, dim3((unsigned)woq::ceil_div(tiles, 2)), dim3(256),
+                             lds, s, a, ga);
+    return launch_kernel(qgemv_int4o_tile<B, 1, 4, GATHER>, dim3((unsigned)tiles), dim3(256), lds, s, a, ga);
 }
 
-template <int B>
-hipError_t launch_int4o_gx(const Int4oGxArgs& a, hipStream_t s) {
-    const int quads = (int)woq::ceil_div(a.p.N, 4);
-    const int grid = (int)woq::ceil_div(quads, (int64_t)GX_WAVES * a.qpw);
-    const size_t lds = (size_t)B * a.p.xp_len * sizeof(uint16_t);
-    return launch_kernel(qgemv_int4o_gx<B>, dim3(grid), dim3(GX_THREADS), lds, s, a);
+template <bool GATHER>
+hipError_t launch_int4o_tile_b(const Int4oArgs& a, const GatherArgs& ga, int64_t b, hipStream_t s) {
+    switch (b) {
+        case 1: return launch_int4o_tile<1, GATHER>(a, ga, s);
+        case 2: return launch_int4o_tile<2, GATHER>(a, ga, s);
+        case 3: return launch_int4o_tile<3, GATHER>(a, ga, s);
+        default: return launch_int4o_tile<4, GATHER>(a, ga, s);
+    }
 }
 
 template <int B>
@@ -410,10 +608,28 @@ hipError_t launch_int8_valu(const Int8Args& a, int quads, hipStream_t s) {
     return launch_kernel(qgemv_int8_valu<B>, dim3(quads), dim3(64), 0, s, a);
 }
 
+template <int NBT, int T, int S>
+hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s) {
+    return launch_kernel(qgemm_int4o_mfma<NBT, T, S>, dim3((unsigned)woq::ceil_div(tiles, T)), dim3(64 * T * S), 0, s,
+                         a, b);
+}
+
+// Tiles per workgroup (T) and waves per tile (S) of the matrix-core kernel,
+// measured on MI355X over the 3B- and 70B-shaped products: the widest
+// products give each wave whole rows and share the staged activations among
+// eight tiles; narrower ones split K over more waves so that every compute
+// unit has loads in flight.
 template <int NBT>
 hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
-    const int tiles = (int)woq::ceil_div(woq::round_up(a.N, 4), 16);
-    return launch_kernel(qgemm_int4o_mfma<NBT>, dim3(tiles), dim3(256), 0, s, a, b);
+    const int tiles = (int)woq::ceil_div(a.N, 16);
+    if (tiles >= 2048) return launch_int4o_mfma_ts<NBT, 8, 1>(a, b, tiles, s);
+    if constexpr (NBT >= 3) {
+        return launch_int4o_mfma_ts<NBT, 2, 2>(a, b, tiles, s);
+    } else {
+        if (tiles >= 640) return launch_int4o_mfma_ts<NBT, 4, 2>(a, b, tiles, s);
+        if (tiles >= 256) return launch_int4o_mfma_ts<NBT, 2, 4>(a, b, tiles, s);
+        return launch_int4o_mfma_ts<NBT, 1, 8>(a, b, tiles, s);
+    }
 }
 
 int check_int4o_w(const woq_int4o_w* w) {
@@ -427,7 +643,7 @@ int check_int4o_w(const woq_int4o_w* w) {
 Int4oArgs make_int4o_args(const woq_int4o_w* w, const uint16_t* xp, uint16_t* y, int64_t ldy) {
     Int4oArgs a;
     a.codes = reinterpret_cast<const uint4*>(w->codes);
-    a.scales = reinterpret_cast<const uint2*>(w->scales);
+    a.scales = reinterpret_cast<const uint16_t*>(w->scales);
     a.wout = reinterpret_cast<const uint4*>(w->w_out);
     a.xp = xp;
     a.y = y;
@@ -470,21 +686,10 @@ int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_
     int st = int4o_common_checks(w, xp, b, y, ldy);
     if (st) return st;
     if (b == 0 || w->N == 0) return WOQ_OK;
-    if (b >= 8) return woq_qgemm_int4o(w, xp, b, y, ldy, stream);
+    if (!woq::int4o_use_valu(w->N, w->geom, b)) return woq_qgemm_int4o(w, xp, b, y, ldy, stream);
     Int4oArgs a = make_int4o_args(w, xp, y, ldy);
-    const int quads = (int)woq::ceil_div(w->N, 4);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    switch (b) {
-        case 1: e = launch_int4o_valu<1>(a, quads, s); break;
-        case 2: e = launch_int4o_valu<2>(a, quads, s); break;
-        case 3: e = launch_int4o_valu<3>(a, quads, s); break;
-        case 4: e = launch_int4o_valu<4>(a, quads, s); break;
-        case 5: e = launch_int4o_valu<5>(a, quads, s); break;
-        case 6: e = launch_int4o_valu<6>(a, quads, s); break;
-        default: e = launch_int4o_valu<7>(a, quads, s); break;
-    }
-    return launch_status(e);
+    GatherArgs ga = {};
+    return launch_status(launch_int4o_tile_b<false>(a, ga, b, (hipStream_t)stream));
 }
 
 int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, const uint16_t* pos, int64_t b,
@@ -497,35 +702,20 @@ int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, cons
     if (!x || !pos || !y) return WOQ_EINVAL;
     if (!woq::aligned16(x) || !woq::aligned16(pos) || (ldx & 7) || ((uintptr_t)y & 1u)) return WOQ_EALIGN;
     if (!woq_qgemv_int4o_x_supported(&g, b)) return WOQ_EUNSUPPORTED;
-    Int4oGxArgs a;
-    a.p = make_int4o_args(w, nullptr, y, ldy);
-    a.x = x;
-    a.pos = pos;
-    a.K = (int)g.K;
-    a.K_bg = (int)g.K_bg;
-    a.n_out = (int)g.n_out;
-    a.ldx = (int)ldx;
-    // one quad per wave: more quads per workgroup would stage the activations
-    // fewer times but leaves fewer waves to keep loads in flight, which costs
-    // more (measured on the 70B-shaped products)
-    a.qpw = 1;
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    switch (b) {
-        case 1: e = launch_int4o_gx<1>(a, s); break;
-        case 2: e = launch_int4o_gx<2>(a, s); break;
-        case 3: e = launch_int4o_gx<3>(a, s); break;
-        case 4: e = launch_int4o_gx<4>(a, s); break;
-        case 5: e = launch_int4o_gx<5>(a, s); break;
-        case 6: e = launch_int4o_gx<6>(a, s); break;
-        default: e = launch_int4o_gx<7>(a, s); break;
-    }
-    return launch_status(e);
+    Int4oArgs a = make_int4o_args(w, nullptr, y, ldy);
+    GatherArgs ga;
+    ga.x = x;
+    ga.pos = pos;
+    ga.K = (int)g.K;
+    ga.K_bg = (int)g.K_bg;
+    ga.n_out = (int)g.n_out;
+    ga.ldx = (int)ldx;
+    return launch_status(launch_int4o_tile_b<true>(a, ga, b, (hipStream_t)stream));
 }
 
 int woq_qgemv_int4o_x_supported(const woq_int4o_geom* g, int64_t b) {
-    if (!g || b < 1 || b > 7) return 0;
-    return g->xp_len <= 65535 && b * g->xp_len * 2 <= GX_LDS_BYTES;
+    if (!g || b < 1 || b > 4) return 0;
+    return g->xp_len <= 65535 && b * g->xp_len * 2 <= woq::INT4O_VALU_LDS_BYTES;
 }
 
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy, void* stream) {

@@ -103,40 +103,36 @@ __device__ __forceinline__ void zero_acc(float (&acc)[4][B]) {
         for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 }
 
-// Dot products of one INT4O chunk (four rows, 32 channels) with B activation
-// rows xv (32 fp16 each).
+// Dot products of one INT4O chunk of one row (32 background channels of one
+// group) with B activation rows (the same 32 channels, fp16); the group scale s
+// multiplies this chunk's sum.  Pairs that carry 16 x code accumulate apart and
+// are divided by 16 (exact) before the two parts are added.
 template <int B>
-__device__ __forceinline__ void int4o_chunk(const uint4 (&w)[4], uint2 sc, const uint4 (&xv)[B][4],
-                                            float (&acc)[4][B]) {
-    const float s[4] = {h_to_f((uint16_t)(sc.x & 0xFFFF)), h_to_f((uint16_t)(sc.x >> 16)),
-                        h_to_f((uint16_t)(sc.y & 0xFFFF)), h_to_f((uint16_t)(sc.y >> 16))};
+__device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&xv)[B][4], float (&acc)[B]) {
     const uint32_t bias = bias_reg();
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    Int4Pairs p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
-        Int4Pairs p[4];
+    for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d], bias);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d], bias);
+    for (int b = 0; b < B; ++b) {
+        const uint32_t xw[16] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
+                                 xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w,
+                                 xv[b][2].x, xv[b][2].y, xv[b][2].z, xv[b][2].w,
+                                 xv[b][3].x, xv[b][3].y, xv[b][3].z, xv[b][3].w};
+        float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const uint32_t xw[16] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
-                                     xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w,
-                                     xv[b][2].x, xv[b][2].y, xv[b][2].z, xv[b][2].w,
-                                     xv[b][3].x, xv[b][3].y, xv[b][3].z, xv[b][3].w};
-            float lo = 0.0f, hi = 0.0f;
+        for (int P = 0; P < 2; ++P) {
 #pragma unroll
-            for (int P = 0; P < 2; ++P) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const Int4Pairs& q = p[2 * P + e];
-                    lo = dot2(q.lo0, as_h2(xw[8 * P + 2 * e + 0]), lo);
-                    lo = dot2(q.lo1, as_h2(xw[8 * P + 2 * e + 1]), lo);
-                    hi = dot2(q.hi0, as_h2(xw[8 * P + 4 + 2 * e + 0]), hi);
-                    hi = dot2(q.hi1, as_h2(xw[8 * P + 4 + 2 * e + 1]), hi);
-                }
+            for (int e = 0; e < 2; ++e) {
+                const Int4Pairs& q = p[2 * P + e];
+                lo = dot2(q.lo0, as_h2(xw[8 * P + 2 * e + 0]), lo);
+                lo = dot2(q.lo1, as_h2(xw[8 * P + 2 * e + 1]), lo);
+                hi = dot2(q.hi0, as_h2(xw[8 * P + 4 + 2 * e + 0]), hi);
+                hi = dot2(q.hi1, as_h2(xw[8 * P + 4 + 2 * e + 1]), hi);
             }
-            acc[r][b] = fmaf(s[r], fmaf(hi, 0.0625f, lo), acc[r][b]);
         }
+        acc[b] = fmaf(s, fmaf(hi, 0.0625f, lo), acc[b]);
     }
 }
 
@@ -197,35 +193,46 @@ __device__ __forceinline__ float quad_reduce(float (&acc)[4][B], int lane) {
     return out;
 }
 
+// Workgroup control barrier that waits only for this wave's LDS and scalar
+// memory operations, not for its outstanding vector loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+// Sum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 32-channel
+// chunks of a group that lanes c = l >> 4 hold for row l & 15).
+__device__ __forceinline__ float sum_over_chunks(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
 // ---------------------------------------------------------------------------
-// Pipelined streaming of a wave's quads.
+// Pipelined streaming of a wave's INT8 quads.
 //
 // A wave owns quads q0, q0 + qstride, ... (nq of them).  Each quad is a
-// sequence of chunk iterations: iteration i covers chunk c = lane + 64 i of
-// the quad's chunk space.  For INT4O the chunk space is the background chunks
-// [0, CPR) followed by the outlier chunks [CPR, CPR + no8); for INT8 it is the
-// code chunks [0, nchunks).  The wave walks the flat sequence of (quad,
-// iteration) items through a window of U register slots: the loads of item
-// t + U are issued as soon as item t has been consumed, so U items are always
-// in flight.  The first items can be issued early (prefetch) because the
-// weights do not depend on the activations.
+// sequence of chunk iterations: iteration i covers the 16-byte chunk
+// c = lane + 64 i of each of the quad's four rows, c < nchunks.  The wave
+// walks the flat sequence of (quad, iteration) items through a window of U
+// register slots: the loads of item t + U are issued as soon as item t has
+// been consumed, so U items are always in flight.  The first items can be
+// issued early (prefetch) because the weights do not depend on the
+// activations.
 //
-// Loads are issued unconditionally: a lane whose chunk lies outside the chunk
-// space reads a valid dummy address and ignores the result, so no slot
-// register is written on a divergent path (merging such writes would force a
-// wait for the load).
+// Loads are issued unconditionally: a lane whose chunk lies outside the row
+// reads a valid dummy address and ignores the result, so no slot register is
+// written on a divergent path (merging such writes would force a wait for the
+// load).
 struct QuadTask {
     const uint4* codes;      // quad-major rows of CPR chunks
-    const uint2* scales;     // INT4O: [quads][G4] x 4 fp16
-    const uint4* wout;       // INT4O: rows of no8 chunks
-    int CPR, no8, nchunks;   // nchunks: INT8 chunks holding real columns; INT4O: CPR + no8
+    int CPR, nchunks;        // chunks per row; chunks holding real columns
     int q0, qstride, nq, IT; // IT: iterations per quad
 };
 
 template <int U>
 struct Slots {
     uint4 w[U][4];
-    uint2 sc[U];
 };
 
 // Cursor over (quad, iteration) items.
@@ -239,95 +246,34 @@ struct ItemCursor {
     }
 };
 
-template <bool INT4O>
-__device__ __forceinline__ void issue_item(const QuadTask& t, ItemCursor cur, int lane, uint4 (&w)[4], uint2& sc) {
+__device__ __forceinline__ void issue_item(const QuadTask& t, ItemCursor cur, int lane, uint4 (&w)[4]) {
     const int q = t.q0 + cur.j * t.qstride;
     const int c = lane + 64 * cur.i;
-    const uint4* base;
-    int rs;
-    if (INT4O) {
-        const bool bg = c < t.CPR;
-        const bool ol = !bg && c < t.CPR + t.no8;
-        const uint4* dummy = t.CPR > 0 ? t.codes : t.wout;
-        base = bg ? t.codes + ((int64_t)q * 4 * t.CPR + c)
-                  : ol ? t.wout + ((int64_t)q * 4 * t.no8 + (c - t.CPR)) : dummy;
-        rs = bg ? t.CPR : ol ? t.no8 : 0;
-        if (t.CPR > 0) sc = gload_u2(t.scales + (bg ? (int64_t)q * (t.CPR >> 2) + (c >> 2) : 0));
-    } else {
-        const bool ok = c < t.nchunks;
-        base = ok ? t.codes + ((int64_t)q * 4 * t.CPR + c) : t.codes;
-        rs = ok ? t.CPR : 0;
-    }
+    const bool ok = c < t.nchunks;
+    const uint4* base = ok ? t.codes + ((int64_t)q * 4 * t.CPR + c) : t.codes;
+    const int rs = ok ? t.CPR : 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = gload_nt(base + r * rs);
 }
 
-// Issue all U slots of the window unconditionally: slots past the task's last
-// item reload item 0 (results ignored), so the number of loads in flight is
-// the same on every path and later waits can count them exactly.  The task
-// must have an item 0 at a valid address (q0 a real quad).
-template <bool INT4O, int U>
-__device__ __forceinline__ void prefetch_items_fixed(const QuadTask& t, int lane, Slots<U>& s) {
-    const int T = t.nq * t.IT;
-    ItemCursor cur = {0, 0};
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const ItemCursor c = u < T ? cur : ItemCursor{0, 0};
-        issue_item<INT4O>(t, c, lane, s.w[u], s.sc[u]);
-        cur.advance(t.IT);
-    }
-}
-
-// Workgroup control barrier that waits only for this wave's LDS and scalar
-// memory operations, not for its outstanding vector loads and stores.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-}
-
 // Issue items [from, to) of the window (to <= U), counting from item 0.
-template <bool INT4O, int U>
+template <int U>
 __device__ __forceinline__ void prefetch_items(const QuadTask& t, int lane, Slots<U>& s, int from = 0, int to = U) {
     const int T = t.nq * t.IT;
     ItemCursor cur = {0, 0};
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (u >= from && u < to && u < T) issue_item<INT4O>(t, cur, lane, s.w[u], s.sc[u]);
+        if (u >= from && u < to && u < T) issue_item(t, cur, lane, s.w[u]);
         cur.advance(t.IT);
     }
 }
 
-// Consume the item in slot (w, sc): chunk c of the quad; xs holds the
-// activations (row stride xstride) in the chunk space's order, background
-// then, from bg_len on, the outlier channels (INT4O).
-template <bool INT4O, int B, class XPtr>
-__device__ __forceinline__ void consume_item(const QuadTask& t, int c, const uint4 (&w)[4], uint2 sc, XPtr xs,
-                                             int xstride, int bg_len, float (&acc)[4][B]) {
-    if (INT4O) {
-        if (c < t.CPR) {
-            uint4 xv[B][4];
-#pragma unroll
-            for (int b = 0; b < B; ++b)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) xv[b][k] = load_x16(xs + b * xstride + 32 * c + 8 * k);
-            int4o_chunk<B>(w, sc, xv, acc);
-        } else if (c < t.CPR + t.no8) {
-            const int o = bg_len + 8 * (c - t.CPR);
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const uint4 xv = load_x16(xs + b * xstride + o);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = acc[r][b];
-                    v = dot2(as_h2(w[r].x), as_h2(xv.x), v);
-                    v = dot2(as_h2(w[r].y), as_h2(xv.y), v);
-                    v = dot2(as_h2(w[r].z), as_h2(xv.z), v);
-                    v = dot2(as_h2(w[r].w), as_h2(xv.w), v);
-                    acc[r][b] = v;
-                }
-            }
-        }
-    } else if (c < t.nchunks) {
+// Consume the item in slot w: chunk c of the quad; xs holds the activations
+// (row stride xstride).
+template <int B, class XPtr>
+__device__ __forceinline__ void consume_item(const QuadTask& t, int c, const uint4 (&w)[4], XPtr xs, int xstride,
+                                             float (&acc)[4][B]) {
+    if (c < t.nchunks) {
         uint4 xv[B][2];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -342,11 +288,11 @@ __device__ __forceinline__ void consume_item(const QuadTask& t, int c, const uin
 // already issued (prefetch_items); the rest of the window is issued here.
 // emit(quad, out) is called once per quad with the wave-reduced sums (lane
 // r * B + b holds row r, batch row b).
-template <bool INT4O, int B, int U, class XPtr, class Emit>
-__device__ __forceinline__ void stream_task(const QuadTask& t, Slots<U>& s, XPtr xs, int xstride, int bg_len,
-                                            int lane, int issued, Emit&& emit) {
+template <int B, int U, class XPtr, class Emit>
+__device__ __forceinline__ void stream_task(const QuadTask& t, Slots<U>& s, XPtr xs, int xstride, int lane,
+                                            int issued, Emit&& emit) {
     const int T = t.nq * t.IT;
-    if (issued < U) prefetch_items<INT4O, U>(t, lane, s, issued, U);
+    if (issued < U) prefetch_items<U>(t, lane, s, issued, U);
     float acc[4][B];
     zero_acc(acc);
     const int IT = t.IT > 0 ? t.IT : 1;
@@ -357,8 +303,8 @@ __device__ __forceinline__ void stream_task(const QuadTask& t, Slots<U>& s, XPtr
         for (int u = 0; u < U; ++u) {
             const int item = t0 + u;
             if (item < T) {
-                consume_item<INT4O, B>(t, lane + 64 * use.i, s.w[u], s.sc[u], xs, xstride, bg_len, acc);
-                if (item + U < T) issue_item<INT4O>(t, nxt, lane, s.w[u], s.sc[u]);
+                consume_item<B>(t, lane + 64 * use.i, s.w[u], xs, xstride, acc);
+                if (item + U < T) issue_item(t, nxt, lane, s.w[u]);
                 nxt.advance(IT);
                 if (use.i == IT - 1) {
                     emit(t.q0 + use.j * t.qstride, quad_reduce<B>(acc, lane));

@@ -343,21 +343,34 @@ int woq_layout_int8_inverse(const uint8_t* dev, int64_t N, int64_t K, int8_t* q)
 int woq_int4o_dev_sizes(int64_t N, const woq_int4o_geom* g, int64_t* codes_bytes, int64_t* scales_bytes,
                         int64_t* wout_bytes) {
     if (N < 0 || !woq::int4o_geom_valid(g)) return WOQ_EINVAL;
-    const int64_t N4 = woq::round_up(N, 4);
-    if (codes_bytes) *codes_bytes = N4 * 64 * g->G4;
-    if (scales_bytes) *scales_bytes = N4 * g->G4 * 2;
-    if (wout_bytes) *wout_bytes = N4 * g->n_out8 * 2;
+    const int64_t N16 = woq::round_up(N, 16);
+    if (codes_bytes) *codes_bytes = N16 * 64 * g->G4;
+    if (scales_bytes) *scales_bytes = N16 * g->G4 * 2;
+    if (wout_bytes) *wout_bytes = N16 * g->n_out8 * 2;
     return WOQ_OK;
 }
+
+namespace {
+
+// Tile layout offsets (16-row tiles; see woq.h).
+inline int64_t code_chunk_offset(int64_t r, int64_t gi, int c, int64_t G4) {
+    return (((r >> 4) * G4 + gi) * 4 + c) * 256 + (r & 15) * 16;      // bytes
+}
+inline int64_t scale_index(int64_t r, int64_t gi, int64_t G4) { return ((r >> 4) * G4 + gi) * 16 + (r & 15); }
+inline int64_t wout_index(int64_t r, int64_t i, int64_t no8) {         // fp16 element i of row r
+    return (((r >> 4) * no8 + (i >> 3)) * 16 + (r & 15)) * 8 + (i & 7);
+}
+
+}  // namespace
 
 int woq_layout_int4o(const uint8_t* packed, const uint16_t* scales, const uint16_t* w_out, int64_t N,
                      const woq_int4o_geom* g, uint8_t* dev_codes, uint16_t* dev_scales, uint16_t* dev_wout) {
     if (N < 0 || !woq::int4o_geom_valid(g)) return WOQ_EINVAL;
     if ((g->G4 && (!dev_codes || !dev_scales)) || (g->n_out8 && !dev_wout)) return WOQ_EINVAL;
     if (N > 0 && ((g->G && (!packed || !scales)) || (g->n_out && !w_out))) return WOQ_EINVAL;
-    const int64_t N4 = woq::round_up(N, 4), G = g->G, G4 = g->G4, half = g->K_pad / 2;
+    const int64_t N16 = woq::round_up(N, 16), G = g->G, G4 = g->G4, half = g->K_pad / 2, no8 = g->n_out8 / 8;
     parallel_for(
-        N4,
+        N16,
         [&](int64_t r0, int64_t r1) {
             for (int64_t r = r0; r < r1; ++r) {
                 const bool real = r < N;
@@ -370,16 +383,15 @@ int woq_layout_int4o(const uint8_t* packed, const uint16_t* scales, const uint16
                             NibbleSlot s = nibble_slot(t);
                             dw[s.dword] |= (uint32_t)(code + 8) << s.shift;
                         }
-                        uint8_t* d = dev_codes + (r * G4 + gi) * 64 + c * 16;
-                        std::memcpy(d, dw, 16);  // little-endian dwords
+                        std::memcpy(dev_codes + code_chunk_offset(r, gi, c, G4), dw, 16);   // little-endian dwords
                     }
-                    dev_scales[((r >> 2) * G4 + gi) * 4 + (r & 3)] = (real && gi < G) ? scales[r * G + gi] : 0;
+                    dev_scales[scale_index(r, gi, G4)] = (real && gi < G) ? scales[r * G + gi] : 0;
                 }
                 for (int64_t i = 0; i < g->n_out8; ++i)
-                    dev_wout[r * g->n_out8 + i] = (real && i < g->n_out) ? w_out[r * g->n_out + i] : 0;
+                    dev_wout[wout_index(r, i, no8)] = (real && i < g->n_out) ? w_out[r * g->n_out + i] : 0;
             }
         },
-        4);
+        16);
     return WOQ_OK;
 }
 
@@ -390,7 +402,7 @@ int woq_layout_int4o_inverse(const uint8_t* dev_codes, const uint16_t* dev_scale
     if (N > 0 && ((g->G && (!dev_codes || !dev_scales || !packed || !scales)) ||
                   (g->n_out && (!dev_wout || !w_out))))
         return WOQ_EINVAL;
-    const int64_t G = g->G, G4 = g->G4, half = g->K_pad / 2;
+    const int64_t G = g->G, G4 = g->G4, half = g->K_pad / 2, no8 = g->n_out8 / 8;
     parallel_for(
         N,
         [&](int64_t r0, int64_t r1) {
@@ -400,7 +412,7 @@ int woq_layout_int4o_inverse(const uint8_t* dev_codes, const uint16_t* dev_scale
                 for (int64_t gi = 0; gi < G; ++gi) {
                     for (int c = 0; c < 4; ++c) {
                         uint32_t dw[4];
-                        std::memcpy(dw, dev_codes + (r * G4 + gi) * 64 + c * 16, 16);
+                        std::memcpy(dw, dev_codes + code_chunk_offset(r, gi, c, G4), 16);
                         for (int t = 0; t < 32; ++t) {
                             NibbleSlot s = nibble_slot(t);
                             int code = (int)((dw[s.dword] >> s.shift) & 0xF) - 8;
@@ -408,12 +420,12 @@ int woq_layout_int4o_inverse(const uint8_t* dev_codes, const uint16_t* dev_scale
                             out[col >> 1] |= (uint8_t)((code & 0xF) << ((col & 1) * 4));
                         }
                     }
-                    scales[r * G + gi] = dev_scales[((r >> 2) * G4 + gi) * 4 + (r & 3)];
+                    scales[r * G + gi] = dev_scales[scale_index(r, gi, G4)];
                 }
-                for (int64_t i = 0; i < g->n_out; ++i) w_out[r * g->n_out + i] = dev_wout[r * g->n_out8 + i];
+                for (int64_t i = 0; i < g->n_out; ++i) w_out[r * g->n_out + i] = dev_wout[wout_index(r, i, no8)];
             }
         },
-        4);
+        16);
     return WOQ_OK;
 }
 

@@ -5,10 +5,11 @@
 //
 // Two ways to run a pass:
 //  * woq_stack_run: one launch per permutation and per product, stream-ordered.
-//  * woq_stack_run_fused: one persistent launch for the whole pass.  On this
-//    hardware a dependent launch costs several microseconds, comparable to the
-//    time it takes to stream one decode linear, so the fused pass keeps every
-//    workgroup resident and separates steps with a device-side barrier.
+//  * woq_stack_run_fused (INT8 stacks): one persistent launch for the whole
+//    pass.  On this hardware a dependent launch costs several microseconds,
+//    comparable to the time it takes to stream one decode linear, so the fused
+//    pass keeps every workgroup resident and separates steps with a
+//    device-side barrier.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -22,15 +23,12 @@ namespace {
 
 using namespace woqk;
 
-// A step as the persistent kernel sees it (device memory, read-only).
+// An INT8 step as the persistent kernel sees it (device memory, read-only).
 struct DevStep {
     const uint4* codes;
-    const uint2* scales;     // INT4O
-    const uint4* wout;       // INT4O
-    const int32_t* perm;     // INT4O
     const uint16_t* x;
     uint16_t* y;
-    int fmt, N, CPR, nchunks, G4, no8, xlen, K, K_bg, n_out, ldx, ldy, nseg;
+    int N, CPR, nchunks, xlen, K, ldx, ldy, nseg;
     int seg_end[WOQ_MAX_SEGMENTS];
     float seg_scale[WOQ_MAX_SEGMENTS];
 };
@@ -66,11 +64,8 @@ constexpr int PREFETCH_SRC = 18;    // staged activation sources per thread reso
 __device__ __forceinline__ QuadTask make_task(const DevStep& st, int gw, int NW) {
     QuadTask t;
     t.codes = st.codes;
-    t.scales = st.scales;
-    t.wout = st.wout;
     t.CPR = st.CPR;
-    t.no8 = st.no8;
-    t.nchunks = st.fmt == WOQ_FMT_INT4O ? st.CPR + st.no8 : st.nchunks;
+    t.nchunks = st.nchunks;
     t.IT = (t.nchunks + 63) >> 6;
     const int quads = (st.N + 3) >> 2;
     t.q0 = gw;
@@ -80,16 +75,7 @@ __device__ __forceinline__ QuadTask make_task(const DevStep& st, int gw, int NW)
 }
 
 // Source index in the activation row of staged element k (-1: zero padding).
-__device__ __forceinline__ int stage_src(const DevStep& st, int k) {
-    if (st.fmt == WOQ_FMT_INT4O) {
-        const int bg = 128 * st.G4;
-        int src = -1;
-        if (k < st.K_bg) src = *gptr(st.perm + k);
-        else if (k >= bg && k - bg < st.n_out) src = *gptr(st.perm + st.K_bg + (k - bg));
-        return ((unsigned)src < (unsigned)st.K) ? src : -1;
-    }
-    return k < st.K ? k : -1;
-}
+__device__ __forceinline__ int stage_src(const DevStep& st, int k) { return k < st.K ? k : -1; }
 
 template <int B, int U>
 __device__ __forceinline__ void fused_step(const DevStep& st, const QuadTask& task, Slots<U>& slots,
@@ -115,33 +101,23 @@ __device__ __forceinline__ void fused_step(const DevStep& st, const QuadTask& ta
         for (int b = 0; b < B; ++b) xs[b * xlen + k] = sk >= 0 ? *gptr(st.x + (int64_t)b * st.ldx + sk) : (uint16_t)0;
     }
     lds_barrier();
-    if (st.fmt == WOQ_FMT_INT4O) {
-        stream_task<true, B, U>(task, slots, (lx_ptr)xs, xlen, 128 * st.G4, lane, EARLY_ITEMS, [&](int q, float out) {
-            if (lane < 4 * B) {
-                const int r = lane / B, b = lane % B, n = 4 * q + r;
-                if (n < st.N) *gptr(st.y + (int64_t)b * st.ldy + n) = f_to_h(out);
+    stream_task<B, U>(task, slots, (lx_ptr)xs, xlen, lane, EARLY_ITEMS, [&](int q, float out) {
+        if (lane < 4 * B) {
+            const int r = lane / B, b = lane % B, n = 4 * q + r;
+            if (n < st.N) {
+                float scale = st.seg_scale[st.nseg - 1];
+                for (int i = st.nseg - 1; i >= 0; --i)
+                    if (n < st.seg_end[i]) scale = st.seg_scale[i];
+                *gptr(st.y + (int64_t)b * st.ldy + n) = f_to_h(out * scale);
             }
-        });
-    } else {
-        stream_task<false, B, U>(task, slots, (lx_ptr)xs, xlen, 0, lane, EARLY_ITEMS, [&](int q, float out) {
-            if (lane < 4 * B) {
-                const int r = lane / B, b = lane % B, n = 4 * q + r;
-                if (n < st.N) {
-                    float scale = st.seg_scale[st.nseg - 1];
-                    for (int i = st.nseg - 1; i >= 0; --i)
-                        if (n < st.seg_end[i]) scale = st.seg_scale[i];
-                    *gptr(st.y + (int64_t)b * st.ldy + n) = f_to_h(out * scale);
-                }
-            }
-        });
-    }
+        }
+    });
 }
 
 template <int U>
 __device__ __forceinline__ void prefetch_step(const DevStep& st, const QuadTask& task, Slots<U>& slots,
                                               int (&src)[PREFETCH_SRC], int tid, int lane) {
-    if (st.fmt == WOQ_FMT_INT4O) prefetch_items<true, U>(task, lane, slots, 0, EARLY_ITEMS);
-    else prefetch_items<false, U>(task, lane, slots, 0, EARLY_ITEMS);
+    prefetch_items<U>(task, lane, slots, 0, EARLY_ITEMS);
 #pragma unroll
     for (int i = 0; i < PREFETCH_SRC; ++i) {
         const int k = tid + i * FUSED_THREADS;
@@ -253,7 +229,7 @@ struct woq_stack {
     u64* sync = nullptr;
     int max_xlen = 0;
     int grid = 0;
-    bool fused_ok = true;                  // every step supported by the fused kernel
+    bool fused_ok = true;                  // every step supported by the fused kernel (INT8 only)
 };
 
 namespace {
@@ -303,13 +279,20 @@ int make_positions(woq_stack* st) {
     return WOQ_OK;
 }
 
-// Largest N for which a step folds its permutation into the product.  Every
-// workgroup of that kernel stages the whole activation row (16 output rows per
-// workgroup), so its extra traffic grows with N; measured on MI355X, the
-// folded form is faster up to the 3B gate|up width (16384 rows at K = 3072)
-// and the 70B down projection (8192 rows at K = 28672), and slower than a
-// separate permutation launch for the 70B gate|up product (57344 rows).
+// Steps fold the permutation into the product (one launch instead of two)
+// where that is faster on MI355X: every workgroup of the folded kernel
+// gathers the whole activation row first, which pays for itself up to rows
+// of about 8K channels and products of 16384 rows (the 3B-shaped and the 70B
+// q|k|v and o products), but not for the 70B gate|up (57344 rows) or down
+// (28672 channels) products, where a separate permutation launch is cheaper.
 constexpr int64_t ONE_LAUNCH_MAX_N = 16384;
+constexpr int64_t ONE_LAUNCH_MAX_XLEN = 8704;
+
+bool fold_permutation(const woq_stack_step& s, int64_t b) {
+    const woq_int4o_geom& g = s.w4.geom;
+    return woq::int4o_use_valu(s.w4.N, g, b) && s.w4.N <= ONE_LAUNCH_MAX_N && b * g.xp_len <= ONE_LAUNCH_MAX_XLEN &&
+           woq_qgemv_int4o_x_supported(&g, b) && (g.K & 7) == 0;
+}
 
 // One pass over the steps; ev (2 per step) brackets each product launch.
 int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b, void* stream,
@@ -320,8 +303,7 @@ int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outp
         const uint16_t* x = inputs[s.in_slot];
         uint16_t* y = outputs[s.out_slot];
         int rc;
-        if (s.fmt == WOQ_FMT_INT4O && st->pos[i] && s.w4.N <= ONE_LAUNCH_MAX_N &&
-            woq_qgemv_int4o_x_supported(&s.w4.geom, b) && (s.w4.geom.K & 7) == 0 && woq::aligned16(x)) {
+        if (s.fmt == WOQ_FMT_INT4O && st->pos[i] && fold_permutation(s, b) && woq::aligned16(x)) {
             // permutation folded into the product: one launch
             if (ev) woq::set_launch_events(ev[2 * i], ev[2 * i + 1]);
             rc = woq_qgemv_int4o_x(&s.w4, x, s.w4.geom.K, st->pos[i], b, y, s.w4.N, stream);
@@ -393,7 +375,7 @@ int launch_fused(woq_stack* st, int64_t b, void* stream) {
 int prepare_fused(woq_stack* st, int64_t b) {
     if (!st->fused_ok) return WOQ_EUNSUPPORTED;
     for (const woq_stack_step& s : st->steps)
-        if ((s.fmt == WOQ_FMT_INT4O && b > 7) || b > 8) return WOQ_EUNSUPPORTED;
+        if (b > 8) return WOQ_EUNSUPPORTED;
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, st->device);
     if (e != hipSuccess) return hip_status(e);
@@ -446,25 +428,10 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
         const woq_stack_step& s = steps[i];
         DevStep d;
         std::memset(&d, 0, sizeof d);
-        d.fmt = s.fmt;
         if (s.fmt == WOQ_FMT_INT4O) {
-            const woq_int4o_geom& g = s.w4.geom;
-            d.codes = (const uint4*)s.w4.codes;
-            d.scales = (const uint2*)s.w4.scales;
-            d.wout = (const uint4*)s.w4.w_out;
-            d.perm = s.perm;
-            d.N = (int)s.w4.N;
-            d.CPR = (int)(4 * g.G4);
-            d.G4 = (int)g.G4;
-            d.no8 = (int)(g.n_out8 / 8);
-            d.xlen = (int)g.xp_len;
-            d.K = (int)g.K;
-            d.K_bg = (int)g.K_bg;
-            d.n_out = (int)g.n_out;
-            d.ldx = (int)g.K;
-            d.ldy = (int)s.w4.N;
-            if (!woq::aligned16(s.w4.codes) || !woq::aligned16(s.w4.w_out) || ((uintptr_t)s.w4.scales & 7u))
-                st->fused_ok = false;
+            // the persistent pass streams INT8 quads only
+            st->fused_ok = false;
+            continue;
         } else {
             d.codes = (const uint4*)s.w8.codes;
             d.N = (int)s.w8.N;
@@ -498,6 +465,17 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
         return rc;
     }
     *out = st;
+    return WOQ_OK;
+}
+
+int woq_stack_launches(const woq_stack* st, int64_t b, int32_t* launches) {
+    if (!st || !launches || b < 1 || b > st->max_b) return WOQ_EINVAL;
+    int32_t n = 0;
+    for (size_t i = 0; i < st->steps.size(); ++i) {
+        const woq_stack_step& s = st->steps[i];
+        n += (s.fmt == WOQ_FMT_INT4O && !(st->pos[i] && fold_permutation(s, b))) ? 2 : 1;
+    }
+    *launches = n;
     return WOQ_OK;
 }
 

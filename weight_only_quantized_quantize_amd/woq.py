@@ -87,6 +87,7 @@ _SIGS = {
     "woq_qgemv_int4o_x_supported": (c_int, [POINTER(Int4oGeom), c_int64]),
     "woq_stack_create": (c_int, [POINTER(StackStep), c_int32, c_int64, POINTER(c_void_p)]),
     "woq_stack_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
+    "woq_stack_launches": (c_int, [c_void_p, c_int64, POINTER(c_int32)]),
     "woq_stack_time": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
                                POINTER(c_float), POINTER(c_float)]),
     "woq_stack_run_fused": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
@@ -389,6 +390,11 @@ class Stack:
 
     def run(self, b: int, stream=None):
         _check(_lib().woq_stack_run(self.handle, self._pin, self._pout, b, _stream(stream)), "woq_stack_run")
+
+    def launches(self, b: int) -> int:
+        n = c_int32()
+        _check(_lib().woq_stack_launches(self.handle, b, ctypes.byref(n)), "woq_stack_launches")
+        return n.value
 
     def run_fused(self, b: int, stream=None):
         _check(_lib().woq_stack_run_fused(self.handle, self._pin, self._pout, b, _stream(stream)),
