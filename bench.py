@@ -40,7 +40,7 @@ def algorithmic_bytes(fmt: str, N: int, K: int, b: int) -> int:
 
 TRAFFIC_PROFILES = {
     # (config, runner, batch) -> committed counter summary of that workload
-    (2, "launch", 1): "profiles/qgemv_int4o_valu__3b_int4o_stack_b1__traffic.md",
+    (2, "launch", 1): "profiles/qgemv_int4o_tile__3b_int4o_stack_b1__traffic.md",
 }
 
 
@@ -123,6 +123,20 @@ def cpu_baseline(spec, b: int, budget_s: float = 12.0):
                       f"host os.cpu_count()={os.cpu_count()}, BLAS threads={blas_threads}"}
 
 
+def copy_calibration():
+    """Three device-to-device copies of 1 GiB: each reads and writes exactly
+    2**30 bytes, which fixes the scale of the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    x = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copied_bytes": 3 * 2 ** 30, "copies": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +149,11 @@ def main():
     ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
                     help="fused: one persistent launch per step; launch: one launch per permutation and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB on the device three times (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (the decode linears are measured on one "
               "device's share); --gpus above 1 is not supported", file=sys.stderr)
