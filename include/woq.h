@@ -233,7 +233,8 @@ int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t 
  * architecture diagram: the outlier GEMM and the fused background GEMM added
  * into one FP16 output).  xp from woq_permute_x (fp16 [b, xp_len]); y fp16
  * [b, ldy], ldy >= N.  The vector-ALU kernel runs for b <= 2, and for b <= 4
- * when N < 6144, if b * xp_len fp16 values fit in 62 KB of LDS; otherwise the
+ * when N < 6144, if b * (2 * xp_len + 16 * G4) bytes (the staged activations
+ * and a correction per 32-channel chunk) fit in 62 KB of LDS; otherwise the
  * matrix-core kernel (woq_qgemm_int4o) runs - on MI355X the faster of the two
  * in each case.  1 <= b <= 64 (b = 0 is a no-op).
  */
@@ -255,8 +256,8 @@ int woq_perm_positions(const int32_t* perm, const woq_int4o_geom* g, uint16_t* p
  * copy of woq_perm_positions, 16-byte aligned) into the permuted, split row,
  * held in on-chip memory while the weights stream; this is the vector-ALU
  * kernel of woq_qgemv_int4o at any 1 <= b <= 4.  WOQ_EUNSUPPORTED unless
- * woq_qgemv_int4o_x_supported(g, b) (1 <= b <= 4, xp_len <= 65535 and the
- * staged row, b * xp_len fp16 values, fits 62 KB); callers then use the
+ * woq_qgemv_int4o_x_supported(g, b) (1 <= b <= 4, xp_len <= 65535 and
+ * b * (2 * xp_len + 16 * G4) bytes fit 62 KB); callers then use the
  * two-call form.
  */
 int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, const uint16_t* pos,

@@ -115,7 +115,7 @@ __device__ __forceinline__ void scatter8(uint16_t* xs, int xp_len, const uint4 (
 // order.
 template <int B, int T, int S, bool GATHER>
 __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, GatherArgs ga) {
-    extern __shared__ __align__(16) uint16_t xs[];   // [B][xp_len]
+    extern __shared__ __align__(16) uint16_t xs[];   // [B][xp_len], then float corr[B][4 * G4]
     __shared__ float red[S > 1 ? T * S : 1][B][16];
     constexpr int W = T * S, NT = 64 * W, P = TILE_WINDOW;
     constexpr int SC = 4;                            // staged pieces per thread issued before the weights
@@ -200,8 +200,20 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
     }
     lds_barrier();
 
-    // 4. background groups
+    // 4. bias correction of every 32-channel background chunk, per batch row
     const lx_ptr xl = (lx_ptr)xs;
+    float* corr = reinterpret_cast<float*>(xs + B * xp_len);
+    const int nq = 4 * G4;
+    for (int e = tid; e < B * nq; e += NT) {
+        const int b = e / nq, q = e - b * nq;
+        uint4 xq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xq[k] = load_x16(xl + b * xp_len + 32 * q + 8 * k);
+        corr[e] = activation_chunk_correction(xq);
+    }
+    lds_barrier();
+
+    // 5. background groups
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
@@ -217,16 +229,19 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
             if (j < J) {
                 const int g = s + S * j;
                 uint4 xg[B][4];
+                float cg[B];
 #pragma unroll
-                for (int b = 0; b < B; ++b)
+                for (int b = 0; b < B; ++b) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) xg[b][q] = load_x16(xl + b * xp_len + 128 * g + 32 * c + 8 * q);
-                int4o_row_chunk<B>(w, sc, xg, acc);
+                    cg[b] = corr[b * nq + 4 * g + c];
+                }
+                int4o_row_chunk<B>(w, sc, xg, cg, acc);
             }
         }
     }
 
-    // 5. FP16 outlier columns: step st covers outlier chunks 4 st .. 4 st + 3 (lane chunk c)
+    // 6. FP16 outlier columns: step st covers outlier chunks 4 st .. 4 st + 3 (lane chunk c)
     const uint4* ob = a.wout + (int64_t)tb * a.no8 * 16 + m;
     for (int st = s; 32 * st < 8 * a.no8; st += S) {
         const int i8 = 4 * st + c;
@@ -246,7 +261,7 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
         }
     }
 
-    // 6. sums over the four chunk lanes, then over the S waves of the tile
+    // 7. sums over the four chunk lanes, then over the S waves of the tile
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = sum_over_chunks(acc[b]);
     if (S > 1) {
@@ -589,7 +604,7 @@ int launch_status(hipError_t e) {
 template <int B, bool GATHER>
 hipError_t launch_int4o_tile(const Int4oArgs& a, const GatherArgs& ga, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
-    const size_t lds = (size_t)B * a.xp_len * sizeof(uint16_t);
+    const size_t lds = (size_t)woq::int4o_valu_lds_bytes(a.xp_len, 4 * (int64_t)a.G4, B);
     if (tiles >= 1024)
         return launch_kernel(qgemv_int4o_tile<B, 2, 2, GATHER>, dim3((unsigned)woq::ceil_div(tiles, 2)), dim3(256),
                              lds, s, a, ga);
@@ -718,7 +733,7 @@ int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, cons
 
 int woq_qgemv_int4o_x_supported(const woq_int4o_geom* g, int64_t b) {
     if (!g || b < 1 || b > 4) return 0;
-    return g->xp_len <= 65535 && b * g->xp_len * 2 <= woq::INT4O_VALU_LDS_BYTES;
+    return g->xp_len <= 65535 && woq::int4o_valu_lds_bytes(g->xp_len, 4 * g->G4, b) <= woq::INT4O_VALU_LDS_BYTES;
 }
 
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy, void* stream) {

@@ -104,16 +104,29 @@ __device__ __forceinline__ void zero_acc(float (&acc)[4][B]) {
 }
 
 // Dot products of one INT4O chunk of one row (32 background channels of one
-// group) with B activation rows (the same 32 channels, fp16); the group scale s
-// multiplies this chunk's sum.  Pairs that carry 16 x code accumulate apart and
-// are divided by 16 (exact) before the two parts are added.
+// group) with B activation rows (the same 32 channels, fp16), on the biased
+// fp16 values the masks produce: low-nibble pairs hold code + 1032 and
+// high-nibble pairs 16 code + 1152, so the chunk's sum of code * x is
+// lo + hi / 16 - corr, with corr = 1032 (sum of x over the low-nibble
+// channels) + 72 (sum of x over the high-nibble channels), computed once per
+// chunk and batch row (activation_chunk_correction).  Skipping the bias
+// subtraction saves one packed add per weight pair; products stay exact and
+// the cancellation costs about 1e-5 of the chunk's magnitude in fp32.  The
+// group scale s multiplies the chunk's sum.
 template <int B>
-__device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&xv)[B][4], float (&acc)[B]) {
+__device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&xv)[B][4], const float (&corr)[B],
+                                                float (&acc)[B]) {
     const uint32_t bias = bias_reg();
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-    Int4Pairs p[4];
+    h2 lo0[4], lo1[4], hi0[4], hi1[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) p[d] = int4_pairs(wd[d], bias);
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t sh = wd[d] >> 8;
+        lo0[d] = as_h2((wd[d] & 0x000F000Fu) | bias);
+        lo1[d] = as_h2((sh & 0x000F000Fu) | bias);
+        hi0[d] = as_h2((wd[d] & 0x00F000F0u) | bias);
+        hi1[d] = as_h2((sh & 0x00F000F0u) | bias);
+    }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const uint32_t xw[16] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
@@ -125,15 +138,33 @@ __device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&
         for (int P = 0; P < 2; ++P) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const Int4Pairs& q = p[2 * P + e];
-                lo = dot2(q.lo0, as_h2(xw[8 * P + 2 * e + 0]), lo);
-                lo = dot2(q.lo1, as_h2(xw[8 * P + 2 * e + 1]), lo);
-                hi = dot2(q.hi0, as_h2(xw[8 * P + 4 + 2 * e + 0]), hi);
-                hi = dot2(q.hi1, as_h2(xw[8 * P + 4 + 2 * e + 1]), hi);
+                const int d = 2 * P + e;
+                lo = dot2(lo0[d], as_h2(xw[8 * P + 2 * e + 0]), lo);
+                lo = dot2(lo1[d], as_h2(xw[8 * P + 2 * e + 1]), lo);
+                hi = dot2(hi0[d], as_h2(xw[8 * P + 4 + 2 * e + 0]), hi);
+                hi = dot2(hi1[d], as_h2(xw[8 * P + 4 + 2 * e + 1]), hi);
             }
         }
-        acc[b] = fmaf(s, fmaf(hi, 0.0625f, lo), acc[b]);
+        acc[b] = fmaf(s, fmaf(hi, 0.0625f, lo) - corr[b], acc[b]);
     }
+}
+
+// The bias correction of one 32-channel background chunk of activations (see
+// int4o_row_chunk): channels 0-7 and 16-23 meet low-nibble codes, 8-15 and
+// 24-31 high-nibble codes.
+__device__ __forceinline__ float activation_chunk_correction(const uint4 (&xv)[4]) {
+    const h2 one = {(f16)1.0f, (f16)1.0f};
+    float sl = 0.0f, sh = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t = dot2(as_h2(xw[j]), one, t);
+        if (q & 1) sh += t;
+        else sl += t;
+    }
+    return 1032.0f * sl + 72.0f * sh;
 }
 
 // Dot products of one INT8 chunk (four rows, 16 channels) with B activation rows.

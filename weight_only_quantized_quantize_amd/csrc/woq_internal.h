@@ -69,15 +69,20 @@ void parallel_for(int64_t n, F&& f, int64_t min_per_thread = 1) {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Staged activation rows of the INT4O vector kernel (b * xp_len fp16 in LDS).
+// LDS of the INT4O vector kernel: the staged activation rows (b * xp_len
+// fp16) and the bias correction of every 32-channel background chunk
+// (b * 4 * G4 floats).
 constexpr int64_t INT4O_VALU_LDS_BYTES = 62 * 1024;
+inline int64_t int4o_valu_lds_bytes(int64_t xp_len, int64_t chunks, int64_t b) {
+    return b * (xp_len * 2 + chunks * 4);
+}
 
 // Which INT4O kernel serves a product of N rows at batch b: the vector kernel
 // for b <= 2, and for b <= 4 on narrow products (fewer than 384 tiles of 16
 // rows), where it is the faster of the two on MI355X; the matrix-core kernel
 // otherwise, and whenever the staged activation rows would not fit in LDS.
 inline bool int4o_use_valu(int64_t N, const woq_int4o_geom& g, int64_t b) {
-    if (b < 1 || b > 4 || b * g.xp_len * 2 > INT4O_VALU_LDS_BYTES) return false;
+    if (b < 1 || b > 4 || int4o_valu_lds_bytes(g.xp_len, 4 * g.G4, b) > INT4O_VALU_LDS_BYTES) return false;
     return b <= 2 || ceil_div(N, 16) < 384;
 }
 
