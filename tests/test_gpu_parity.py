@@ -315,3 +315,23 @@ def test_batch_prefix_invariant(gpu_lib):
     y32, _ = int4o_run(parts, g, perm, x)
     y1, _ = int4o_run(parts, g, perm, x[:1])
     assert O.normwise_rel_err(y32[:1], y1) <= 1e-3
+
+
+@pytest.mark.parametrize("b", [33, 64])
+def test_int4o_mfma_wide_batch_wide_product(gpu_lib, b):
+    """Three and four column tiles on the widest tile plan (N >= 32768 rows,
+    eight tiles per workgroup), checked on sampled rows."""
+    _print_case("int4o mfma wide", b)
+    rng = np.random.default_rng(b)
+    N, K = 32800, 200
+    g = woq.woq_int4o_geometry(K)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x)
+    rows = np.concatenate([np.arange(16), np.sort(rng.choice(N, 200, replace=False)), np.arange(N - 16, N)])
+    check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma wide b={b}")
