@@ -123,6 +123,67 @@ def cpu_baseline(spec, b: int, budget_s: float = 12.0):
                       f"host os.cpu_count()={os.cpu_count()}, BLAS threads={blas_threads}"}
 
 
+def stream_read_ceiling(stream, reps: int = 10) -> float:
+    """GB/s of the library's plain streaming-read kernel over 1 GiB (larger than
+    the 256 MB last-level cache), timed with events on `stream`."""
+    import torch
+    from weight_only_quantized_quantize_amd import woq
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            woq.woq_stream_read(buf, stream)
+        e0.record(stream)
+        for _ in range(reps):
+            woq.woq_stream_read(buf, stream)
+        e1.record(stream)
+    e1.synchronize()
+    del buf
+    return (1 << 30) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def bench_single(args):
+    """One INT8 linear, 4096 x 4096, batch 1: the product alone, launched back
+    to back over 32 copies of the weights (537 MB, more than the last-level
+    cache), timed with events over the steps."""
+    import torch
+    import synth
+    from weight_only_quantized_quantize_amd import woq
+    W, x = synth.config1_inputs()
+    q, sc = woq.woq_quantize_int8(W)
+    copies = 32
+    devs = [woq.DeviceInt8([(q, sc)]) for _ in range(copies)]
+    del W
+    xd = torch.from_numpy(x.copy()).cuda()
+    y = torch.empty(1, 4096, dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(max(args.warmup, copies)):
+        woq.woq_qgemv_int8(devs[i % copies].desc, xd, y, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        woq.woq_qgemv_int8(devs[i % copies].desc, xd, y, stream)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = algorithmic_bytes("int8", 4096, 4096, 1)
+    value = nbytes / (ms * 1e-3) / 1e9
+    ceiling = stream_read_ceiling(stream)
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16xf16->f32 on int8 codes", "data": "synthetic",
+        "config": {"workload": "single INT8 linear 4096x4096, batch 1, weights rotated over 32 copies",
+                   "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "qgemv_int8_valu", "achieved": round(value, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+                     "stream_read_ceiling_gbs": round(ceiling, 1), "frac_of_stream_ceiling": round(value / ceiling, 4)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def copy_calibration():
     """Three device-to-device copies of 1 GiB: each reads and writes exactly
     2**30 bytes, which fixes the scale of the FETCH_SIZE / WRITE_SIZE counters."""
@@ -142,8 +203,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
-                    help="2: 3B INT4O, 3: 9B INT8, 4: 70B INT4O (resident); 5: 9B INT8 streamed from pinned host memory")
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="1: one INT8 4096x4096 linear; 2: 3B INT4O, 3: 9B INT8, 4: 70B INT4O (resident stacks); "
+                         "5: 9B INT8 streamed from pinned host memory")
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="resident layers (default: all)")
     ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
@@ -165,6 +227,8 @@ def main():
     from weight_only_quantized_quantize_amd.stack import ResidentStack
 
     woq.require_gpu()
+    if args.config == 1:
+        return bench_single(args)
     spec = synth.stack_spec(args.config)
     b = args.batch or spec.batches[0]
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
@@ -259,6 +323,9 @@ def main():
                      "mean_launch_us": round(1e3 * kern_ms / launches_per_step, 3),
                      "mean_algorithmic_bytes_per_launch": kernel_bytes // launches_per_step},
     }
+    ceiling = stream_read_ceiling(stream)
+    result["roofline"]["stream_read_ceiling_gbs"] = round(ceiling, 1)
+    result["roofline"]["frac_of_stream_ceiling"] = round(achieved / ceiling, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(spec, b)

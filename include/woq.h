@@ -406,6 +406,17 @@ int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* 
 /* Release the slots and events (after both streams have finished). */
 int woq_pager_destroy(woq_pager* p);
 
+/* ------------------------------------------------------------ measurement */
+
+/*
+ * Read `bytes` bytes (a multiple of 16, 16-byte aligned device memory) with
+ * one 16-byte non-temporal load per lane and chunk, the way the products
+ * stream their weights, and discard them: the achievable streaming-read rate
+ * against which the products' bandwidth is reported.  Asynchronous on
+ * `stream`; the caller times it.  bytes = 0 is a no-op.
+ */
+int woq_stream_read(const void* buf, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

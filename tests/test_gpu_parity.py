@@ -335,3 +335,34 @@ def test_int4o_mfma_wide_batch_wide_product(gpu_lib, b):
     y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x)
     rows = np.concatenate([np.arange(16), np.sort(rng.choice(N, 200, replace=False)), np.arange(N - 16, N)])
     check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma wide b={b}")
+
+
+@pytest.mark.parametrize("N,K", [(1280, 8192), (7168, 8192), (8192, 1024), (8192, 3584)])
+@pytest.mark.parametrize("b", [1, 8, 32])
+def test_int4o_tp8_share_shapes(gpu_lib, N, K, b):
+    """One GPU's share of the 70B-shaped products under 8-way tensor
+    parallelism (q|k|v and gate|up split along N, o and down along K), on
+    sampled rows."""
+    _print_case("int4o tp8 share", N, K, b)
+    rng = np.random.default_rng(N + K + b)
+    g = woq.woq_int4o_geometry(K)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.015).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x)
+    rows = np.sort(rng.choice(N, 64, replace=False))
+    check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"tp8 {N}x{K} b={b}")
+
+
+def test_stream_read_entry_point(gpu_lib):
+    import torch
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    woq.woq_stream_read(buf)
+    torch.cuda.synchronize()
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_stream_read(buf[:15])
+    assert e.value.status == woq.WOQ_EINVAL

@@ -82,6 +82,7 @@ _SIGS = {
     "woq_qgemv_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_qgemm_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_perm_positions": (c_int, [c_void_p, POINTER(Int4oGeom), c_void_p]),
+    "woq_stream_read": (c_int, [c_void_p, c_int64, c_void_p]),
     "woq_qgemv_int4o_x": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                   c_void_p]),
     "woq_qgemv_int4o_x_supported": (c_int, [POINTER(Int4oGeom), c_int64]),
@@ -298,6 +299,11 @@ def woq_qgemv_int4o_x(w: Int4oW, x, pos_dev, y, stream=None, b: int | None = Non
     _check(_lib().woq_qgemv_int4o_x(ctypes.byref(w), _ptr(x), ldx or x.shape[1], _ptr(pos_dev), b, _ptr(y),
                                     y.shape[1], _stream(stream)), "woq_qgemv_int4o_x")
     return y
+
+
+def woq_stream_read(buf, stream=None):
+    """Read every byte of a contiguous device tensor (size a multiple of 16)."""
+    _check(_lib().woq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)), "woq_stream_read")
 
 
 def woq_qgemm_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
