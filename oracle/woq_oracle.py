@@ -16,7 +16,9 @@ Sources (the pages are cited by title and section):
   "Architecture & Key Innovations": the architecture diagram (global static
   permutation, 1% FP16 outlier channels, 99% INT4 background in [-7, +7], 2:1
   uint8 packing, zero-point 0, outlier GEMM plus background GEMM added into one
-  FP16 output) and innovation item 3 (top-1% channels by |W| x |X_profile|).
+  FP16 output), innovation item 3 (top-1% channels by |W| x |X_profile|) and
+  item 4 (INT8 vocabulary tables; an outlier-aware INT4 lm_head that may share
+  the embedding matrix).
 
 Readings where the pages are silent (each one is listed in the design notes):
 
@@ -35,6 +37,10 @@ Readings where the pages are silent (each one is listed in the design notes):
 * a nibble holds a two's-complement code (zero-point 0), the low nibble of a
   byte is the even channel, packing runs along the input dimension.
 * the background is zero-padded to a whole number of 128-channel groups.
+* the INT8 vocabulary table uses the same per-tensor INT8 scheme; looking up a
+  token applies the [ELG] reconstruction to its row: the code times the fp32
+  scale evaluated in fp32, then rounded to fp16 (PyTorch evaluates half
+  arithmetic in fp32).  A token id outside the table gives a zero row.
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 constructed ties, exhaustive nibble tables, exact integer products, planted-set
@@ -89,6 +95,30 @@ def dequantize_int8(q: np.ndarray, s) -> np.ndarray:
 def linear_int8(q: np.ndarray, s, x: np.ndarray) -> np.ndarray:
     """y[b, n] = sum_k (q[n, k] * s) * x[b, k]  (x fp16 [b, K], output float64 [b, N])."""
     return np.asarray(x, np.float64) @ dequantize_int8(q, s).T
+
+
+def embed_int8(q: np.ndarray, s, ids) -> np.ndarray:
+    """[OTF] item 4 (INT8 vocabulary tables) with the [ELG] "FP16 On-The-Fly
+    GPU Reconstruction" applied to the looked-up rows.
+
+    q int8 [V, H] and s are the table's INT8 codes and scale (quantize_int8 of
+    the embedding matrix); ids int [b].  Returns fp16 [b, H]:
+    fp16(fp32(q[id, :] * s)), both roundings to nearest even.  The product of
+    a code (at most 7 bits) and an fp32 scale is exact in float64, so the two
+    casts below are exactly the two roundings.  Rows of ids outside [0, V)
+    are zero.
+    """
+    q = np.asarray(q)
+    ids = np.asarray(ids, np.int64).reshape(-1)
+    V, H = q.shape
+    out = np.zeros((ids.size, H), np.float16)
+    s64 = np.float64(np.float32(s))
+    for r, t in enumerate(ids):
+        if 0 <= t < V:
+            exact = q[t].astype(np.float64) * s64
+            with np.errstate(over="ignore"):                 # overflow gives +-inf, as intended
+                out[r] = exact.astype(np.float32).astype(np.float16)
+    return out
 
 
 # --------------------------------------------------------------------------

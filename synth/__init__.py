@@ -6,5 +6,5 @@ packing, permutation or product arithmetic lives here.
 from .inputs import (  # noqa: F401
     LinearSpec, StackSpec, CONFIGS, SPACES, stack_spec, small_stack_spec,
     weight, decode_input, profile, planted_set, config1_inputs,
-    planted_count, generate_parallel,
+    planted_count, generate_parallel, vocab_size, embedding, token_ids,
 )

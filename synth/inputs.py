@@ -20,6 +20,9 @@ Recipe (all draws from numpy's ``default_rng``):
   same set in every layer): weight columns x10, profile and decode activation
   columns x20, applied in float32 before any rounding to fp16.
 * the activation profile has 128 rows.
+* the tied embedding / lm_head table: slot 40 of layer 0, [vocab, hidden],
+  std as the stack, planted hidden channels x10; decode token ids: slot 41,
+  uniform integers in [0, vocab).
 """
 from __future__ import annotations
 
@@ -101,6 +104,35 @@ CONFIGS = {
 }
 # the streamed workload reuses the INT8 9B-shaped stack unchanged
 CONFIGS[5] = CONFIGS[3]
+
+
+# vocabulary of the tied embedding / lm_head table: the 3B- and 70B-shaped
+# models use a 128256-token vocabulary, the 9B-shaped one 256000; reduced
+# stacks use 1000
+VOCAB = {2: 128256, 3: 256000, 4: 128256}
+
+
+def vocab_size(spec: StackSpec) -> int:
+    return VOCAB.get(spec.cfg_id, 1000)
+
+
+def embedding(spec: StackSpec, out: np.ndarray | None = None) -> np.ndarray:
+    """float32 [vocab, hidden] tied embedding table (also the lm_head weight):
+    slot 40 of layer 0, std as the stack's weights, planted hidden channels x10."""
+    V, H = vocab_size(spec), spec.hidden
+    if out is None:
+        out = np.empty((V, H), np.float32)
+    _rng(spec.cfg_id, 0, 40).standard_normal(dtype=np.float32, out=out)
+    out *= np.float32(spec.std)
+    if spec.planted:
+        out[:, planted_set(spec, "h")] *= np.float32(spec.w_planted_gain)
+    return out
+
+
+def token_ids(spec: StackSpec, b: int | None = None) -> np.ndarray:
+    """int32 [b] decode token ids (slot 41), uniform over the vocabulary."""
+    ids = _rng(spec.cfg_id, 0, 41).integers(0, vocab_size(spec), size=spec.bmax, dtype=np.int32)
+    return ids if b is None else ids[:b].copy()
 
 
 def stack_spec(cfg: int) -> StackSpec:

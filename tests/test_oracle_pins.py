@@ -324,6 +324,53 @@ def test_int4o_product_exact_integer():
         assert abs(Fraction(float(y[0, n])) - exact) <= abs(exact) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 18)
 
 
+# ------------------------------------------------------ INT8 vocabulary ----
+
+def test_embed_lookup_hand_table():
+    """Single-entry lookups derived by hand, including a double rounding."""
+    for ln in read_golden("embed_int8_lookup.txt"):
+        c, m, e, bits = ln.split()[:4]
+        s = np.float32(int(m) * 2.0 ** int(e))
+        assert float(s) == int(m) * 2.0 ** int(e)
+        y = O.embed_int8(np.array([[int(c)]], np.int8), s, [0])
+        assert y.dtype == np.float16 and y.shape == (1, 1)
+        assert int(y.view(np.uint16)[0, 0]) == int(bits, 16), ln
+
+
+def test_embed_lookup_rows_ids_and_bound():
+    """Rows follow the ids (repeats allowed); ids outside the table give zero
+    rows; every entry is within half an fp16 ulp (plus half an fp32 ulp of the
+    product) of the exact code * scale."""
+    rng = np.random.default_rng(11)
+    V, H = 37, 50
+    E = rng.standard_normal((V, H)).astype(np.float32)
+    q, s = O.quantize_int8(E)
+    ids = np.array([5, 0, V - 1, 5, -1, V, 2 ** 31 - 1, 12], np.int64)
+    y = O.embed_int8(q, s, ids)
+    assert y.shape == (ids.size, H) and y.dtype == np.float16
+    for r, t in enumerate(ids):
+        if not 0 <= t < V:
+            assert not y[r].view(np.uint16).any()
+            continue
+        exact = np.array([Fraction(int(c)) * Fraction(float(s)) for c in q[t]], dtype=object)
+        for j in range(H):
+            v = Fraction(float(y[r, j]))
+            ulp16 = Fraction(float(np.spacing(np.float16(abs(float(exact[j]))))))
+            ulp32 = Fraction(float(np.spacing(np.float32(abs(float(exact[j]))))))
+            assert abs(v - exact[j]) <= ulp16 / 2 + ulp32 / 2
+    np.testing.assert_array_equal(y[0], y[3])
+    assert O.embed_int8(q, s, np.array([], np.int64)).shape == (0, H)
+
+
+def test_embed_lookup_power_of_two_scale_is_exact():
+    """With scale 2^-7 every code * scale is exact in fp16, so the lookup is the
+    dequantised row itself."""
+    rng = np.random.default_rng(12)
+    q = rng.integers(-127, 128, size=(9, 70)).astype(np.int8)
+    y = O.embed_int8(q, np.float32(2.0 ** -7), np.arange(9))
+    np.testing.assert_array_equal(y.astype(np.float64), q.astype(np.float64) / 128.0)
+
+
 # ------------------------------------------------------------ byte totals ----
 
 def _golden_totals():
