@@ -211,6 +211,8 @@ def main():
     ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
                     help="fused: one persistent launch per step; launch: one launch per permutation and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vocab", action="store_true",
+                    help="outlier-INT4 stacks: skip the INT8 token lookup and tied lm_head timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB on the device three times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -323,6 +325,8 @@ def main():
                      "mean_launch_us": round(1e3 * kern_ms / launches_per_step, 3),
                      "mean_algorithmic_bytes_per_launch": kernel_bytes // launches_per_step},
     }
+    if spec.fmt == "int4o" and not args.no_vocab:
+        result["vocab"] = bench_vocab(args, spec, rs, b, run, stream, log)
     ceiling = stream_read_ceiling(stream)
     result["roofline"]["stream_read_ceiling_gbs"] = round(ceiling, 1)
     result["roofline"]["frac_of_stream_ceiling"] = round(achieved / ceiling, 4)
@@ -330,6 +334,67 @@ def main():
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(spec, b)
     print(json.dumps(result), flush=True)
+
+
+def bench_vocab(args, spec, rs, b, run, stream, log):
+    """The steps on either side of the stack: INT8 token lookup before it and
+    the tied outlier-INT4 lm_head after it, timed alone (HIP events) and as
+    part of a whole decode step (lookup, stack pass, lm_head)."""
+    import numpy as np
+    import torch
+    import synth
+    from weight_only_quantized_quantize_amd.stack import TiedVocab
+
+    t0 = time.perf_counter()
+    E = synth.embedding(spec)
+    tv = TiedVocab(E, rs.perm_host["h"], max_b=b)
+    del E
+    V, H = tv.V, tv.H
+    log(f"tied vocabulary {V}x{H} prepared in {time.perf_counter() - t0:.1f} s; "
+        f"{tv.device_bytes() / 1e9:.3f} GB resident")
+    ids = torch.from_numpy(synth.token_ids(spec, b)).cuda()
+    emb = torch.empty(b, H, dtype=torch.float16, device="cuda")
+    h = torch.from_numpy(synth.decode_input(spec, spec.layers, 0, b) if b <= spec.bmax else
+                         np.tile(synth.decode_input(spec, spec.layers, 0), (-(-b // spec.bmax), 1))[:b]).cuda()
+    logits = torch.empty(b, V, dtype=torch.float16, device="cuda")
+
+    def timed(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(3):
+            fn()
+        ev[0].record(stream)
+        for _ in range(n):
+            fn()
+        ev[1].record(stream)
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    n = max(args.steps, 20)
+    embed_ms = timed(lambda: tv.embed(ids, emb, stream), n)
+    head_ms = timed(lambda: tv.logits(h, logits, stream), n)
+
+    def step():
+        tv.embed(ids, emb, stream)
+        run(b, stream)
+        tv.logits(h, logits, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    full_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    head_bytes = algorithmic_bytes("int4o", V, H, b)
+    embed_bytes = b * H * 3 + 4 * b + 4
+    return {"vocab": V, "hidden": H, "table_bytes": int(tv.table.nbytes),
+            "embed_us": round(embed_ms * 1e3, 3), "embed_algorithmic_bytes": embed_bytes,
+            "lm_head_us": round(head_ms * 1e3, 3), "lm_head_algorithmic_bytes": head_bytes,
+            "lm_head_gbs": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),
+            "lm_head_launches": 2,
+            "ms_per_step_with_vocab": round(full_ms, 5),
+            "decode_tok_s_with_vocab": round(b / (full_ms * 1e-3), 2)}
 
 
 def bench_streamed(args, spec, b, log):

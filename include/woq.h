@@ -227,6 +227,22 @@ int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t 
                    uint16_t* y, int64_t ldy, void* stream);
 
 /*
+ * INT8 vocabulary lookup ("On-The-Fly Weight Synthesizer (OTF-LLM Engine)",
+ * Architecture & Key Innovations, item 4: vocabulary tables held as INT8; each
+ * looked-up row restored as in "Open Origin - ELG Stream Layer", "FP16
+ * On-The-Fly GPU Reconstruction"):
+ *   y[r, k] = fp16(fp32(code[ids[r], k] * scale(ids[r])))   for r < b, k < K,
+ * the product rounded to fp32 and then to fp16, both to nearest even.  w is the
+ * table (N = vocabulary rows, K = hidden width) in the INT8 device layout;
+ * ids int32 [b] in device memory (4-byte aligned); y fp16 [b, ldy], 16-byte
+ * aligned, ldy a multiple of 8 and >= K.  A row whose id lies outside [0, N)
+ * is written as zeros (ids are device data, so they cannot be checked before
+ * the launch).  b <= 65535; b = 0 is a no-op.
+ */
+int woq_embed_int8(const woq_int8_w* w, const int32_t* ids, int64_t b, uint16_t* y, int64_t ldy,
+                   void* stream);
+
+/*
  * y[r, n] = fp16(sum_i w_out[n, i] xp[r, 128*G4 + i]
  *               + sum_g scale[n, g] sum_{k in g} code[n, k] xp[r, k])
  * with fp32 accumulation ("On-The-Fly Weight Synthesizer (OTF-LLM Engine)",

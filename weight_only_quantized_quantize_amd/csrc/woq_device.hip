@@ -84,6 +84,60 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
     if (acc == 0x9E3779B9u) *gptr(sink) = acc;
 }
 
+// ------------------------------------------------- INT8 vocabulary lookup
+
+struct EmbedArgs {
+    const uint4* codes;     // INT8 device layout, row-major [V4][Kd] offset-binary bytes
+    const int32_t* ids;     // [b]
+    uint16_t* y;            // [b][ldy]
+    int V, K, CPR, ldy;     // CPR = Kd / 16
+    int nseg;
+    int seg_end[WOQ_MAX_SEGMENTS];
+    float seg_scale[WOQ_MAX_SEGMENTS];
+};
+
+// One token per blockIdx.y; each lane expands 16 codes of the row.  The value
+// is the code times the scale rounded to fp32 and then to fp16, both to
+// nearest even.  The fp32 product is pinned in a register before the
+// narrowing: otherwise the compiler fuses the multiply and the narrowing into
+// one mixed-precision FMA that rounds once, straight to fp16, which differs
+// from the two roundings where the fp32 product lands on an fp16 tie.
+__global__ __launch_bounds__(256) void embed_int8_kernel(EmbedArgs a) {
+    const int r = blockIdx.y;
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= a.CPR || 16 * c >= a.K) return;
+    const int t = *gptr(a.ids + r);
+    const bool valid = (unsigned)t < (unsigned)a.V;
+    float s = 0.0f;
+    if (valid) {
+        int i = 0;
+        while (i + 1 < a.nseg && t >= a.seg_end[i]) ++i;
+        s = a.seg_scale[i];
+    }
+    uint4 w = make_uint4(0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u);   // code 0
+    if (valid) w = gload_u4(a.codes + (int64_t)t * a.CPR + c);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t word = wd[j >> 1];
+        const int sh = 16 * (j & 1);
+        float lo = (float)((int)((word >> sh) & 0xFFu) - 128) * s;
+        float hi = (float)((int)((word >> (sh + 8)) & 0xFFu) - 128) * s;
+        asm volatile("" : "+v"(lo), "+v"(hi));
+        h[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    }
+    uint16_t* yr = a.y + (int64_t)r * a.ldy + 16 * c;
+    if (16 * c + 16 <= a.K) {
+        uint4* d = reinterpret_cast<uint4*>(yr);
+        gstore_u4(d, make_uint4(h[0], h[1], h[2], h[3]));
+        gstore_u4(d + 1, make_uint4(h[4], h[5], h[6], h[7]));
+    } else {
+        for (int j = 0; j < 16 && 16 * c + j < a.K; ++j) *gptr(yr + j) = (uint16_t)(h[j >> 1] >> (16 * (j & 1)));
+    }
+}
+
 // ---------------------------------------------------- INT4O, vector ALU (b <= 4)
 
 struct Int4oArgs {
@@ -808,6 +862,38 @@ int woq_stream_read(const void* buf, int64_t bytes, void* stream) {
     if (blocks > INT32_MAX) return WOQ_EUNSUPPORTED;
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        (const uint4*)buf, n16, sink);
+    return launch_status(hipGetLastError());
+}
+
+int woq_embed_int8(const woq_int8_w* w, const int32_t* ids, int64_t b, uint16_t* y, int64_t ldy, void* stream) {
+    if (!w || w->N < 0 || w->K < 1 || b < 0 || ldy < w->K) return WOQ_EINVAL;
+    if (w->nseg < 1 || w->nseg > WOQ_MAX_SEGMENTS || w->seg_end[w->nseg - 1] != w->N) return WOQ_EINVAL;
+    for (int i = 0; i < w->nseg; ++i) {
+        int64_t lo = i ? w->seg_end[i - 1] : 0;
+        if (w->seg_end[i] < lo) return WOQ_EINVAL;
+    }
+    if (b == 0) return WOQ_OK;
+    if (!ids || !y || (w->N > 0 && !w->codes)) return WOQ_EINVAL;
+    if ((w->N > 0 && !woq::aligned16(w->codes)) || ((uintptr_t)ids & 3u) || !woq::aligned16(y) || (ldy & 7))
+        return WOQ_EALIGN;
+    if (b > 65535 || w->N > (int64_t)INT32_MAX - 64 || w->K > (int64_t)INT32_MAX - 64 || ldy > INT32_MAX)
+        return WOQ_EUNSUPPORTED;
+    EmbedArgs a;
+    a.codes = reinterpret_cast<const uint4*>(w->codes);
+    a.ids = ids;
+    a.y = y;
+    a.V = (int)w->N;
+    a.K = (int)w->K;
+    a.CPR = (int)(woq::round_up(w->K, 64) / 16);
+    a.ldy = (int)ldy;
+    a.nseg = w->nseg;
+    for (int i = 0; i < WOQ_MAX_SEGMENTS; ++i) {
+        a.seg_end[i] = i < w->nseg ? (int)w->seg_end[i] : (int)w->N;
+        a.seg_scale[i] = i < w->nseg ? w->seg_scale[i] : 0.0f;
+    }
+    const int threads = 256;
+    const int blocks = (int)woq::ceil_div(woq::ceil_div(w->K, 16), threads);
+    hipLaunchKernelGGL(embed_int8_kernel, dim3(blocks, (unsigned)b), dim3(threads), 0, (hipStream_t)stream, a);
     return launch_status(hipGetLastError());
 }
 

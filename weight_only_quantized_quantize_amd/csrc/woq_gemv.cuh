@@ -55,6 +55,11 @@ __device__ __forceinline__ uint2 gload_u2(const uint2* p) {
     return make_uint2(v[0], v[1]);
 }
 
+// 16-byte global store, 16-byte aligned.
+__device__ __forceinline__ void gstore_u4(uint4* p, uint4 v) {
+    *(__attribute__((address_space(1))) u32x4*)p = u32x4{v.x, v.y, v.z, v.w};
+}
+
 // Streamed 16-byte weight load: weight bytes are read exactly once, so they
 // are marked non-temporal and do not push the shared activations out of cache.
 __device__ __forceinline__ uint4 gload_nt(const uint4* p) {

@@ -193,3 +193,44 @@ class StreamedInt8Stack:
 
     def make_pager(self, max_b: int):
         return woq.Pager(self.pool, self.layer_off, self.layer_bytes, self.steps, len(GROUPS), max_b)
+
+
+class TiedVocab:
+    """The vocabulary matrix on both sides of the stack, tied: an INT8 table
+    for the token lookup and the outlier-aware INT4 lm_head quantised from the
+    same float matrix over the hidden space's global permutation.
+
+    E: float32 [V, H]; perm: int32 [H], the hidden space's permutation (the one
+    the stack's q|k|v and gate|up products use); max_b: largest batch.
+    """
+
+    def __init__(self, E, perm, max_b: int, device="cuda"):
+        import torch
+        E = np.ascontiguousarray(E, np.float32)
+        self.V, self.H = E.shape
+        self.max_b = max_b
+        q, s = woq.woq_quantize_int8(E)
+        self.table = woq.DeviceInt8([(q, s)], device)
+        del q
+        self.geom = woq.woq_int4o_geometry(self.H)
+        self.head = woq.DeviceInt4o([woq.woq_quantize_int4o(E, perm)], self.geom, device)
+        self.perm_dev = torch.from_numpy(np.ascontiguousarray(perm, np.int32)).to(device)
+        self.xp = torch.zeros(max_b, self.geom.xp_len, dtype=torch.float16, device=device)
+
+    def device_bytes(self) -> int:
+        tot = self.table.nbytes
+        for t in (self.head.codes, self.head.scales, self.head.w_out):
+            if t is not None:
+                tot += t.numel() * t.element_size()
+        return tot
+
+    def embed(self, ids, y, stream=None, b: int | None = None):
+        """y[r] = table row ids[r] (fp16), ids int32 [b] on the device."""
+        return woq.woq_embed_int8(self.table.desc, ids, y, stream, b)
+
+    def logits(self, h, y, stream=None, b: int | None = None):
+        """y = lm_head(h): h fp16 [b, H], y fp16 [b, >= V]."""
+        b = h.shape[0] if b is None else b
+        assert b <= self.max_b
+        woq.woq_permute_x(h, self.perm_dev, self.geom, self.xp, stream)
+        return woq.woq_qgemv_int4o(self.head.desc, self.xp, y, stream, b)

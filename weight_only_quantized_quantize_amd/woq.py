@@ -79,6 +79,7 @@ _SIGS = {
     "woq_layout_int4o_inverse": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, POINTER(Int4oGeom), c_void_p, c_void_p, c_void_p]),
     "woq_permute_x": (c_int, [c_void_p, c_int64, c_void_p, c_int64, POINTER(Int4oGeom), c_void_p, c_void_p]),
     "woq_qgemv_int8": (c_int, [POINTER(Int8W), c_void_p, c_int64, c_int64, c_void_p, c_int64, c_void_p]),
+    "woq_embed_int8": (c_int, [POINTER(Int8W), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_qgemv_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_qgemm_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_perm_positions": (c_int, [c_void_p, POINTER(Int4oGeom), c_void_p]),
@@ -273,6 +274,14 @@ def woq_qgemv_int8(w: Int8W, x, y, stream=None, b: int | None = None):
     b = x.shape[0] if b is None else b
     _check(_lib().woq_qgemv_int8(ctypes.byref(w), _ptr(x), x.shape[1], b, _ptr(y), y.shape[1], _stream(stream)),
            "woq_qgemv_int8")
+    return y
+
+
+def woq_embed_int8(w: Int8W, ids, y, stream=None, b: int | None = None):
+    """Look up rows ``ids`` (int32 device tensor [b]) of an INT8 table into y (fp16 [b, ldy])."""
+    b = ids.shape[0] if b is None else b
+    _check(_lib().woq_embed_int8(ctypes.byref(w), _ptr(ids), b, _ptr(y), y.shape[1], _stream(stream)),
+           "woq_embed_int8")
     return y
 
 
