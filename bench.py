@@ -211,6 +211,9 @@ def main():
     ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
                     help="fused: one persistent launch per step; launch: one launch per permutation and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-budget", type=float, default=None,
+                    help="stacks 2-4: device-memory budget in GB for the weights; the first layers stay resident, "
+                         "the rest stream from pinned host memory (tiered pass)")
     ap.add_argument("--no-vocab", action="store_true",
                     help="outlier-INT4 stacks: skip the INT8 token lookup and tied lm_head timing")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -236,6 +239,8 @@ def main():
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
     if args.config == 5:
         return bench_streamed(args, spec, b, log)
+    if args.hbm_budget is not None:
+        return bench_tiered(args, spec, b, log)
     t0 = time.perf_counter()
     rs = ResidentStack(spec, lambda layer, lin, out: synth.weight(spec, layer, lin, out=out),
                        lambda space: synth.profile(spec, space), layers=args.layers, log=log)
@@ -395,6 +400,97 @@ def bench_vocab(args, spec, rs, b, run, stream, log):
             "lm_head_launches": 2,
             "ms_per_step_with_vocab": round(full_ms, 5),
             "decode_tok_s_with_vocab": round(b / (full_ms * 1e-3), 2)}
+
+
+def bench_tiered(args, spec, b, log):
+    """Tiered decode under a device-memory budget: the planner keeps the first
+    layers resident and streams the rest from one pinned host pool through two
+    device slots.  ``value`` is the algorithmic bandwidth of the whole step;
+    the overlap efficiency compares the step with the serial copy time of the
+    streamed blocks at the measured host-to-device bandwidth."""
+    import statistics
+
+    import torch
+    import synth
+    from weight_only_quantized_quantize_amd.stack import GROUPS, TieredStack
+
+    budget = int(args.hbm_budget * 1e9)
+    t0 = time.perf_counter()
+    ts = TieredStack(spec, lambda layer, lin, out: synth.weight(spec, layer, lin, out=out),
+                     lambda space: synth.profile(spec, space), budget, layers=args.layers, log=log)
+    L, nA = ts.n_layers, ts.n_resident
+    streamed_bytes = ts.streamed_bytes()
+    log(f"prepared {L} layers in {time.perf_counter() - t0:.1f} s: {nA} resident, {L - nA} streamed "
+        f"({streamed_bytes / 1e9:.2f} GB pinned, {ts.block_bytes / 1e6:.1f} MB per layer)")
+    inputs, outputs = [], []
+    for layer in range(L):
+        for names, inp in GROUPS:
+            inputs.append(torch.from_numpy(synth.decode_input(spec, layer, inp, b)).cuda())
+            outputs.append(torch.empty(b, sum(spec.linear(n).N for n in names), dtype=torch.float16, device="cuda"))
+    pager = ts.make_pager(b)
+    pager.bind(inputs, outputs)
+    compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    step_bytes = L * sum(algorithmic_bytes(spec.fmt, sum(spec.linear(n).N for n in names), spec.linear(names[0]).K, b)
+                         for names, _ in GROUPS)
+
+    bw_h2d = None
+    if streamed_bytes:
+        slot = torch.empty(ts.block_bytes, dtype=torch.uint8, device="cuda")
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        copy_ms = []
+        nB = L - nA
+        with torch.cuda.stream(copy):
+            for i in range(12):
+                j = i % nB
+                blk = ts.pool[j * ts.block_bytes:(j + 1) * ts.block_bytes]
+                ev0.record(copy)
+                slot.copy_(blk, non_blocking=True)
+                ev1.record(copy)
+                ev1.synchronize()
+                if i >= 2:
+                    copy_ms.append(ev0.elapsed_time(ev1))
+        del slot
+        bw_h2d = ts.block_bytes / (statistics.median(copy_ms) * 1e-3) / 1e9
+        log(f"host-to-device: {bw_h2d:.2f} GB/s (median of {len(copy_ms)} copies of {ts.block_bytes / 1e6:.1f} MB)")
+
+    for _ in range(args.warmup):
+        pager.run(b, compute, copy)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        pager.run(b, compute, copy)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    pager.close()
+    copy_serial_ms = streamed_bytes / (bw_h2d * 1e9) * 1e3 if bw_h2d else 0.0
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32 on int4 codes" if spec.fmt == "int4o" else "f16xf16->f32 on int8 codes",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}, batch {b}, {args.hbm_budget:g} GB device budget: "
+                               f"{nA} layers resident, {L - nA} streamed from pinned host memory",
+                   "format": spec.fmt, "layers": L, "hidden": spec.hidden, "intermediate": spec.inter,
+                   "q_heads": spec.q_heads, "kv_heads": spec.kv_heads, "head_dim": spec.head_dim, "batch": b,
+                   "runner": "tiered", "hbm_budget_bytes": budget, "resident_layers": nA,
+                   "streamed_layers": L - nA, "layer_block_bytes": ts.block_bytes,
+                   "algorithmic_bytes_per_step": step_bytes},
+        "decode_tok_s": round(b / (ms_per_step * 1e-3), 3),
+        "tiered": {"planned_device_bytes": int(ts.planned_device_bytes), "streamed_bytes_per_step": streamed_bytes,
+                   "h2d_gbs_measured": round(bw_h2d, 3) if bw_h2d else None,
+                   "copy_serial_ms": round(copy_serial_ms, 3),
+                   "overlap_efficiency": round(copy_serial_ms / ms_per_step, 4) if bw_h2d else None},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def bench_streamed(args, spec, b, log):

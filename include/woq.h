@@ -178,6 +178,39 @@ int woq_layout_int4o_inverse(const uint8_t* dev_codes, const uint16_t* dev_scale
                              const uint16_t* dev_wout, int64_t N, const woq_int4o_geom* g,
                              uint8_t* packed, uint16_t* scales, uint16_t* w_out);
 
+/* ------------------------------------------------- device: encoders (prep) */
+
+/*
+ * The INT8 encoding of woq_quantize_int8 computed on the device, written
+ * straight into the INT8 device layout (woq_layout_int8), bit for bit what the
+ * host functions give.  W: fp32 [N, K] row-major in device memory (4-byte
+ * aligned); dev: woq_int8_dev_bytes(N, K) bytes (16-byte aligned); *scale
+ * (device fp32) receives the scale - it doubles as the running maximum while
+ * the call runs; *status (device int32) receives 0, or WOQ_ERANGE if W holds a
+ * NaN or an infinity (then *scale is NaN and every code 0).  Asynchronous on
+ * stream: four launches (maximum, codes, scale, status clear).  For weights
+ * that already sit in device memory or arrive layer by layer: the host keeps
+ * no copy (the bounded-memory prep of "On-The-Fly Weight Synthesizer
+ * (OTF-LLM Engine)", item 2, done by the GPU).
+ */
+int woq_quantize_int8_dev(const float* W, int64_t N, int64_t K, uint8_t* dev, float* scale, int32_t* status,
+                          void* stream);
+
+/*
+ * The outlier-aware INT4 encoding of woq_quantize_int4o under perm (device
+ * int32 [g->K]) computed on the device, written straight into the INT4O
+ * device layout (woq_layout_int4o; sizes from woq_int4o_dev_sizes, each array
+ * 16-byte aligned; dev_wout may be null when g->n_out8 == 0), bit for bit what
+ * the host functions give.  W: fp32 [N, g->K] row-major in device memory.
+ * *status (device int32) receives 0; WOQ_ERANGE for a non-finite weight or a
+ * group scale that overflows fp16; WOQ_EINVAL for a permutation entry outside
+ * [0, K) (that entry reads as 0; a repeated entry is not detected - perm must
+ * come from woq_outlier_select).  Asynchronous on stream.
+ */
+int woq_quantize_int4o_dev(const float* W, int64_t N, const int32_t* perm, const woq_int4o_geom* g,
+                           uint8_t* dev_codes, uint16_t* dev_scales, uint16_t* dev_wout, int32_t* status,
+                           void* stream);
+
 /* ----------------------------------------------------------- device ops */
 
 #define WOQ_MAX_SEGMENTS 8
@@ -393,33 +426,67 @@ typedef struct {
 typedef struct woq_pager woq_pager;
 
 /*
- * Streamed decode over INT8 layers that live in pinned host memory ("Open
+ * Tier plan under a device-memory budget (NTransformer summary, "3-Tier
+ * Adaptive Caching Architecture": tier A layers stay resident in device
+ * memory, tier B layers live in pinned host memory and are streamed in by
+ * host-to-device DMA; host function).  Layers are taken in order: layers
+ * 0 .. n_A-1 are resident, the rest streamed, with n_A the largest count for
+ * which the resident bytes plus, when any layer streams, two slots of the
+ * largest streamed block fit budget_bytes.  Resident layers come first so that
+ * the first copies overlap their products.  resident[l] (int32 [n_layers])
+ * receives 1 or 0; *device_bytes (may be null) the bytes the plan places in
+ * device memory.  WOQ_ENOMEM if not even two slots fit; WOQ_EINVAL if a layer
+ * has no bytes.
+ */
+int woq_plan_tiers(const int64_t* layer_bytes, int32_t n_layers, int64_t budget_bytes, int32_t* resident,
+                   int64_t* device_bytes);
+
+/*
+ * Tiered decode pass over n_layers layers of steps_per_layer products each
+ * (steps in layer order; each step reads inputs[in_slot] and writes
+ * outputs[out_slot] of woq_pager_run, as woq_stack_run does).  Layer l is
+ * resident when layer_bytes[l] == 0: its steps hold device pointers.  Otherwise
+ * it is streamed: its block is layer_bytes[l] bytes at pinned_pool +
+ * layer_off[l] (page-locked memory from hipHostMalloc or an equivalent pinned
+ * allocation, owned by the caller, valid while the pager exists), and the
+ * weight pointers of its steps (w8.codes; w4.codes, w4.scales, w4.w_out) hold
+ * byte offsets into that block instead of addresses, each 16-byte aligned with
+ * its array inside the block (WOQ_EINVAL otherwise).  INT8 and INT4O steps may
+ * be mixed as in woq_stack_create, whose limits apply (max_b <= 8 with INT8
+ * steps, <= 64 otherwise).  The pager allocates two device slots of the
+ * largest streamed block, its events and the stack runner's workspace.
+ */
+int woq_tiered_create(const void* pinned_pool, const int64_t* layer_off, const int64_t* layer_bytes,
+                      int32_t n_layers, const woq_stack_step* steps, int32_t steps_per_layer, int64_t max_b,
+                      woq_pager** out);
+
+/*
+ * Streamed decode over INT8 layers that all live in pinned host memory ("Open
  * Origin - ELG Stream Layer", Key Features 1-3: a block-allocated INT8 pool in
  * pinned RAM, asynchronous layer paging, double-buffered prefetch of layer N+1
- * on a secondary stream while layer N computes).  Layer l's block is
- * layer_bytes[l] bytes at pinned_pool + layer_off[l] (page-locked memory from
- * hipHostMalloc or an equivalent pinned allocation, owned by the caller, valid
- * while the pager exists).  steps holds steps_per_layer entries per layer, in
- * layer order.  The pager allocates two device slots of max(layer_bytes) and
- * its events; WOQ_ENOMEM if that fails.  1 <= max_b <= 8.
+ * on a secondary stream while layer N computes): woq_tiered_create with every
+ * layer streamed, step s of layer l an INT8 product whose codes start
+ * code_offset bytes into the layer's block, reading inputs[l * steps_per_layer
+ * + s] and writing outputs[l * steps_per_layer + s].  1 <= max_b <= 8.
  */
 int woq_pager_create(const void* pinned_pool, const int64_t* layer_off, const int64_t* layer_bytes,
                      int32_t n_layers, const woq_pager_step* steps, int32_t steps_per_layer, int64_t max_b,
                      woq_pager** out);
 
 /*
- * One streamed pass: on copy_stream, layer l's block is copied into slot
- * l mod 2 once the products of layer l-2 have finished with that slot; on
- * compute_stream, layer l's products start once its copy has landed.  Step s
- * of layer l reads inputs[l * steps_per_layer + s] (fp16 [b, K]) and writes
- * outputs[l * steps_per_layer + s] (fp16 [b, N]).  The two streams must be
- * distinct; both are left with work queued (synchronise compute_stream to wait
- * for the outputs).  Passes of one pager must not overlap.
+ * One pass: on copy_stream, the j-th streamed layer's block is copied into
+ * slot j mod 2 once the products of streamed layer j-2 have finished with
+ * that slot (the first two copies start at once, behind any work already
+ * queued on compute_stream); on compute_stream, the layers run in order, a
+ * streamed layer's products once its copy has landed.  The two streams must
+ * be distinct when any layer streams; both are left with work queued
+ * (synchronise compute_stream to wait for the outputs).  Passes of one pager
+ * must not overlap.
  */
 int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
                   void* compute_stream, void* copy_stream);
 
-/* Release the slots and events (after both streams have finished). */
+/* Release the slots, events and workspace (after both streams have finished). */
 int woq_pager_destroy(woq_pager* p);
 
 /* ------------------------------------------------------------ measurement */

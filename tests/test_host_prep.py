@@ -317,6 +317,83 @@ def test_pager_create_validates_before_allocating():
     assert lib.woq_pager_destroy(None) == woq.WOQ_OK
 
 
+def test_tiered_create_validates_streamed_offsets():
+    """A streamed INT4O step's codes, scales and outlier arrays must lie inside
+    its layer's block at 16-byte aligned offsets (checked before any device
+    call)."""
+    import ctypes
+    lib = woq.lib()
+    pool = np.zeros(1 << 16, np.uint8)
+    N, K = 32, 300
+    g = woq.woq_int4o_geometry(K)
+    cb, sb, wb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    assert lib.woq_int4o_dev_sizes(N, ctypes.byref(g), ctypes.byref(cb), ctypes.byref(sb), ctypes.byref(wb)) == 0
+    cb, sb, wb = cb.value, sb.value, wb.value
+    total = cb + sb + wb
+
+    def create(codes, scales, wout, layer_bytes):
+        st = woq.StackStep()
+        st.fmt, st.in_slot, st.out_slot = woq.FMT_INT4O, 0, 0
+        st.w4.codes, st.w4.scales, st.w4.w_out = codes, scales, wout
+        st.w4.N, st.w4.geom = N, g
+        st.perm = 16          # never read: creation stops at the offset checks
+        steps = (woq.StackStep * 1)(st)
+        off = (ctypes.c_int64 * 1)(0)
+        nb = (ctypes.c_int64 * 1)(layer_bytes)
+        h = ctypes.c_void_p()
+        return lib.woq_tiered_create(woq._ptr(pool), off, nb, 1, steps, 1, 1, ctypes.byref(h))
+
+    assert create(0, cb, cb + sb, total - 16) == woq.WOQ_EINVAL     # outliers run past the block
+    assert create(8, cb + 16, cb + sb + 16, total + 64) == woq.WOQ_EINVAL   # codes misaligned
+    assert create(0, cb + 4, cb + sb + 16, total + 64) == woq.WOQ_EINVAL    # scales misaligned
+    h = ctypes.c_void_p()
+    assert lib.woq_tiered_create(None, None, None, 1, None, 1, 1, ctypes.byref(h)) == woq.WOQ_EINVAL
+
+
+def test_plan_tiers_properties():
+    """Resident layers form a prefix; the plan fits the budget; one more
+    resident layer would not; everything resident when the model fits; two
+    slots are the floor."""
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        L = int(rng.integers(1, 12))
+        lb = rng.integers(1, 1000, L)
+        budget = int(rng.integers(0, int(lb.sum()) + 2000))
+        try:
+            res, dev = woq.woq_plan_tiers(lb, budget)
+        except woq.WoqError as e:
+            assert e.status == woq.WOQ_ENOMEM
+            assert budget < 2 * lb.max() and budget < lb.sum()
+            continue
+        nA = int(res.sum())
+        assert np.all(res[:nA] == 1) and np.all(res[nA:] == 0)
+
+        def need(n):
+            return int(lb[:n].sum()) + (2 * int(lb[n:].max()) if n < L else 0)
+        assert dev == need(nA) <= budget
+        assert all(need(n) > budget for n in range(nA + 1, L + 1))
+        if budget >= lb.sum():
+            assert nA == L and dev == lb.sum()
+
+
+def test_plan_tiers_equal_layers_closed_form():
+    """Equal blocks of B bytes: n_A = L if L*B fits, else floor(budget/B) - 2
+    (two slots), and not enough for two slots is an error."""
+    B, L = 454_000_000, 80
+    for budget_gb in (1, 16, 24, 30, 36.3, 36.4, 288):
+        budget = int(budget_gb * 1e9)
+        if budget < 2 * B:
+            with pytest.raises(woq.WoqError):
+                woq.woq_plan_tiers([B] * L, budget)
+            continue
+        res, dev = woq.woq_plan_tiers([B] * L, budget)
+        want = L if L * B <= budget else min(L - 1, budget // B - 2)
+        assert res.sum() == want, budget_gb
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_plan_tiers([0, 5], 100)
+    assert e.value.status == woq.WOQ_EINVAL
+
+
 # ------------------------------------------------- permutation positions
 
 @pytest.mark.parametrize("K", [8, 130, 1000, 3072])

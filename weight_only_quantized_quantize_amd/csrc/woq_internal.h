@@ -21,6 +21,11 @@ void set_hip_error(int code);
 // reports); set by the runner's timing pass around one launch.
 void set_launch_events(void* start, void* stop);
 
+// Launch step i of a stack with the given step contents (the entry itself or
+// a copy whose weight pointers were moved); argument checks as woq_stack_run.
+int stack_run_step(woq_stack* st, int64_t i, const woq_stack_step* s, const uint16_t* x, uint16_t* y, int64_t b,
+                   void* stream);
+
 inline int64_t round_up(int64_t a, int64_t m) { return (a + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t a, int64_t m) { return (a + m - 1) / m; }
 

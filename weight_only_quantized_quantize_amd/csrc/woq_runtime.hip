@@ -294,32 +294,37 @@ bool fold_permutation(const woq_stack_step& s, int64_t b) {
            woq_qgemv_int4o_x_supported(&g, b) && (g.K & 7) == 0;
 }
 
+// One step (the step table's entry i, or a copy of it whose weight pointers
+// were moved, e.g. into a pager slot); ev (2 entries, or null) brackets the
+// product launch.
+int run_step(woq_stack* st, size_t i, const woq_stack_step& s, const uint16_t* x, uint16_t* y, int64_t b,
+             void* stream, hipEvent_t* ev) {
+    int rc;
+    if (s.fmt == WOQ_FMT_INT4O && st->pos[i] && fold_permutation(s, b) && woq::aligned16(x)) {
+        // permutation folded into the product: one launch
+        if (ev) woq::set_launch_events(ev[0], ev[1]);
+        rc = woq_qgemv_int4o_x(&s.w4, x, s.w4.geom.K, st->pos[i], b, y, s.w4.N, stream);
+        if (ev) woq::set_launch_events(nullptr, nullptr);
+        return rc;
+    }
+    if (s.fmt == WOQ_FMT_INT4O) {
+        rc = woq_permute_x(x, s.w4.geom.K, s.perm, b, &s.w4.geom, st->xp, stream);
+        if (rc) return rc;
+    }
+    // with events, the product launch records them at its own dispatch boundaries
+    if (ev) woq::set_launch_events(ev[0], ev[1]);
+    if (s.fmt == WOQ_FMT_INT4O) rc = woq_qgemv_int4o(&s.w4, st->xp, b, y, s.w4.N, stream);
+    else rc = woq_qgemv_int8(&s.w8, x, s.w8.K, b, y, s.w8.N, stream);
+    if (ev) woq::set_launch_events(nullptr, nullptr);
+    return rc;
+}
+
 // One pass over the steps; ev (2 per step) brackets each product launch.
 int run_pass(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b, void* stream,
              hipEvent_t* ev) {
-    hipStream_t hs = (hipStream_t)stream;
     for (size_t i = 0; i < st->steps.size(); ++i) {
         const woq_stack_step& s = st->steps[i];
-        const uint16_t* x = inputs[s.in_slot];
-        uint16_t* y = outputs[s.out_slot];
-        int rc;
-        if (s.fmt == WOQ_FMT_INT4O && st->pos[i] && fold_permutation(s, b) && woq::aligned16(x)) {
-            // permutation folded into the product: one launch
-            if (ev) woq::set_launch_events(ev[2 * i], ev[2 * i + 1]);
-            rc = woq_qgemv_int4o_x(&s.w4, x, s.w4.geom.K, st->pos[i], b, y, s.w4.N, stream);
-            if (ev) woq::set_launch_events(nullptr, nullptr);
-            if (rc) return rc;
-            continue;
-        }
-        if (s.fmt == WOQ_FMT_INT4O) {
-            rc = woq_permute_x(x, s.w4.geom.K, s.perm, b, &s.w4.geom, st->xp, stream);
-            if (rc) return rc;
-        }
-        // with events, the product launch records them at its own dispatch boundaries
-        if (ev) woq::set_launch_events(ev[2 * i], ev[2 * i + 1]);
-        if (s.fmt == WOQ_FMT_INT4O) rc = woq_qgemv_int4o(&s.w4, st->xp, b, y, s.w4.N, stream);
-        else rc = woq_qgemv_int8(&s.w8, x, s.w8.K, b, y, s.w8.N, stream);
-        if (ev) woq::set_launch_events(nullptr, nullptr);
+        int rc = run_step(st, i, s, inputs[s.in_slot], outputs[s.out_slot], b, stream, ev ? ev + 2 * i : nullptr);
         if (rc) return rc;
     }
     return WOQ_OK;
@@ -395,6 +400,16 @@ int prepare_fused(woq_stack* st, int64_t b) {
 }
 
 }  // namespace
+
+namespace woq {
+
+int stack_run_step(woq_stack* st, int64_t i, const woq_stack_step* s, const uint16_t* x, uint16_t* y, int64_t b,
+                   void* stream) {
+    if (!st || !s || i < 0 || i >= (int64_t)st->steps.size() || b < 1 || b > st->max_b) return WOQ_EINVAL;
+    return run_step(st, (size_t)i, *s, x, y, b, stream, nullptr);
+}
+
+}  // namespace woq
 
 extern "C" {
 

@@ -40,8 +40,13 @@ def _map_weights(spec, jobs, weight_fn, fn, threads):
         return list(ex.map(run, jobs))
 
 
-class ResidentStack:
-    """All layers of a stack resident in HBM plus the runner.
+def _concat(parts, i):
+    return np.concatenate([p[i] for p in parts]) if len(parts) > 1 else parts[0][i]
+
+
+class _QuantisedStack:
+    """Global permutations (INT4O) and per-layer quantisation, shared by the
+    resident and tiered stacks.
 
     spec: object with .fmt ("int8" | "int4o"), .layers, .linears(),
           .space_width(space), .bmax
@@ -49,27 +54,32 @@ class ResidentStack:
     profile_fn(space): fp16 activation profile [T, K] of an input space
     """
 
-    def __init__(self, spec, weight_fn, profile_fn=None, device="cuda", threads=None, layers=None, log=None):
+    def _setup(self, spec, weight_fn, profile_fn, device, threads, layers, log, perms=None):
         import torch
         self.spec = spec
         self.device = device
         self.fmt = spec.fmt
         self.n_layers = spec.layers if layers is None else layers
-        threads = threads or min(16, os.cpu_count() or 1)
-        log = log or (lambda *a: None)
-        lin_by = {l.name: l for l in spec.linears()}
+        self.threads = threads or min(16, os.cpu_count() or 1)
+        self.log = log or (lambda *a: None)
+        self.weight_fn = weight_fn
         self.perm_host = {}
         self.perm_dev = {}
         self.geom = {}
-        if self.fmt == "int4o":
+        if self.fmt == "int4o" and perms is not None:
+            for space, perm in perms.items():           # permutations chosen elsewhere (e.g. another stack)
+                self.perm_host[space] = np.ascontiguousarray(perm, np.int32)
+                self.perm_dev[space] = torch.from_numpy(self.perm_host[space]).to(device)
+                self.geom[space] = woq.woq_int4o_geometry(spec.space_width(space))
+        elif self.fmt == "int4o":
             spaces = sorted({l.space for l in spec.linears()})
             jobs = [(layer, lin) for layer in range(spec.layers) for lin in spec.linears()]
-            log(f"column sums over {len(jobs)} weights")
+            self.log(f"column sums over {len(jobs)} weights")
 
             def colsum(layer, lin, W):
                 return woq.woq_colabs_accumulate(W, np.zeros(lin.K))
 
-            sums = _map_weights(spec, jobs, weight_fn, colsum, threads)
+            sums = _map_weights(spec, jobs, weight_fn, colsum, self.threads)
             for space in spaces:
                 K = spec.space_width(space)
                 acc = np.zeros(K)
@@ -80,42 +90,58 @@ class ResidentStack:
                 self.perm_host[space] = perm
                 self.perm_dev[space] = torch.from_numpy(perm).to(device)
                 self.geom[space] = woq.woq_int4o_geometry(K)
-        self.layers = []          # per layer: list of (group names, input index, device weight)
-        chunk = 4
-        for l0 in range(0, self.n_layers, chunk):
-            ls = range(l0, min(self.n_layers, l0 + chunk))
+
+    def _quantised_layers(self, layer_ids):
+        """Yield (layer, [(names, input index, parts)]) in layer order, four
+        layers quantised at a time."""
+        spec = self.spec
+        layer_ids = list(layer_ids)
+        for c0 in range(0, len(layer_ids), 4):
+            ls = layer_ids[c0:c0 + 4]
             jobs = [(layer, lin) for layer in ls for lin in spec.linears()]
-            log(f"quantising layers {ls.start}..{ls.stop - 1}")
+            self.log(f"quantising layers {ls[0]}..{ls[-1]}")
             if self.fmt == "int4o":
-                res = _map_weights(spec, jobs, weight_fn,
+                res = _map_weights(spec, jobs, self.weight_fn,
                                    lambda layer, lin, W: woq.woq_quantize_int4o(W, self.perm_host[lin.space]),
-                                   threads)
+                                   self.threads)
             else:
-                res = _map_weights(spec, jobs, weight_fn, lambda layer, lin, W: woq.woq_quantize_int8(W), threads)
+                res = _map_weights(spec, jobs, self.weight_fn, lambda layer, lin, W: woq.woq_quantize_int8(W),
+                                   self.threads)
             got = {(layer, lin.name): r for (layer, lin), r in zip(jobs, res)}
+            del res
             for layer in ls:
-                groups = []
-                for names, inp in GROUPS:
-                    parts = [got[(layer, n)] for n in names]
-                    if self.fmt == "int4o":
-                        dev = woq.DeviceInt4o(parts, self.geom[lin_by[names[0]].space], device)
-                    else:
-                        dev = woq.DeviceInt8(parts, device)
-                    groups.append((names, inp, dev))
-                self.layers.append(groups)
-            del got, res
+                yield layer, [(names, inp, [got.pop((layer, n)) for n in names]) for names, inp in GROUPS]
+
+    def _space(self, names):
+        return self.spec.linear(names[0]).space
+
+    def _device(self, names, parts):
+        if self.fmt == "int4o":
+            return woq.DeviceInt4o(parts, self.geom[self._space(names)], self.device)
+        return woq.DeviceInt8(parts, self.device)
+
+    def _resident_step(self, names, dev, slot):
+        if self.fmt == "int4o":
+            return woq.step_int4o(dev, self.perm_dev[self._space(names)], slot, slot)
+        return woq.step_int8(dev, slot, slot)
+
+
+class ResidentStack(_QuantisedStack):
+    """All layers of a stack resident in HBM plus the runner."""
+
+    def __init__(self, spec, weight_fn, profile_fn=None, device="cuda", threads=None, layers=None, log=None,
+                 perms=None):
+        self._setup(spec, weight_fn, profile_fn, device, threads, layers, log, perms)
+        self.layers = []          # per layer: list of (group names, input index, device weight)
+        for layer, groups in self._quantised_layers(range(self.n_layers)):
+            self.layers.append([(names, inp, self._device(names, parts)) for names, inp, parts in groups])
         self.runner = None
 
     def steps(self):
         out = []
         for layer, groups in enumerate(self.layers):
             for gi, (names, inp, dev) in enumerate(groups):
-                slot = 4 * layer + gi
-                if self.fmt == "int4o":
-                    space = self.spec.linear(names[0]).space
-                    out.append(woq.step_int4o(dev, self.perm_dev[space], slot, slot))
-                else:
-                    out.append(woq.step_int8(dev, slot, slot))
+                out.append(self._resident_step(names, dev, 4 * layer + gi))
         return out
 
     def make_runner(self, max_b: int):
@@ -139,6 +165,99 @@ class ResidentStack:
                     if x is not None:
                         tot += x.numel() * x.element_size()
         return tot
+
+
+def _align(n: int, a: int = 256) -> int:
+    return -(-n // a) * a
+
+
+class TieredStack(_QuantisedStack):
+    """A stack split by woq_plan_tiers under a device-memory budget: the first
+    layers resident in HBM (tier A), the rest in one pinned host pool (tier B)
+    streamed through the pager's two slots.  Works for both formats.
+
+    A streamed layer's block holds, for q|k|v, o, gate|up and down in turn, the
+    device layout arrays (INT4O: codes, scales, outlier weights; INT8: codes),
+    each at a 256-byte aligned offset."""
+
+    def __init__(self, spec, weight_fn, profile_fn, budget_bytes: int, device="cuda", threads=None, layers=None,
+                 log=None, resident=None, perms=None):
+        import torch
+        self._setup(spec, weight_fn, profile_fn, device, threads, layers, log, perms)
+        # block layout of one layer (identical for every layer)
+        self.array_offsets = []        # per group: offsets of its arrays in the block
+        o = 0
+        for names, _ in GROUPS:
+            N = sum(spec.linear(n).N for n in names)
+            if self.fmt == "int4o":
+                sizes = woq.woq_int4o_dev_sizes(N, self.geom[self._space(names)])
+            else:
+                sizes = (woq.lib().woq_int8_dev_bytes(N, spec.linear(names[0]).K),)
+            offs = []
+            for sz in sizes:
+                offs.append(o)
+                o += _align(sz)
+            self.array_offsets.append(offs)
+        self.block_bytes = o
+        if resident is None:
+            resident, self.planned_device_bytes = woq.woq_plan_tiers([o] * self.n_layers, budget_bytes)
+        self.resident = np.asarray(resident, np.int32)
+        streamed = [l for l in range(self.n_layers) if not self.resident[l]]
+        self.pool = torch.empty(max(1, len(streamed) * o), dtype=torch.uint8, pin_memory=True)
+        pool_np = self.pool.numpy()
+        self.layer_off = [0] * self.n_layers
+        self.layer_bytes = [0] * self.n_layers
+        for j, l in enumerate(streamed):
+            self.layer_off[l] = j * o
+            self.layer_bytes[l] = o
+        self.devices = {}
+        self.step_list = []
+        for layer, groups in self._quantised_layers(range(self.n_layers)):
+            for gi, (names, inp, parts) in enumerate(groups):
+                slot = 4 * layer + gi
+                if self.resident[layer]:
+                    dev = self._device(names, parts)
+                    self.devices[slot] = dev
+                    self.step_list.append(self._resident_step(names, dev, slot))
+                    continue
+                base = self.layer_off[layer]
+                offs = self.array_offsets[gi]
+                st = woq.StackStep()
+                st.in_slot = st.out_slot = slot
+                if self.fmt == "int4o":
+                    g = self.geom[self._space(names)]
+                    arrays = woq.woq_layout_int4o(_concat(parts, 0), _concat(parts, 1), _concat(parts, 2), g)
+                    for a, off in zip(arrays, offs):
+                        v = a.view(np.uint8)
+                        pool_np[base + off: base + off + v.size] = v
+                    st.fmt = woq.FMT_INT4O
+                    st.w4.codes, st.w4.scales, st.w4.w_out = offs
+                    st.w4.N = sum(p[0].shape[0] for p in parts)
+                    st.w4.geom = g
+                    st.perm = self.perm_dev[self._space(names)].data_ptr()
+                else:
+                    q = _concat(parts, 0)
+                    v = woq.woq_layout_int8(q)
+                    pool_np[base + offs[0]: base + offs[0] + v.size] = v
+                    st.fmt = woq.FMT_INT8
+                    st.w8.codes = offs[0]
+                    st.w8.N, st.w8.K, st.w8.nseg = q.shape[0], q.shape[1], len(parts)
+                    end = 0
+                    for i, (qi, sc) in enumerate(parts):
+                        end += qi.shape[0]
+                        st.w8.seg_end[i] = end
+                        st.w8.seg_scale[i] = float(sc)
+                self.step_list.append(st)
+
+    @property
+    def n_resident(self) -> int:
+        return int(self.resident.sum())
+
+    def streamed_bytes(self) -> int:
+        return sum(self.layer_bytes)
+
+    def make_pager(self, max_b: int):
+        return woq.Pager(self.pool, self.layer_off, self.layer_bytes, self.step_list, len(GROUPS), max_b)
 
 
 class StreamedInt8Stack:

@@ -97,6 +97,12 @@ _SIGS = {
     "woq_stack_time_fused": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
                                      POINTER(c_float)]),
     "woq_stack_destroy": (c_int, [c_void_p]),
+    "woq_quantize_int8_dev": (c_int, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "woq_quantize_int4o_dev": (c_int, [c_void_p, c_int64, c_void_p, POINTER(Int4oGeom), c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p]),
+    "woq_plan_tiers": (c_int, [c_void_p, c_int32, c_int64, c_void_p, POINTER(c_int64)]),
+    "woq_tiered_create": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int64), c_int32, POINTER(StackStep),
+                                  c_int32, c_int64, POINTER(c_void_p)]),
     "woq_pager_create": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int64), c_int32, POINTER(PagerStep), c_int32,
                                  c_int64, POINTER(c_void_p)]),
     "woq_pager_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_void_p]),
@@ -275,6 +281,25 @@ def woq_qgemv_int8(w: Int8W, x, y, stream=None, b: int | None = None):
     _check(_lib().woq_qgemv_int8(ctypes.byref(w), _ptr(x), x.shape[1], b, _ptr(y), y.shape[1], _stream(stream)),
            "woq_qgemv_int8")
     return y
+
+
+def woq_quantize_int8_dev(W, dev, scale, status, stream=None):
+    """INT8 encoding of the device tensor W (fp32 [N, K]) into the device
+    layout ``dev`` (uint8 tensor of woq_int8_dev_bytes) and ``scale`` (fp32
+    device tensor [1]); ``status`` (int32 device tensor [1]) receives 0 or
+    WOQ_ERANGE."""
+    N, K = W.shape
+    _check(_lib().woq_quantize_int8_dev(_ptr(W), N, K, _ptr(dev), _ptr(scale), _ptr(status), _stream(stream)),
+           "woq_quantize_int8_dev")
+
+
+def woq_quantize_int4o_dev(W, perm_dev, g: Int4oGeom, codes, scales, w_out, status, stream=None):
+    """Outlier-aware INT4 encoding of the device tensor W (fp32 [N, K]) into the
+    device layout arrays (torch tensors sized by woq_int4o_dev_sizes)."""
+    N = W.shape[0]
+    _check(_lib().woq_quantize_int4o_dev(_ptr(W), N, _ptr(perm_dev), ctypes.byref(g), _ptr(codes), _ptr(scales),
+                                         _ptr(w_out) if w_out is not None else None, _ptr(status),
+                                         _stream(stream)), "woq_quantize_int4o_dev")
 
 
 def woq_embed_int8(w: Int8W, ids, y, stream=None, b: int | None = None):
@@ -460,18 +485,35 @@ def step_int8(dev: "DeviceInt8", in_slot: int, out_slot: int) -> StackStep:
 
 # ------------------------------------------------------------ streamed pager
 
+def woq_plan_tiers(layer_bytes, budget_bytes: int):
+    """(resident flags int32 [L], device bytes) of the tier plan under a budget."""
+    lb = np.ascontiguousarray(layer_bytes, np.int64)
+    res = np.zeros(lb.size, np.int32)
+    dev = c_int64()
+    _check(_lib().woq_plan_tiers(_ptr(lb), lb.size, int(budget_bytes), _ptr(res), ctypes.byref(dev)),
+           "woq_plan_tiers")
+    return res, dev.value
+
+
 class Pager:
-    """Owns a woq_pager over a caller-owned pinned pool (kept referenced)."""
+    """Owns a woq_pager over a caller-owned pinned pool (kept referenced).
+
+    ``steps`` are PagerStep (INT8 layers, all streamed: woq_pager_create) or
+    StackStep (tiered: woq_tiered_create, layer_bytes[l] == 0 marks a resident
+    layer, streamed steps carry byte offsets in their weight pointers)."""
 
     def __init__(self, pool, layer_off, layer_bytes, steps, steps_per_layer: int, max_b: int):
         self.pool = pool
         self.off = (c_int64 * len(layer_off))(*layer_off)
         self.bytes = (c_int64 * len(layer_bytes))(*layer_bytes)
-        self.steps = (PagerStep * len(steps))(*steps)
+        tiered = isinstance(steps[0], StackStep)
+        self.steps = ((StackStep if tiered else PagerStep) * len(steps))(*steps)
         self.n = len(steps)
         h = c_void_p()
-        _check(_lib().woq_pager_create(_ptr(pool), self.off, self.bytes, len(layer_off), self.steps, steps_per_layer,
-                                       max_b, ctypes.byref(h)), "woq_pager_create")
+        pool_ptr = _ptr(pool) if pool is not None else None
+        fn = "woq_tiered_create" if tiered else "woq_pager_create"
+        _check(getattr(_lib(), fn)(pool_ptr, self.off, self.bytes, len(layer_off), self.steps, steps_per_layer,
+                                   max_b, ctypes.byref(h)), fn)
         self.handle = h
 
     def bind(self, inputs, outputs):
