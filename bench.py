@@ -211,6 +211,8 @@ def main():
     ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
                     help="fused: one persistent launch per step; launch: one launch per permutation and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prep", action="store_true",
+                    help="stacks 2-4: time the encoders (device and host) on the linears of one layer")
     ap.add_argument("--hbm-budget", type=float, default=None,
                     help="stacks 2-4: device-memory budget in GB for the weights; the first layers stay resident, "
                          "the rest stream from pinned host memory (tiered pass)")
@@ -241,6 +243,8 @@ def main():
         return bench_streamed(args, spec, b, log)
     if args.hbm_budget is not None:
         return bench_tiered(args, spec, b, log)
+    if args.prep:
+        return bench_prep(args, spec, log)
     t0 = time.perf_counter()
     rs = ResidentStack(spec, lambda layer, lin, out: synth.weight(spec, layer, lin, out=out),
                        lambda space: synth.profile(spec, space), layers=args.layers, log=log)
@@ -400,6 +404,86 @@ def bench_vocab(args, spec, rs, b, run, stream, log):
             "lm_head_launches": 2,
             "ms_per_step_with_vocab": round(full_ms, 5),
             "decode_tok_s_with_vocab": round(b / (full_ms * 1e-3), 2)}
+
+
+def bench_prep(args, spec, log):
+    """Encoders on the seven linears of layer 0: the device encoder (fp32
+    weights already in device memory, HIP events around the encoder launches)
+    against the host encoder plus the host layout transform (wall clock, all
+    host threads).  Both give the same bytes (checked here)."""
+    import numpy as np
+    import torch
+    import synth
+    from weight_only_quantized_quantize_amd import woq
+
+    lins = spec.linears()
+    Ws = [synth.weight(spec, 0, lin) for lin in lins]
+    perms = {}
+    if spec.fmt == "int4o":
+        # the selector over this layer's linears (the stack selects over all layers)
+        for sp in sorted({lin.space for lin in lins}):
+            acc = np.zeros(spec.space_width(sp))
+            for lin, W in zip(lins, Ws):
+                if lin.space == sp:
+                    woq.woq_colabs_accumulate(W, acc)
+            perms[sp] = woq.woq_outlier_select(acc, synth.profile(spec, sp))
+    stream = torch.cuda.current_stream()
+    dev_out, host_out = [], []
+    Wd = [torch.from_numpy(W).cuda() for W in Ws]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run_device():
+        outs = []
+        for lin, W in zip(lins, Wd):
+            if spec.fmt == "int4o":
+                g = woq.woq_int4o_geometry(lin.K)
+                cb, sb, wb = woq.woq_int4o_dev_sizes(lin.N, g)
+                c = torch.empty(cb, dtype=torch.uint8, device="cuda")
+                sc = torch.empty(sb // 2, dtype=torch.int16, device="cuda")
+                wo = torch.empty(wb // 2, dtype=torch.int16, device="cuda")
+                pd = torch.from_numpy(perms[lin.space]).cuda()
+                outs.append((c, sc, wo, pd))
+            else:
+                outs.append((torch.empty(woq.lib().woq_int8_dev_bytes(lin.N, lin.K), dtype=torch.uint8,
+                                         device="cuda"), torch.empty(1, dtype=torch.float32, device="cuda")))
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for lin, W, o in zip(lins, Wd, outs):
+            if spec.fmt == "int4o":
+                woq.woq_quantize_int4o_dev(W, o[3], woq.woq_int4o_geometry(lin.K), o[0], o[1], o[2], status, stream)
+            else:
+                woq.woq_quantize_int8_dev(W, o[0], o[1], status, stream)
+        ev[1].record(stream)
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]), outs
+
+    run_device()                                   # warm-up
+    dev_ms, dev_out = min((run_device() for _ in range(3)), key=lambda t: t[0])
+    t0 = time.perf_counter()
+    for lin, W in zip(lins, Ws):
+        if spec.fmt == "int4o":
+            g = woq.woq_int4o_geometry(lin.K)
+            host_out.append(woq.woq_layout_int4o(*woq.woq_quantize_int4o(W, perms[lin.space]), g))
+        else:
+            q, sc = woq.woq_quantize_int8(W)
+            host_out.append((woq.woq_layout_int8(q), sc))
+    host_ms = (time.perf_counter() - t0) * 1e3
+    same = True
+    for d, h in zip(dev_out, host_out):
+        if spec.fmt == "int4o":
+            same &= np.array_equal(d[0].cpu().numpy(), h[0]) and np.array_equal(d[1].cpu().numpy().view(np.uint16), h[1])
+            same &= np.array_equal(d[2].cpu().numpy().view(np.uint16), h[2])
+        else:
+            same &= np.array_equal(d[0].cpu().numpy(), h[0]) and float(d[1].cpu()[0]) == float(h[1])
+    fp32_bytes = sum(W.nbytes for W in Ws)
+    print(json.dumps({
+        "workload": f"{spec.name}: encoders on the {len(lins)} linears of one layer",
+        "format": spec.fmt, "fp32_weight_bytes": fp32_bytes,
+        "device_ms": round(dev_ms, 3), "device_gbs_fp32_in": round(fp32_bytes / (dev_ms * 1e-3) / 1e9, 1),
+        "host_ms": round(host_ms, 1), "host_gbs_fp32_in": round(fp32_bytes / (host_ms * 1e-3) / 1e9, 2),
+        "host_threads": os.cpu_count(), "device_equals_host": bool(same),
+        "status": int(status.cpu()[0])}), flush=True)
 
 
 def bench_tiered(args, spec, b, log):

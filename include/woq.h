@@ -57,6 +57,8 @@ extern "C" {
 #define WOQ_EUNSUPPORTED (-5)  /* valid request that this build does not implement */
 #define WOQ_ERANGE       (-6)  /* value not representable: non-finite weight, fp16 scale overflow */
 #define WOQ_ETIMEOUT     (-7)  /* a fused stack run gave up waiting at a step boundary */
+#define WOQ_EIO          (-8)  /* a file could not be opened, read or written */
+#define WOQ_EFORMAT      (-9)  /* not a pool file, or a damaged one (magic, version, sizes or checksum) */
 
 #define WOQ_ABI_VERSION 1
 
@@ -200,7 +202,7 @@ int woq_quantize_int8_dev(const float* W, int64_t N, int64_t K, uint8_t* dev, fl
  * The outlier-aware INT4 encoding of woq_quantize_int4o under perm (device
  * int32 [g->K]) computed on the device, written straight into the INT4O
  * device layout (woq_layout_int4o; sizes from woq_int4o_dev_sizes, each array
- * 16-byte aligned; dev_wout may be null when g->n_out8 == 0), bit for bit what
+ * 16-byte aligned; an array of size 0 may be null), bit for bit what
  * the host functions give.  W: fp32 [N, g->K] row-major in device memory.
  * *status (device int32) receives 0; WOQ_ERANGE for a non-finite weight or a
  * group scale that overflows fp16; WOQ_EINVAL for a permutation entry outside
@@ -488,6 +490,36 @@ int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* 
 
 /* Release the slots, events and workspace (after both streams have finished). */
 int woq_pager_destroy(woq_pager* p);
+
+/* ------------------------------------------------------ persisted pool */
+
+/*
+ * A pool file holds the encoded layer blocks of a stack (device layouts, as
+ * streamed by the tiered pass) and opaque caller metadata, so that a later
+ * process loads them instead of encoding the weights again - the persisted
+ * INT8 pool of "Open Origin - ELG Stream Layer" (its first boot quantises and
+ * saves, later boots load), for either format.  Host functions; synchronous.
+ * Each block sits at a 4096-byte aligned offset with a 64-bit checksum (FNV-1a
+ * over 8-byte words of each 1 MiB chunk, then over the chunk hashes); the
+ * table and the metadata carry a checksum of their own.  Reads and writes use
+ * up to 16 threads.
+ */
+
+/* Write the file at path (replaced if it exists).  blocks[i] (host memory,
+ * pinned or not) of block_bytes[i] bytes.  WOQ_EIO on a file error. */
+int woq_pool_save(const char* path, const void* meta, int64_t meta_bytes, const void* const* blocks,
+                  const int64_t* block_bytes, int32_t n_blocks);
+
+/* Read the table: *n_blocks and *meta_bytes; the first max_blocks block sizes
+ * into block_bytes and the first meta_cap metadata bytes into meta (either may
+ * be null).  WOQ_EFORMAT for a file that is not an intact pool header. */
+int woq_pool_info(const char* path, int32_t* n_blocks, int64_t* meta_bytes, int64_t* block_bytes,
+                  int32_t max_blocks, void* meta, int64_t meta_cap);
+
+/* Read block i into dst (host memory of dst_bytes >= the block's size; pinned
+ * memory serves a later DMA directly) and verify its checksum: WOQ_EFORMAT on
+ * a mismatch or a truncated file (dst then holds what was read). */
+int woq_pool_read_block(const char* path, int32_t i, void* dst, int64_t dst_bytes);
 
 /* ------------------------------------------------------------ measurement */
 

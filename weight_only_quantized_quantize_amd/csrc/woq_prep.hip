@@ -218,11 +218,12 @@ int woq_quantize_int8_dev(const float* W, int64_t N, int64_t K, uint8_t* dev, fl
 int woq_quantize_int4o_dev(const float* W, int64_t N, const int32_t* perm, const woq_int4o_geom* g,
                            uint8_t* dev_codes, uint16_t* dev_scales, uint16_t* dev_wout, int32_t* status,
                            void* stream) {
-    if (!woq::int4o_geom_valid(g) || N < 1 || !W || !perm || !dev_codes || !dev_scales || !status ||
-        (g->n_out8 > 0 && !dev_wout))
-        return WOQ_EINVAL;
-    if (((uintptr_t)W & 3u) || ((uintptr_t)perm & 3u) || !woq::aligned16(dev_codes) || !woq::aligned16(dev_scales) ||
-        (dev_wout && !woq::aligned16(dev_wout)) || ((uintptr_t)status & 3u))
+    if (!woq::int4o_geom_valid(g) || N < 1 || !W || !perm || !status) return WOQ_EINVAL;
+    // with every channel an outlier there is no background (no codes, no scales)
+    if ((g->G4 > 0 && (!dev_codes || !dev_scales)) || (g->n_out8 > 0 && !dev_wout)) return WOQ_EINVAL;
+    if (((uintptr_t)W & 3u) || ((uintptr_t)perm & 3u) || (dev_codes && !woq::aligned16(dev_codes)) ||
+        (dev_scales && !woq::aligned16(dev_scales)) || (dev_wout && !woq::aligned16(dev_wout)) ||
+        ((uintptr_t)status & 3u))
         return WOQ_EALIGN;
     const int64_t N16 = woq::round_up(N, 16);
     if (N16 * g->G4 > INT32_MAX || N > ((int64_t)1 << 40) / g->K || N16 > INT32_MAX) return WOQ_EUNSUPPORTED;
@@ -239,7 +240,7 @@ int woq_quantize_int4o_dev(const float* W, int64_t N, const int32_t* perm, const
     a.K_bg = (int)g->K_bg;
     a.G4 = (int)g->G4;
     a.N16 = (int)N16;
-    hipLaunchKernelGGL(quantize_int4o_kernel, dim3((unsigned)(N16 * g->G4)), dim3(64), 0, s, a);
+    if (g->G4 > 0) hipLaunchKernelGGL(quantize_int4o_kernel, dim3((unsigned)(N16 * g->G4)), dim3(64), 0, s, a);
     if (g->n_out8 > 0) {
         const int64_t total = N16 * g->n_out8;
         hipLaunchKernelGGL(outliers_int4o_kernel, dim3((unsigned)woq::ceil_div(total, 256)), dim3(256), 0, s, W, perm,

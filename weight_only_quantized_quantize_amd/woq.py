@@ -19,6 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwoq.so")
 
 WOQ_OK, WOQ_EINVAL, WOQ_EALIGN, WOQ_ENOMEM, WOQ_EHIP, WOQ_EUNSUPPORTED, WOQ_ERANGE, WOQ_ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
+WOQ_EIO, WOQ_EFORMAT = -8, -9
 MAX_SEGMENTS = 8
 
 
@@ -100,6 +101,10 @@ _SIGS = {
     "woq_quantize_int8_dev": (c_int, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
     "woq_quantize_int4o_dev": (c_int, [c_void_p, c_int64, c_void_p, POINTER(Int4oGeom), c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p]),
+    "woq_pool_save": (c_int, [ctypes.c_char_p, c_void_p, c_int64, POINTER(c_void_p), POINTER(c_int64), c_int32]),
+    "woq_pool_info": (c_int, [ctypes.c_char_p, POINTER(c_int32), POINTER(c_int64), POINTER(c_int64), c_int32,
+                              c_void_p, c_int64]),
+    "woq_pool_read_block": (c_int, [ctypes.c_char_p, c_int32, c_void_p, c_int64]),
     "woq_plan_tiers": (c_int, [c_void_p, c_int32, c_int64, c_void_p, POINTER(c_int64)]),
     "woq_tiered_create": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int64), c_int32, POINTER(StackStep),
                                   c_int32, c_int64, POINTER(c_void_p)]),
@@ -297,8 +302,10 @@ def woq_quantize_int4o_dev(W, perm_dev, g: Int4oGeom, codes, scales, w_out, stat
     """Outlier-aware INT4 encoding of the device tensor W (fp32 [N, K]) into the
     device layout arrays (torch tensors sized by woq_int4o_dev_sizes)."""
     N = W.shape[0]
-    _check(_lib().woq_quantize_int4o_dev(_ptr(W), N, _ptr(perm_dev), ctypes.byref(g), _ptr(codes), _ptr(scales),
-                                         _ptr(w_out) if w_out is not None else None, _ptr(status),
+    def opt(t):
+        return _ptr(t) if t is not None and t.numel() else None
+    _check(_lib().woq_quantize_int4o_dev(_ptr(W), N, _ptr(perm_dev), ctypes.byref(g), opt(codes), opt(scales),
+                                         opt(w_out), _ptr(status),
                                          _stream(stream)), "woq_quantize_int4o_dev")
 
 
@@ -484,6 +491,36 @@ def step_int8(dev: "DeviceInt8", in_slot: int, out_slot: int) -> StackStep:
 
 
 # ------------------------------------------------------------ streamed pager
+
+def woq_pool_save(path: str, meta: bytes, blocks):
+    """Write a pool file: ``meta`` bytes and ``blocks`` (NumPy uint8 arrays or
+    CPU tensors, contiguous)."""
+    n = len(blocks)
+    ptrs = (c_void_p * max(1, n))(*[_ptr(b) for b in blocks])
+    sizes = (c_int64 * max(1, n))(*[int(b.nbytes if isinstance(b, np.ndarray) else b.numel() * b.element_size())
+                                   for b in blocks])
+    mbuf = ctypes.create_string_buffer(meta, len(meta)) if meta else None
+    _check(_lib().woq_pool_save(os.fsencode(path), mbuf, len(meta), ptrs, sizes, n), "woq_pool_save")
+
+
+def woq_pool_info(path: str):
+    """(meta bytes, [block sizes]) of a pool file."""
+    nb, mb = c_int32(), c_int64()
+    _check(_lib().woq_pool_info(os.fsencode(path), ctypes.byref(nb), ctypes.byref(mb), None, 0, None, 0),
+           "woq_pool_info")
+    sizes = (c_int64 * max(1, nb.value))()
+    meta = ctypes.create_string_buffer(max(1, mb.value))
+    _check(_lib().woq_pool_info(os.fsencode(path), ctypes.byref(nb), ctypes.byref(mb), sizes, nb.value, meta,
+                                mb.value), "woq_pool_info")
+    return meta.raw[:mb.value], [sizes[i] for i in range(nb.value)]
+
+
+def woq_pool_read_block(path: str, i: int, dst):
+    """Read block i into dst (NumPy uint8 array or contiguous CPU tensor) and verify it."""
+    n = dst.nbytes if isinstance(dst, np.ndarray) else dst.numel() * dst.element_size()
+    _check(_lib().woq_pool_read_block(os.fsencode(path), i, _ptr(dst), n), "woq_pool_read_block")
+    return dst
+
 
 def woq_plan_tiers(layer_bytes, budget_bytes: int):
     """(resident flags int32 [L], device bytes) of the tier plan under a budget."""
