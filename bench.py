@@ -211,6 +211,9 @@ def main():
     ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
                     help="fused: one persistent launch per step; launch: one launch per permutation and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pool-roundtrip", action="store_true",
+                    help="stacks 2-4: encode every layer, save the pool file under $TMPDIR, load it back, run a "
+                         "pass (checked against the in-memory stack) and report the times")
     ap.add_argument("--prep", action="store_true",
                     help="stacks 2-4: time the encoders (device and host) on the linears of one layer")
     ap.add_argument("--hbm-budget", type=float, default=None,
@@ -241,10 +244,12 @@ def main():
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
     if args.config == 5:
         return bench_streamed(args, spec, b, log)
-    if args.hbm_budget is not None:
-        return bench_tiered(args, spec, b, log)
     if args.prep:
         return bench_prep(args, spec, log)
+    if args.pool_roundtrip:
+        return bench_pool(args, spec, b, log)
+    if args.hbm_budget is not None:
+        return bench_tiered(args, spec, b, log)
     t0 = time.perf_counter()
     rs = ResidentStack(spec, lambda layer, lin, out: synth.weight(spec, layer, lin, out=out),
                        lambda space: synth.profile(spec, space), layers=args.layers, log=log)
@@ -404,6 +409,65 @@ def bench_vocab(args, spec, rs, b, run, stream, log):
             "lm_head_launches": 2,
             "ms_per_step_with_vocab": round(full_ms, 5),
             "decode_tok_s_with_vocab": round(b / (full_ms * 1e-3), 2)}
+
+
+def bench_pool(args, spec, b, log):
+    """Persisted pool: encode (host, all threads) into a pinned pool, save the
+    file, load it into a fresh stack (every layer read into pinned memory, or
+    through it into device memory for the layers a budget keeps resident) and
+    run one pass; the loaded stack's outputs must equal the original's bit for
+    bit.  The file is deleted afterwards."""
+    import tempfile
+
+    import torch
+    import synth
+    from weight_only_quantized_quantize_amd.stack import GROUPS, PooledStack, TieredStack
+
+    L = args.layers or spec.layers
+    t0 = time.perf_counter()
+    ts = TieredStack(spec, lambda layer, lin, out: synth.weight(spec, layer, lin, out=out),
+                     lambda space: synth.profile(spec, space), 0, layers=L, resident=[0] * L, log=log)
+    encode_s = time.perf_counter() - t0
+    fd, path = tempfile.mkstemp(suffix=".woqpool")
+    os.close(fd)
+    try:
+        t0 = time.perf_counter()
+        ts.save_pool(path)
+        save_s = time.perf_counter() - t0
+        file_bytes = os.path.getsize(path)
+        inputs, outs_a, outs_b = [], [], []
+        for layer in range(L):
+            for names, inp in GROUPS:
+                inputs.append(torch.from_numpy(synth.decode_input(spec, layer, inp, b)).cuda())
+                N = sum(spec.linear(n).N for n in names)
+                outs_a.append(torch.empty(b, N, dtype=torch.float16, device="cuda"))
+                outs_b.append(torch.empty(b, N, dtype=torch.float16, device="cuda"))
+        compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+        pa = ts.make_pager(b)
+        pa.bind(inputs, outs_a)
+        pa.run(b, compute, copy)
+        torch.cuda.synchronize()
+        pa.close()
+        del ts, pa
+        budget = int(args.hbm_budget * 1e9) if args.hbm_budget is not None else None
+        t0 = time.perf_counter()
+        ps = PooledStack(path, budget_bytes=budget, resident=None if budget is not None else [1] * L)
+        load_s = time.perf_counter() - t0
+        pb = ps.make_pager(b)
+        pb.bind(inputs, outs_b)
+        pb.run(b, compute, copy)
+        torch.cuda.synchronize()
+        pb.close()
+        same = all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(outs_a, outs_b))
+    finally:
+        os.remove(path)
+    print(json.dumps({
+        "workload": f"{spec.name}" + (f", {L} layers" if L != spec.layers else "") + ": persisted pool round trip",
+        "format": spec.fmt, "layers": L, "file_bytes": file_bytes, "encode_s": round(encode_s, 2),
+        "save_s": round(save_s, 2), "save_gbs": round(file_bytes / save_s / 1e9, 2),
+        "load_s": round(load_s, 2), "load_gbs": round(file_bytes / load_s / 1e9, 2),
+        "loaded_resident_layers": ps.n_resident, "outputs_equal_after_load": bool(same),
+        "note": "load right after save reads from the page cache"}), flush=True)
 
 
 def bench_prep(args, spec, log):

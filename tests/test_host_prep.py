@@ -394,6 +394,48 @@ def test_plan_tiers_equal_layers_closed_form():
     assert e.value.status == woq.WOQ_EINVAL
 
 
+# ------------------------------------------------------- persisted pool
+
+def test_pool_roundtrip_and_damage(tmp_path):
+    """Blocks and metadata come back byte for byte; a flipped byte in a block,
+    in the table or in the magic, and a truncated file, are reported."""
+    rng = np.random.default_rng(8)
+    blocks = [rng.integers(0, 256, n, dtype=np.uint8) for n in (0, 1, 4095, 4096, (1 << 20) + 13, 3 << 20)]
+    meta = b'{"hello": "pool"}'
+    path = str(tmp_path / "p.woqpool")
+    woq.woq_pool_save(path, meta, blocks)
+    m, sizes = woq.woq_pool_info(path)
+    assert m == meta and sizes == [b.size for b in blocks]
+    for i, b in enumerate(blocks):
+        dst = np.full(b.size + 7, 0xEE, np.uint8)
+        woq.woq_pool_read_block(path, i, dst)
+        np.testing.assert_array_equal(dst[:b.size], b)
+        assert np.all(dst[b.size:] == 0xEE)
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_pool_read_block(path, 4, np.empty(10, np.uint8))        # too small
+    assert e.value.status == woq.WOQ_EINVAL
+    raw = bytearray(open(path, "rb").read())
+    assert len(raw) % 4096 == 0
+
+    def damaged(mutate, block=4):
+        bad = bytearray(raw)
+        mutate(bad)
+        p2 = str(tmp_path / "bad.woqpool")
+        open(p2, "wb").write(bytes(bad))
+        with pytest.raises(woq.WoqError) as e:
+            woq.woq_pool_read_block(p2, block, np.empty(sizes[block], np.uint8))
+        return e.value.status
+
+    off4 = int(np.frombuffer(bytes(raw[32 + 24 * 4: 32 + 24 * 4 + 8]), np.uint64)[0])
+    assert damaged(lambda b: b.__setitem__(off4 + 12345, b[off4 + 12345] ^ 1)) == woq.WOQ_EFORMAT
+    assert damaged(lambda b: b.__setitem__(40, b[40] ^ 1)) == woq.WOQ_EFORMAT      # table
+    assert damaged(lambda b: b.__setitem__(0, ord("X"))) == woq.WOQ_EFORMAT      # magic
+    assert damaged(lambda b: b.__delitem__(slice(off4 + 100, None))) == woq.WOQ_EFORMAT   # truncated
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_pool_info(str(tmp_path / "missing.woqpool"))
+    assert e.value.status == woq.WOQ_EIO
+
+
 # ------------------------------------------------- permutation positions
 
 @pytest.mark.parametrize("K", [8, 130, 1000, 3072])

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwoq.so")
 ARCH = os.environ.get("WOQ_OFFLOAD_ARCH", "gfx950")
 
-HOST_SOURCES = ["woq_host.cpp"]
+HOST_SOURCES = ["woq_host.cpp", "woq_pool.cpp"]
 DEVICE_SOURCES = ["woq_device.hip", "woq_runtime.hip", "woq_pager.cpp", "woq_prep.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]

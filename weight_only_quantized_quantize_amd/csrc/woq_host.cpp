@@ -109,6 +109,9 @@ const char* woq_strerror(int status) {
         case WOQ_EHIP: return "HIP runtime error";
         case WOQ_EUNSUPPORTED: return "unsupported request";
         case WOQ_ERANGE: return "value out of range (non-finite weight or fp16 scale overflow)";
+        case WOQ_ETIMEOUT: return "timed out waiting at a step boundary";
+        case WOQ_EIO: return "file input/output error";
+        case WOQ_EFORMAT: return "not a pool file, or a damaged one";
         default: return "unknown status";
     }
 }

@@ -8,6 +8,7 @@ gate|up (hidden input), down (intermediate input).
 """
 from __future__ import annotations
 
+import json
 import os
 import threading
 from concurrent.futures import ThreadPoolExecutor
@@ -247,6 +248,121 @@ class TieredStack(_QuantisedStack):
                         end += qi.shape[0]
                         st.w8.seg_end[i] = end
                         st.w8.seg_scale[i] = float(sc)
+                self.step_list.append(st)
+
+    @property
+    def n_resident(self) -> int:
+        return int(self.resident.sum())
+
+    def streamed_bytes(self) -> int:
+        return sum(self.layer_bytes)
+
+    def make_pager(self, max_b: int):
+        return woq.Pager(self.pool, self.layer_off, self.layer_bytes, self.step_list, len(GROUPS), max_b)
+
+    def save_pool(self, path: str):
+        """Persist the encoded stack: every layer's block plus the global
+        permutations, with what a loader needs to rebuild the steps.  Every
+        layer must be streamed (built with resident all 0), so that its block
+        is in the host pool."""
+        if self.n_resident:
+            raise ValueError("save_pool needs every layer in the host pool (resident all 0)")
+        spec = self.spec
+        groups = []
+        for gi, (names, inp) in enumerate(GROUPS):
+            lin = spec.linear(names[0])
+            groups.append({"names": list(names), "input": inp, "K": lin.K, "space": lin.space,
+                           "N": sum(spec.linear(n).N for n in names), "offsets": self.array_offsets[gi]})
+        int8 = []
+        if self.fmt == "int8":
+            for layer in range(self.n_layers):
+                row = []
+                for gi in range(len(GROUPS)):
+                    w = self.step_list[4 * layer + gi].w8
+                    row.append({"seg_end": [w.seg_end[i] for i in range(w.nseg)],
+                                "seg_scale_bits": [int(np.float32(w.seg_scale[i]).view(np.uint32))
+                                                   for i in range(w.nseg)]})
+                int8.append(row)
+        spaces, perm_parts, o = {}, [], 0
+        for sp in sorted(self.perm_host):
+            p = np.ascontiguousarray(self.perm_host[sp], np.int32)
+            spaces[sp] = [o, int(p.size), int(self.geom[sp].n_out)]
+            perm_parts.append(p)
+            o += p.size
+        perms = np.concatenate(perm_parts).view(np.uint8) if perm_parts else np.zeros(0, np.uint8)
+        meta = {"kind": "woq stack pool", "fmt": self.fmt, "workload": spec.name, "n_layers": self.n_layers,
+                "steps_per_layer": len(GROUPS), "block_bytes": self.block_bytes, "groups": groups,
+                "int8_segments": int8, "perm_spaces": spaces}
+        pool = self.pool.numpy()
+        blocks = [pool[self.layer_off[l]: self.layer_off[l] + self.block_bytes] for l in range(self.n_layers)]
+        woq.woq_pool_save(path, json.dumps(meta).encode(), blocks + [perms])
+
+
+class PooledStack:
+    """A stack loaded from a pool file written by TieredStack.save_pool: no
+    weight is encoded again.  The tier plan is made at load time (budget, or an
+    explicit resident list): resident layers are read through one pinned
+    staging block into device memory, streamed layers straight into the
+    pinned pool the pager copies from."""
+
+    def __init__(self, path: str, budget_bytes: int | None = None, resident=None, device="cuda"):
+        import torch
+        raw, sizes = woq.woq_pool_info(path)
+        meta = json.loads(raw.decode())
+        if meta.get("kind") != "woq stack pool":
+            raise ValueError("not a stack pool")
+        self.meta = meta
+        self.fmt = meta["fmt"]
+        L, B = meta["n_layers"], meta["block_bytes"]
+        self.n_layers, self.block_bytes = L, B
+        perms = np.empty(sizes[L], np.uint8)
+        woq.woq_pool_read_block(path, L, perms)
+        perms = perms.view(np.int32)
+        self.perm_host, self.perm_dev, self.geom = {}, {}, {}
+        for sp, (o, K, n_out) in meta["perm_spaces"].items():
+            self.perm_host[sp] = perms[o:o + K].copy()
+            self.perm_dev[sp] = torch.from_numpy(self.perm_host[sp]).to(device)
+            self.geom[sp] = woq.woq_int4o_geometry(K, n_out)
+        if resident is None:
+            resident, self.planned_device_bytes = woq.woq_plan_tiers([B] * L, budget_bytes)
+        self.resident = np.asarray(resident, np.int32)
+        streamed = [l for l in range(L) if not self.resident[l]]
+        self.pool = torch.empty(max(1, len(streamed) * B), dtype=torch.uint8, pin_memory=True)
+        pool_np = self.pool.numpy()
+        self.layer_off, self.layer_bytes = [0] * L, [0] * L
+        self.device_blocks = {}
+        staging = torch.empty(B, dtype=torch.uint8, pin_memory=True) if len(streamed) < L else None
+        for l in range(L):
+            if self.resident[l]:
+                woq.woq_pool_read_block(path, l, staging.numpy())
+                d = torch.empty(B, dtype=torch.uint8, device=device)
+                d.copy_(staging)                       # synchronous: the staging block is reused
+                self.device_blocks[l] = d
+            else:
+                j = streamed.index(l)
+                self.layer_off[l], self.layer_bytes[l] = j * B, B
+                woq.woq_pool_read_block(path, l, pool_np[j * B:(j + 1) * B])
+        self.step_list = []
+        for l in range(L):
+            base = self.device_blocks[l].data_ptr() if self.resident[l] else 0
+            for gi, gr in enumerate(meta["groups"]):
+                st = woq.StackStep()
+                st.in_slot = st.out_slot = 4 * l + gi
+                offs = gr["offsets"]
+                if self.fmt == "int4o":
+                    st.fmt = woq.FMT_INT4O
+                    st.w4.codes, st.w4.scales, st.w4.w_out = (base + o for o in offs)
+                    st.w4.N = gr["N"]
+                    st.w4.geom = self.geom[gr["space"]]
+                    st.perm = self.perm_dev[gr["space"]].data_ptr()
+                else:
+                    seg = meta["int8_segments"][l][gi]
+                    st.fmt = woq.FMT_INT8
+                    st.w8.codes = base + offs[0]
+                    st.w8.N, st.w8.K, st.w8.nseg = gr["N"], gr["K"], len(seg["seg_end"])
+                    for i, (e, sb) in enumerate(zip(seg["seg_end"], seg["seg_scale_bits"])):
+                        st.w8.seg_end[i] = e
+                        st.w8.seg_scale[i] = float(np.uint32(sb).view(np.float32))
                 self.step_list.append(st)
 
     @property
