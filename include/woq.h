@@ -54,7 +54,7 @@ extern "C" {
 #define WOQ_EALIGN       (-2)  /* pointer or leading dimension not aligned as required */
 #define WOQ_ENOMEM       (-3)  /* host or device allocation failed (runtime objects only) */
 #define WOQ_EHIP         (-4)  /* a HIP call failed; woq_last_hip_error() gives its code */
-#define WOQ_EUNSUPPORTED (-5)  /* valid request that this build does not implement */
+#define WOQ_EUNSUPPORTED (-5)  /* valid request that the library does not implement */
 #define WOQ_ERANGE       (-6)  /* value not representable: non-finite weight, fp16 scale overflow */
 #define WOQ_ETIMEOUT     (-7)  /* a fused stack run gave up waiting at a step boundary */
 #define WOQ_EIO          (-8)  /* a file could not be opened, read or written */
