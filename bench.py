@@ -305,7 +305,10 @@ def main():
         # product kernels: a second pass of K steps with HIP events around each product launch
         step_ms, _ = runner.time(b, args.steps, stream)
         kern_ms = sum(step_ms)
-        kname = ("qgemv_int4o_tile" if b <= 4 else "qgemm_int4o_mfma") if spec.fmt == "int4o" else "qgemv_int8_valu"
+        if spec.fmt == "int4o":
+            kname = "qgemv_int4o_tile" if b <= 4 else "qgemm_int4o_mfma"
+        else:
+            kname = "qgemv_int8_valu" if b < 5 else "qgemv_int8_valu + qgemm_int8_mfma (N >= 16384, or 8192 at b >= 7)"
         launches_per_step = len(shapes)
         kernel_bytes = step_bytes
     ms_per_step = wall * 1e3 / args.steps
@@ -368,8 +371,7 @@ def bench_vocab(args, spec, rs, b, run, stream, log):
         f"{tv.device_bytes() / 1e9:.3f} GB resident")
     ids = torch.from_numpy(synth.token_ids(spec, b)).cuda()
     emb = torch.empty(b, H, dtype=torch.float16, device="cuda")
-    h = torch.from_numpy(synth.decode_input(spec, spec.layers, 0, b) if b <= spec.bmax else
-                         np.tile(synth.decode_input(spec, spec.layers, 0), (-(-b // spec.bmax), 1))[:b]).cuda()
+    h = torch.from_numpy(synth.decode_input(spec, spec.layers, 0, b)).cuda()   # the hidden state after the stack
     logits = torch.empty(b, V, dtype=torch.float16, device="cuda")
 
     def timed(fn, n):

@@ -257,6 +257,8 @@ int woq_permute_x(const uint16_t* x, int64_t ldx, const int32_t* perm, int64_t b
  * in registers (the reconstruction step of "Open Origin - ELG Stream Layer",
  * fused into the product).  x fp16 [b, ldx], 16-byte aligned, ldx a multiple
  * of 8 and >= K; y fp16 [b, ldy], ldy >= N.  1 <= b <= 8 (b = 0 is a no-op).
+ * The vector-ALU kernel runs, except for N >= 16384 at b >= 5 and N >= 8192
+ * at b >= 7, where a matrix-core kernel runs (the faster one on MI355X).
  */
 int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t b,
                    uint16_t* y, int64_t ldy, void* stream);
@@ -301,8 +303,10 @@ int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_
 int woq_perm_positions(const int32_t* perm, const woq_int4o_geom* g, uint16_t* pos);
 
 /*
- * woq_permute_x and woq_qgemv_int4o in one launch, with the same result bit
- * for bit: x is read in its natural channel order (fp16 [b, ldx], 16-byte
+ * woq_permute_x and woq_qgemv_int4o in one launch - the same result bit for
+ * bit wherever woq_qgemv_int4o runs its vector kernel (b <= 2, or b <= 4 when
+ * N < 6144), the same values up to summation order where it runs the
+ * matrix-core kernel: x is read in its natural channel order (fp16 [b, ldx], 16-byte
  * aligned, ldx a multiple of 8 and >= K) and scattered through pos (device
  * copy of woq_perm_positions, 16-byte aligned) into the permuted, split row,
  * held in on-chip memory while the weights stream; this is the vector-ALU

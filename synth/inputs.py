@@ -193,7 +193,9 @@ def decode_input(spec: StackSpec, layer: int, idx: int, b: int | None = None) ->
     """fp16 [b, K] decode activation number ``idx`` (0..3) of a layer."""
     _, space, _ = INPUTS[idx]
     K = spec.space_width(space)
-    z = _rng(spec.cfg_id, layer, 10 + idx).standard_normal((spec.bmax, K), dtype=np.float32)
+    # rows are drawn in order, so a smaller batch is a prefix of a larger one
+    rows = spec.bmax if b is None else max(b, spec.bmax)
+    z = _rng(spec.cfg_id, layer, 10 + idx).standard_normal((rows, K), dtype=np.float32)
     if spec.planted:
         z[:, planted_set(spec, space)] *= np.float32(spec.x_planted_gain)
     x = z.astype(np.float16)

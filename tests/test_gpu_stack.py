@@ -3,7 +3,8 @@ persistent pass of INT8 stacks).
 
 The runner's launches are the public entry points, so its outputs must equal
 those entry points composed by hand bit for bit; the fused INT8 pass uses the
-same per-quad arithmetic and must agree bit for bit too.  Everything is also
+vector kernel's per-quad arithmetic and must agree bit for bit where the
+launches run the vector kernel too (b <= 2), within tolerance above.  Everything is also
 checked against the oracle, whose weights and permutations are computed by the
 oracle itself from the same seeded inputs.
 """
@@ -96,7 +97,12 @@ def test_small_stack_runner_equals_entry_points_and_oracle(gpu_lib, cfg, b):
             runner.run_fused(b)
         runner.check()
         for i, (a, t) in enumerate(zip(ref_launch, outs)):
-            np.testing.assert_array_equal(a.view(np.uint16), host(t).view(np.uint16), err_msg=f"fused step {i}")
+            if b < 3:
+                # both run the vector kernel's arithmetic: identical bits
+                np.testing.assert_array_equal(a.view(np.uint16), host(t).view(np.uint16), err_msg=f"fused step {i}")
+            else:
+                # the per-launch pass runs the matrix-core product from b = 3: summation order differs
+                assert O.normwise_rel_err(host(t).astype(np.float64), a.astype(np.float64)) <= TOL, f"fused step {i}"
     else:
         with pytest.raises(woq.WoqError) as e:   # the persistent pass streams INT8 only
             runner.run_fused(b)

@@ -394,6 +394,27 @@ def test_plan_tiers_equal_layers_closed_form():
     assert e.value.status == woq.WOQ_EINVAL
 
 
+def test_binding_refuses_batches_larger_than_buffers():
+    """The C ABI takes plain pointers; the binding checks row counts first."""
+    x = np.zeros((4, 64), np.float16)
+    y = np.zeros((8, 16), np.float16)
+    woq.need_rows(4, x, y)
+    with pytest.raises(ValueError):
+        woq.need_rows(8, x, y)
+    with pytest.raises(ValueError):
+        woq.woq_qgemv_int8(woq.Int8W(), x, y, b=8)
+
+
+def test_decode_input_rows_for_any_batch():
+    """Inputs have exactly b rows, also above the workload's largest batch,
+    and a smaller batch is a prefix of a larger one."""
+    spec = synth.stack_spec(3)
+    x8 = synth.decode_input(spec, 1, 2, 8)
+    assert x8.shape == (8, spec.space_width("h"))        # input 2 (gate|up) reads the hidden space
+    np.testing.assert_array_equal(synth.decode_input(spec, 1, 2, 4), x8[:4])
+    np.testing.assert_array_equal(synth.decode_input(spec, 1, 2), x8[:spec.bmax])
+
+
 # ------------------------------------------------------- persisted pool
 
 def test_pool_roundtrip_and_damage(tmp_path):

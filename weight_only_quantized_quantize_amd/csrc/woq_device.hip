@@ -364,6 +364,19 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
 
 // --------------------------------------------------------- INT8, batch <= 8
 
+// Which INT8 kernel serves a product of N rows at batch b (measured on
+// MI355X over the 9B-shaped products): the vector kernel streams the
+// row-major codes at up to 5 TB/s but re-reads each activation chunk from L1
+// for every four rows and spends 2 dot2 per 4 weights per batch row, so its
+// time grows with b; the matrix-core kernel's time does not grow with b but
+// its wave loads cover 16 rows x 64 bytes, which streams slower.  The matrix
+// cores win on wide products from b = 5 (57344-row-class: 30 vs 62 us at
+// b = 8) and on mid-size ones from b = 7; narrow ones stay on the vector ALU.
+inline bool int8_use_mfma(int64_t N, int64_t b) {
+    const int64_t tiles = (N + 15) / 16;
+    return (tiles >= 1024 && b >= 5) || (tiles >= 512 && b >= 7);
+}
+
 struct Int8Args {
     const uint4* codes;     // [N4][Kd/16] chunks of 16 bytes
     const uint16_t* x;      // [b][ldx]
@@ -425,6 +438,169 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
     }
 }
 
+// ------------------------------------------------ INT8, matrix cores (b >= 3)
+
+// A workgroup of T x S waves owns T tiles of 16 output rows of the row-major
+// INT8 layout; the S waves of a tile split the 64-channel groups of every K
+// chunk (CH groups) between them.  Lane l loads the 16-byte piece l >> 4 of
+// group g of row l & 15 (channels 64g + 16(l >> 4) .. + 15); its first and
+// last 8 codes are the A operands of two v_mfma_f32_16x16x32_f16 steps whose
+// k slots 8(l >> 4) .. + 7 stand for those channels, and the B operands (batch
+// column l & 15) read the same channels from the activations staged in LDS.
+// The per-tensor (per-segment) scale multiplies the fp32 sum once, at the end.
+// Activations are staged per K chunk (all b columns) once for the T tiles, two
+// chunks ahead of use through registers, as in the INT4O matrix-core kernel.
+template <int T, int S>
+__global__ __launch_bounds__(64 * T * S) void qgemm_int8_mfma(Int8Args a, int b) {
+    constexpr int W = T * S;
+    constexpr int CH = S > 8 ? S : 8;                 // 64-channel groups per chunk
+    constexpr int KC = CH / S;                        // groups per wave per chunk
+    constexpr int P = 8;                              // weight window (groups)
+    static_assert(P % KC == 0, "window must hold whole chunks");
+    constexpr int UNR = P / KC < 2 ? 2 : P / KC;
+    static_assert(UNR % 2 == 0 && UNR % (P / KC) == 0, "unroll");
+    constexpr int COLS = 16;                          // batch columns of the B operand
+    constexpr int XS = CH * 64 + 8;                   // LDS column stride (fp16), padded against bank conflicts
+    constexpr int PPC = CH * 8;                       // 16-byte pieces of one column per chunk
+    constexpr int NPT = (COLS * PPC + 64 * W - 1) / (64 * W);
+    constexpr int RED = 4 * W * 16 * 17;
+    constexpr int XSB = 2 * 2 * COLS * XS;
+    __shared__ __align__(16) uint16_t lds[(XSB > RED ? XSB : RED) / 2];
+    uint16_t (*xs)[COLS][XS] = reinterpret_cast<uint16_t (*)[COLS][XS]>(lds);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int tile = wave / S, s = wave % S;
+    const int m = lane & 15;
+    const int c = lane >> 4;
+    const int tiles = (a.N + 15) >> 4;
+    const int t16 = blockIdx.x * T + tile;
+    const bool tile_ok = t16 < tiles;
+    const int n4 = (a.N + 3) & ~3;                    // rows of the layout
+    const int row = tile_ok && t16 * 16 + m < n4 ? t16 * 16 + m : 0;
+    const int G = a.CPR / 4;                          // 64-channel groups per row (Kd / 64)
+    const int nchunks = (G + CH - 1) / CH;
+
+    f4 acc = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int e = tid; e < 2 * COLS * XS; e += 64 * W) {
+        const int col = (e / XS) % COLS;
+        if (col >= b) lds[e] = 0;
+    }
+
+    // staging: piece p of chunk k -> column p / PPC, channels 8 (p % PPC) of the chunk
+    uint4 stg[2][NPT];
+    auto stage_load = [&](uint4 (&r)[NPT], int k) {
+        const int kk = k < nchunks ? k : 0;
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int p = tid + i * 64 * W;
+            const int col = p / PPC, ch = kk * CH * 64 + 8 * (p % PPC);
+            const bool ok = col < b && ch < a.K;
+            uint4 v = load_x16((gx_ptr)(a.x + (ok ? (int64_t)col * a.ldx + ch : 0)));
+            if (ok && ch + 8 > a.K) {                 // the last piece of a row that ends inside it
+                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (ch + 2 * j >= a.K) w[j] = 0;
+                    else if (ch + 2 * j + 1 >= a.K) w[j] &= 0xFFFFu;
+                }
+                v = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+            r[i] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto stage_store = [&](const uint4 (&r)[NPT], int buf) {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int p = tid + i * 64 * W;
+            const int col = p / PPC, off = p % PPC;
+            if (col < b)
+                *(__attribute__((address_space(3))) u32x4*)&xs[buf][col][8 * off] =
+                    (u32x4){r[i].x, r[i].y, r[i].z, r[i].w};
+        }
+    };
+
+    // this wave's groups: in chunk k, k*CH + s*KC + kk (kk < KC); j counts them
+    const int full = G / CH, rem = G - full * CH;
+    const int J = full * KC + min(max(rem - s * KC, 0), KC);
+    auto group_of = [&](int j) { return (j / KC) * CH + s * KC + (j % KC); };
+    const uint4* wld = a.codes + (int64_t)row * a.CPR + c;
+
+    uint4 wq[P];
+    if (nchunks > 0) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) wq[u] = gload_nt(wld + 4 * (u < J ? group_of(u) : 0));
+        stage_load(stg[0], 0);
+        stage_load(stg[1], 1);
+        stage_store(stg[0], 0);
+    }
+    __syncthreads();
+    for (int k0 = 0; k0 < nchunks; k0 += UNR) {
+#pragma unroll
+        for (int cb = 0; cb < UNR; ++cb) {
+            const int k = k0 + cb;
+            if (k < nchunks) {
+                stage_load(stg[cb & 1], k + 2);
+#pragma unroll
+                for (int kk = 0; kk < KC; ++kk) {
+                    const int u = (cb * KC + kk) % P;
+                    const int j = k * KC + kk;
+                    const bool gv = k * CH + s * KC + kk < G;
+                    const uint4 w = wq[u];
+                    wq[u] = gload_nt(wld + 4 * (j + P < J ? group_of(j + P) : 0));
+                    h2 p0, p1, p2, p3, p4, p5, p6, p7;
+                    int8_pairs(w.x, p0, p1);
+                    int8_pairs(w.y, p2, p3);
+                    int8_pairs(w.z, p4, p5);
+                    int8_pairs(w.w, p6, p7);
+                    const h8 A0 = (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                    const h8 A1 = (h8){p4[0], p4[1], p5[0], p5[1], p6[0], p6[1], p7[0], p7[1]};
+                    const int gl = s * KC + kk;
+                    const lx_ptr xb = (lx_ptr)&xs[cb & 1][m][64 * gl + 16 * c];
+                    const h8 B0 = __builtin_bit_cast(h8, load_x16(xb));
+                    const h8 B1 = __builtin_bit_cast(h8, load_x16(xb + 8));
+                    if (gv) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B0, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B1, acc, 0, 0, 0);
+                    }
+                }
+                if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1);
+                lds_barrier();
+            }
+        }
+    }
+
+    // lane (c, m) holds rows 4c .. 4c + 3 of the tile, batch column m
+    if (S > 1) {
+        typedef float RedTile[16][17];
+        RedTile* red = reinterpret_cast<RedTile*>(lds);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][4 * c + i][m] = acc[i];
+        __syncthreads();
+        if (s == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = acc[i];
+                for (int p = 1; p < S; ++p) v += red[wave + p][4 * c + i][m];
+                acc[i] = v;
+            }
+        }
+    }
+    if (s == 0 && tile_ok && m < b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = t16 * 16 + 4 * c + i;
+            if (n < a.N) {
+                float sc = a.seg_scale[a.nseg - 1];
+                for (int q = a.nseg - 1; q >= 0; --q)
+                    if (n < a.seg_end[q]) sc = a.seg_scale[q];
+                *gptr(a.y + (int64_t)m * a.ldy + n) = f_to_h(acc[i] * sc);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------ INT4O, matrix cores (b >= 8)
 
 // A workgroup of T x S waves owns T tiles of 16 output rows; the S waves of a
@@ -445,7 +621,7 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
 // unconditional (clamped to a valid address, results unused), so the number
 // of loads in flight is the same on every path and each wait is exact.
 // Partial sums of the S waves of a tile meet in LDS.
-template <int NBT, int T, int S>
+template <int NBT, int T, int S, int RB>
 __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int b) {
     constexpr int W = T * S;
     // groups per chunk: with the K split, chunks of 8 groups halve the
@@ -462,7 +638,7 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     constexpr int XS = CH * 128 + 8;                  // LDS column stride (fp16), padded against bank conflicts
     constexpr int PPC = CH * 16;                      // 16-byte pieces of one column per chunk
     constexpr int NPT = (COLS * PPC + 64 * W - 1) / (64 * W);   // staged pieces per thread (b = COLS)
-    constexpr int RED = 4 * W * NBT * 16 * 17;
+    constexpr int RED = 4 * W * RB * NBT * 16 * 17;
     constexpr int XSB = 2 * 2 * COLS * XS;
     __shared__ __align__(16) uint16_t lds[(XSB > RED ? XSB : RED) / 2];
     uint16_t (*xs)[COLS][XS] = reinterpret_cast<uint16_t (*)[COLS][XS]>(lds);
@@ -473,17 +649,25 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     const int m = lane & 15;           // row within the tile (A) / batch column (B)
     const int c = lane >> 4;           // 32-channel chunk of the group / k-block
     const int tiles = (a.N + 15) >> 4;
-    const int t16 = blockIdx.x * T + tile;
-    const bool tile_ok = t16 < tiles;
-    const int tb = tile_ok ? t16 : 0;
-    const int trow0 = t16 * 16;
+    // this wave's RB tiles (register blocking: every staged activation read
+    // from LDS feeds RB tiles' matrix-core steps)
+    const int t16 = (blockIdx.x * T + tile) * RB;
+    bool tile_ok[RB];
+    int tb[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        tile_ok[r] = t16 + r < tiles;
+        tb[r] = tile_ok[r] ? t16 + r : 0;
+    }
     const int G4 = a.G4, xp_len = a.xp_len;
     const int nchunks = (G4 + CH - 1) / CH;
     const int bgl = 128 * G4;
 
-    f4 acc[NBT];
+    f4 acc[RB][NBT];
 #pragma unroll
-    for (int t = 0; t < NBT; ++t) acc[t] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) acc[r][t] = (f4){0.f, 0.f, 0.f, 0.f};
 
     // columns b .. COLS-1 of both buffers hold zeros for the whole kernel
     for (int e = tid; e < 2 * COLS * XS; e += 64 * W) {
@@ -522,17 +706,25 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     auto group_of = [&](int j) { return (j / KC) * CH + s * KC + (j % KC); };
     // tile layout: lane (m, c) reads 16 bytes of the tile's 1 KB block of group g,
     // and the scales of D rows 4c .. 4c + 3 (8 contiguous bytes)
-    const uint4* wld = a.codes + (int64_t)tb * G4 * 64 + c * 16 + m;
-    const uint2* sld = reinterpret_cast<const uint2*>(a.scales) + (int64_t)tb * G4 * 4 + c;
+    const uint4* wld[RB];
+    const uint2* sld[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        wld[r] = a.codes + (int64_t)tb[r] * G4 * 64 + c * 16 + m;
+        sld[r] = reinterpret_cast<const uint2*>(a.scales) + (int64_t)tb[r] * G4 * 4 + c;
+    }
 
-    uint4 wq[P];
-    uint2 sc[P];
+    uint4 wq[P][RB];
+    uint2 sc[P][RB];
     if (nchunks > 0) {                 // G4 > 0: group 0 exists
 #pragma unroll
         for (int u = 0; u < P; ++u) {
             const int g = u < J ? group_of(u) : 0;
-            wq[u] = gload_nt(wld + (int64_t)g * 64);
-            sc[u] = gload_u2(sld + g * 4);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                wq[u][r] = gload_nt(wld[r] + (int64_t)g * 64);
+                sc[u][r] = gload_u2(sld[r] + g * 4);
+            }
         }
         stage_load(stg[0], 0);
         stage_load(stg[1], 1);
@@ -552,24 +744,30 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
                     const int j = k * KC + kk;
                     const int g = k * CH + s * KC + kk;
                     const bool gv = g < G4;
-                    const uint32_t wd[4] = {wq[u].x, wq[u].y, wq[u].z, wq[u].w};
-                    const float sf[4] = {h_to_f((uint16_t)(sc[u].x & 0xFFFF)), h_to_f((uint16_t)(sc[u].x >> 16)),
-                                         h_to_f((uint16_t)(sc[u].y & 0xFFFF)), h_to_f((uint16_t)(sc[u].y >> 16))};
                     const int gn = j + P < J ? group_of(j + P) : 0;
-                    wq[u] = gload_nt(wld + (int64_t)gn * 64);
-                    sc[u] = gload_u2(sld + gn * 4);
-                    Int4Pairs pr[4];
+                    h8 A[RB][4];
+                    float sf[RB][4];
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) pr[d] = int4_pairs(wd[d], bias);
-                    h8 A[4];
+                    for (int r = 0; r < RB; ++r) {
+                        const uint32_t wd[4] = {wq[u][r].x, wq[u][r].y, wq[u][r].z, wq[u][r].w};
+                        sf[r][0] = h_to_f((uint16_t)(sc[u][r].x & 0xFFFF));
+                        sf[r][1] = h_to_f((uint16_t)(sc[u][r].x >> 16));
+                        sf[r][2] = h_to_f((uint16_t)(sc[u][r].y & 0xFFFF));
+                        sf[r][3] = h_to_f((uint16_t)(sc[u][r].y >> 16));
+                        wq[u][r] = gload_nt(wld[r] + (int64_t)gn * 64);
+                        sc[u][r] = gload_u2(sld[r] + gn * 4);
+                        Int4Pairs pr[4];
 #pragma unroll
-                    for (int Pp = 0; Pp < 2; ++Pp) {
-                        const Int4Pairs& e0 = pr[2 * Pp];
-                        const Int4Pairs& e1 = pr[2 * Pp + 1];
-                        A[2 * Pp + 0] = (h8){e0.lo0[0], e0.lo0[1], e0.lo1[0], e0.lo1[1],
-                                             e1.lo0[0], e1.lo0[1], e1.lo1[0], e1.lo1[1]};
-                        A[2 * Pp + 1] = (h8){e0.hi0[0], e0.hi0[1], e0.hi1[0], e0.hi1[1],
-                                             e1.hi0[0], e1.hi0[1], e1.hi1[0], e1.hi1[1]};
+                        for (int d = 0; d < 4; ++d) pr[d] = int4_pairs(wd[d], bias);
+#pragma unroll
+                        for (int Pp = 0; Pp < 2; ++Pp) {
+                            const Int4Pairs& e0 = pr[2 * Pp];
+                            const Int4Pairs& e1 = pr[2 * Pp + 1];
+                            A[r][2 * Pp + 0] = (h8){e0.lo0[0], e0.lo0[1], e0.lo1[0], e0.lo1[1],
+                                                    e1.lo0[0], e1.lo0[1], e1.lo1[0], e1.lo1[1]};
+                            A[r][2 * Pp + 1] = (h8){e0.hi0[0], e0.hi0[1], e0.hi1[0], e0.hi1[1],
+                                                    e1.hi0[0], e1.hi0[1], e1.hi1[0], e1.hi1[1]};
+                        }
                     }
                     const int gl = s * KC + kk;  // group within the chunk
 #pragma unroll
@@ -578,14 +776,18 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
                         h8 Bv[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
-                        f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
-                        lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], Bv[0], lo, 0, 0, 0);
-                        hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], Bv[1], hi, 0, 0, 0);
-                        lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], Bv[2], lo, 0, 0, 0);
-                        hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], Bv[3], hi, 0, 0, 0);
-                        if (gv)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(sf[i], fmaf(hi[i], 0.0625f, lo[i]), acc[t][i]);
+                        for (int r = 0; r < RB; ++r) {
+                            f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
+                            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][0], Bv[0], lo, 0, 0, 0);
+                            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][1], Bv[1], hi, 0, 0, 0);
+                            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][2], Bv[2], lo, 0, 0, 0);
+                            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][3], Bv[3], hi, 0, 0, 0);
+                            if (gv)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    acc[r][t][i] = fmaf(sf[r][i], fmaf(hi[i], 0.0625f, lo[i]), acc[r][t][i]);
+                        }
                     }
                 }
                 // chunk k + 1 (loaded during chunk k - 1) into the other buffer, last read in chunk k - 1
@@ -600,13 +802,17 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     const uint16_t* xo_base = a.xp + bgl;
     const int n_o8 = a.no8 * 8;
     for (int st0 = s; st0 * 32 < n_o8; st0 += 4 * S) {
-        h8 Av[4], Bo[4][NBT];
+        h8 Av[RB][4], Bo[4][NBT];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int col0 = 32 * (st0 + q * S) + 8 * c;
             const bool in = col0 < n_o8;
-            Av[q] = __builtin_bit_cast(h8, gload_u4(a.wout + ((int64_t)tb * a.no8 + (in ? col0 >> 3 : 0)) * 16 + m));
-            if (!in) Av[q] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                Av[r][q] = __builtin_bit_cast(
+                    h8, gload_u4(a.wout + ((int64_t)tb[r] * a.no8 + (in ? col0 >> 3 : 0)) * 16 + m));
+                if (!in) Av[r][q] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+            }
 #pragma unroll
             for (int t = 0; t < NBT; ++t) {
                 const int bc = t * 16 + m;
@@ -618,38 +824,50 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int t = 0; t < NBT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av[q], Bo[q][t], acc[t], 0, 0, 0);
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int t = 0; t < NBT; ++t)
+                    acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av[r][q], Bo[q][t], acc[r][t], 0, 0, 0);
     }
 
     // lane (c, m) holds rows 4c .. 4c + 3 of the tile, batch column 16t + m
     if (S > 1) {
-        typedef float RedTile[NBT][16][17];
+        typedef float RedTile[RB][NBT][16][17];
         RedTile* red = reinterpret_cast<RedTile*>(lds);
         __syncthreads();                               // the staging buffers are dead
 #pragma unroll
-        for (int t = 0; t < NBT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][t][4 * c + i][m] = acc[t][i];
-        __syncthreads();
-        if (s == 0) {
+        for (int r = 0; r < RB; ++r)
 #pragma unroll
             for (int t = 0; t < NBT; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = acc[t][i];
-                    for (int p = 1; p < S; ++p) v += red[wave + p][t][4 * c + i][m];
-                    acc[t][i] = v;
-                }
+                for (int i = 0; i < 4; ++i) red[wave][r][t][4 * c + i][m] = acc[r][t][i];
+        __syncthreads();
+        if (s == 0) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int t = 0; t < NBT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = acc[r][t][i];
+                        for (int p = 1; p < S; ++p) v += red[wave + p][r][t][4 * c + i][m];
+                        acc[r][t][i] = v;
+                    }
         }
     }
-    if (s == 0 && tile_ok) {
+    if (s == 0) {
 #pragma unroll
-        for (int t = 0; t < NBT; ++t) {
-            const int bc = t * 16 + m;
+        for (int r = 0; r < RB; ++r) {
+            if (!tile_ok[r]) continue;
+            const int trow0 = (t16 + r) * 16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = trow0 + 4 * c + i;
-                if (bc < b && n < a.N) *gptr(a.y + (int64_t)bc * a.ldy + n) = f_to_h(acc[t][i]);
+            for (int t = 0; t < NBT; ++t) {
+                const int bc = t * 16 + m;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = trow0 + 4 * c + i;
+                    if (bc < b && n < a.N) *gptr(a.y + (int64_t)bc * a.ldy + n) = f_to_h(acc[r][t][i]);
+                }
             }
         }
     }
@@ -703,21 +921,37 @@ hipError_t launch_int8_valu(const Int8Args& a, int quads, hipStream_t s) {
     return launch_kernel(qgemv_int8_valu<B>, dim3(quads), dim3(64), 0, s, a);
 }
 
-template <int NBT, int T, int S>
-hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s) {
-    return launch_kernel(qgemm_int4o_mfma<NBT, T, S>, dim3((unsigned)woq::ceil_div(tiles, T)), dim3(64 * T * S), 0, s,
-                         a, b);
+template <int T, int S>
+hipError_t launch_int8_mfma_ts(const Int8Args& a, int b, hipStream_t s) {
+    const int tiles = (int)woq::ceil_div(a.N, 16);
+    return launch_kernel(qgemm_int8_mfma<T, S>, dim3((unsigned)woq::ceil_div(tiles, T)), dim3(64 * T * S), 0, s, a,
+                         b);
 }
 
-// Tiles per workgroup (T) and waves per tile (S) of the matrix-core kernel,
-// measured on MI355X over the 3B- and 70B-shaped products: the widest
-// products give each wave whole rows and share the staged activations among
-// eight tiles; narrower ones split K over more waves so that every compute
-// unit has loads in flight.
+hipError_t launch_int8_mfma(const Int8Args& a, int b, hipStream_t s) {
+    const int tiles = (int)woq::ceil_div(a.N, 16);
+    if (tiles >= 1024) return launch_int8_mfma_ts<8, 1>(a, b, s);
+    return launch_int8_mfma_ts<2, 4>(a, b, s);
+}
+
+template <int NBT, int T, int S, int RB = 1>
+hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s) {
+    return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB>, dim3((unsigned)woq::ceil_div(tiles, T * RB)),
+                         dim3(64 * T * S), 0, s, a, b);
+}
+
+// Tiles per workgroup (T), waves per tile (S) and tiles per wave (RB) of the
+// matrix-core kernel, measured on MI355X over the 3B- and 70B-shaped
+// products: the widest products give each wave two whole tiles (each
+// activation fragment read from LDS feeds both, which halves the LDS reads
+// and the staged activation traffic per weight byte: 70B gate|up 59 -> 51 us
+// at b = 8 and 88 -> 67 us at b = 32) and share the staged activations among
+// eight waves; narrower ones split K over more waves so that every compute
+// unit has loads in flight (there, two tiles per wave were slower).
 template <int NBT>
 hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
-    if (tiles >= 2048) return launch_int4o_mfma_ts<NBT, 8, 1>(a, b, tiles, s);
+    if (tiles >= 2048) return launch_int4o_mfma_ts<NBT, 8, 1, NBT <= 2 ? 2 : 1>(a, b, tiles, s);
     if constexpr (NBT >= 3) {
         return launch_int4o_mfma_ts<NBT, 2, 2>(a, b, tiles, s);
     } else {
@@ -927,6 +1161,7 @@ int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t 
     const int quads = (int)woq::ceil_div(w->N, 4);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (int8_use_mfma(w->N, b)) return launch_status(launch_int8_mfma(a, (int)b, s));
     switch (b) {
         case 1: e = launch_int8_valu<1>(a, quads, s); break;
         case 2: e = launch_int8_valu<2>(a, quads, s); break;

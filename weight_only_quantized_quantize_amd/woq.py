@@ -274,8 +274,17 @@ def woq_layout_int4o_inverse(dc, ds, dw, N: int, g: Int4oGeom):
 
 # --------------------------------------------------------------- device ops
 
+def need_rows(b: int, *tensors):
+    """The library takes plain pointers and cannot see buffer sizes: refuse a
+    batch larger than any of the row-major buffers it would read or write."""
+    for t in tensors:
+        if t is not None and b > t.shape[0]:
+            raise ValueError(f"batch {b} exceeds a buffer of {t.shape[0]} rows")
+
+
 def woq_permute_x(x, perm_dev, g: Int4oGeom, xp, stream=None, ldx: int | None = None):
     b = x.shape[0]
+    need_rows(b, xp)
     _check(_lib().woq_permute_x(_ptr(x), ldx or x.shape[1], _ptr(perm_dev), b, ctypes.byref(g), _ptr(xp),
                                 _stream(stream)), "woq_permute_x")
     return xp
@@ -283,6 +292,7 @@ def woq_permute_x(x, perm_dev, g: Int4oGeom, xp, stream=None, ldx: int | None = 
 
 def woq_qgemv_int8(w: Int8W, x, y, stream=None, b: int | None = None):
     b = x.shape[0] if b is None else b
+    need_rows(b, x, y)
     _check(_lib().woq_qgemv_int8(ctypes.byref(w), _ptr(x), x.shape[1], b, _ptr(y), y.shape[1], _stream(stream)),
            "woq_qgemv_int8")
     return y
@@ -312,6 +322,7 @@ def woq_quantize_int4o_dev(W, perm_dev, g: Int4oGeom, codes, scales, w_out, stat
 def woq_embed_int8(w: Int8W, ids, y, stream=None, b: int | None = None):
     """Look up rows ``ids`` (int32 device tensor [b]) of an INT8 table into y (fp16 [b, ldy])."""
     b = ids.shape[0] if b is None else b
+    need_rows(b, ids, y)
     _check(_lib().woq_embed_int8(ctypes.byref(w), _ptr(ids), b, _ptr(y), y.shape[1], _stream(stream)),
            "woq_embed_int8")
     return y
@@ -319,6 +330,7 @@ def woq_embed_int8(w: Int8W, ids, y, stream=None, b: int | None = None):
 
 def woq_qgemv_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
     b = xp.shape[0] if b is None else b
+    need_rows(b, xp, y)
     _check(_lib().woq_qgemv_int4o(ctypes.byref(w), _ptr(xp), b, _ptr(y), y.shape[1], _stream(stream)),
            "woq_qgemv_int4o")
     return y
@@ -337,6 +349,7 @@ def woq_qgemv_int4o_x_supported(g: Int4oGeom, b: int) -> bool:
 
 def woq_qgemv_int4o_x(w: Int4oW, x, pos_dev, y, stream=None, b: int | None = None, ldx: int | None = None):
     b = x.shape[0] if b is None else b
+    need_rows(b, x, y)
     _check(_lib().woq_qgemv_int4o_x(ctypes.byref(w), _ptr(x), ldx or x.shape[1], _ptr(pos_dev), b, _ptr(y),
                                     y.shape[1], _stream(stream)), "woq_qgemv_int4o_x")
     return y
@@ -349,6 +362,7 @@ def woq_stream_read(buf, stream=None):
 
 def woq_qgemm_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
     b = xp.shape[0] if b is None else b
+    need_rows(b, xp, y)
     _check(_lib().woq_qgemm_int4o(ctypes.byref(w), _ptr(xp), b, _ptr(y), y.shape[1], _stream(stream)),
            "woq_qgemm_int4o")
     return y
@@ -436,6 +450,7 @@ class Stack:
         self._pin, self._pout = self._ptrs(self._in), self._ptrs(self._out)
 
     def run(self, b: int, stream=None):
+        need_rows(b, *self._in, *self._out)
         _check(_lib().woq_stack_run(self.handle, self._pin, self._pout, b, _stream(stream)), "woq_stack_run")
 
     def launches(self, b: int) -> int:
@@ -444,6 +459,7 @@ class Stack:
         return n.value
 
     def run_fused(self, b: int, stream=None):
+        need_rows(b, *self._in, *self._out)
         _check(_lib().woq_stack_run_fused(self.handle, self._pin, self._pout, b, _stream(stream)),
                "woq_stack_run_fused")
 
@@ -451,12 +467,14 @@ class Stack:
         _check(_lib().woq_stack_check(self.handle, _stream(stream)), "woq_stack_check")
 
     def time_fused(self, b: int, iters: int, stream=None) -> float:
+        need_rows(b, *self._in, *self._out)
         pass_ms = c_float()
         _check(_lib().woq_stack_time_fused(self.handle, self._pin, self._pout, b, _stream(stream), iters,
                                            ctypes.byref(pass_ms)), "woq_stack_time_fused")
         return pass_ms.value
 
     def time(self, b: int, iters: int, stream=None):
+        need_rows(b, *self._in, *self._out)
         step_ms = (c_float * max(1, self.n))()
         pass_ms = c_float()
         _check(_lib().woq_stack_time(self.handle, self._pin, self._pout, b, _stream(stream), iters, step_ms,
@@ -559,6 +577,7 @@ class Pager:
         self._pout = (c_void_p * len(self._out))(*[t.data_ptr() for t in self._out])
 
     def run(self, b: int, compute_stream, copy_stream):
+        need_rows(b, *self._in, *self._out)
         _check(_lib().woq_pager_run(self.handle, self._pin, self._pout, b, _stream(compute_stream),
                                     _stream(copy_stream)), "woq_pager_run")
 
