@@ -370,8 +370,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
 // for every four rows and spends 2 dot2 per 4 weights per batch row, so its
 // time grows with b; the matrix-core kernel's time does not grow with b but
 // its wave loads cover 16 rows x 64 bytes, which streams slower.  The matrix
-// cores win on wide products from b = 5 (57344-row-class: 30 vs 62 us at
-// b = 8) and on mid-size ones from b = 7; narrow ones stay on the vector ALU.
+// cores win on wide products from b = 5 (9B gate|up, 28672 x 3584: 30 vs
+// 62 us at b = 8) and on mid-size ones from b = 7; narrow ones stay on the vector ALU.
 inline bool int8_use_mfma(int64_t N, int64_t b) {
     const int64_t tiles = (N + 15) / 16;
     return (tiles >= 1024 && b >= 5) || (tiles >= 512 && b >= 7);
