@@ -900,6 +900,15 @@ template <int B, bool GATHER>
 hipError_t launch_int4o_tile(const Int4oArgs& a, const GatherArgs& ga, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
     const size_t lds = (size_t)woq::int4o_valu_lds_bytes(a.xp_len, 4 * (int64_t)a.G4, B);
+    // plans from in-stack sweeps on MI355X (b = 1): long rows on few tiles
+    // (3B down, 70B down) want eight waves per tile so every SIMD streams;
+    // wide products with long rows (70B gate|up) one tile per workgroup; wide
+    // products with short rows (3B gate|up, the 128256-row head) two tiles of
+    // two waves; the rest one tile of four waves
+    if (a.G4 >= 48 && (tiles < 256 || a.G4 >= 128))
+        return launch_kernel(qgemv_int4o_tile<B, 1, 8, GATHER>, dim3((unsigned)tiles), dim3(512), lds, s, a, ga);
+    if (tiles >= 2048 && a.G4 >= 48)
+        return launch_kernel(qgemv_int4o_tile<B, 1, 4, GATHER>, dim3((unsigned)tiles), dim3(256), lds, s, a, ga);
     if (tiles >= 1024)
         return launch_kernel(qgemv_int4o_tile<B, 2, 2, GATHER>, dim3((unsigned)woq::ceil_div(tiles, 2)), dim3(256),
                              lds, s, a, ga);
