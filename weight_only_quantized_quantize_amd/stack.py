@@ -203,6 +203,8 @@ class TieredStack(_QuantisedStack):
         if resident is None:
             resident, self.planned_device_bytes = woq.woq_plan_tiers([o] * self.n_layers, budget_bytes)
         self.resident = np.asarray(resident, np.int32)
+        if self.resident.shape != (self.n_layers,):
+            raise ValueError(f"resident needs one flag per layer ({self.n_layers})")
         streamed = [l for l in range(self.n_layers) if not self.resident[l]]
         self.pool = torch.empty(max(1, len(streamed) * o), dtype=torch.uint8, pin_memory=True)
         pool_np = self.pool.numpy()
@@ -326,6 +328,8 @@ class PooledStack:
         if resident is None:
             resident, self.planned_device_bytes = woq.woq_plan_tiers([B] * L, budget_bytes)
         self.resident = np.asarray(resident, np.int32)
+        if self.resident.shape != (L,):
+            raise ValueError(f"resident needs one flag per layer ({L})")
         streamed = [l for l in range(L) if not self.resident[l]]
         self.pool = torch.empty(max(1, len(streamed) * B), dtype=torch.uint8, pin_memory=True)
         pool_np = self.pool.numpy()
