@@ -367,6 +367,28 @@ def test_int4o_mfma_wide_batch_wide_product(gpu_lib, b, N, K):
     check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma wide b={b}")
 
 
+@pytest.mark.parametrize("b,N,K", [(3, 6200, 8200), (5, 700, 28700), (8, 4100, 8300), (8, 700, 28700),
+                                   (6, 300, 10000), (8, 16, 8100)])
+def test_int4o_mfma_long_rows_small_batch(gpu_lib, b, N, K):
+    """Matrix-core products on rows of 64 groups or more at b <= 8, which stage
+    only 8 activation columns in chunks of 16 groups: ragged row counts, a
+    partial last chunk, on sampled rows including the first and last."""
+    _print_case("int4o mfma long rows", b, N, K)
+    rng = np.random.default_rng(b * 7 + N + K)
+    g = woq.woq_int4o_geometry(K)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x, force_mfma=True)
+    rows = np.unique(np.concatenate([np.arange(min(N, 16)), np.sort(rng.choice(N, min(N, 100), replace=False)),
+                                     np.arange(max(0, N - 16), N)]))
+    check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma long rows b={b} {N}x{K}")
+
+
 @pytest.mark.parametrize("N,K", [(1280, 8192), (7168, 8192), (8192, 1024), (8192, 3584)])
 @pytest.mark.parametrize("b", [1, 8, 32])
 def test_int4o_tp8_share_shapes(gpu_lib, N, K, b):

@@ -621,20 +621,22 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int8_mfma(Int8Args a, int b)
 // unconditional (clamped to a valid address, results unused), so the number
 // of loads in flight is the same on every path and each wait is exact.
 // Partial sums of the S waves of a tile meet in LDS.
-template <int NBT, int T, int S, int RB>
+template <int NBT, int T, int S, int RB, bool HALF>
 __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int b) {
+    static_assert(!HALF || NBT == 1, "half-width staging is for one column tile");
     constexpr int W = T * S;
     // groups per chunk: with the K split, chunks of 8 groups halve the
     // barriers per group (measured faster on MI355X); wide batches are bound
-    // by the LDS the staged columns need
-    constexpr int CHB = NBT == 1 ? (S >= 2 ? 8 : 4) : NBT == 2 ? 4 : 2;
+    // by the LDS the staged columns need; with 8 staged columns (b <= 8) the
+    // same LDS holds chunks of 16 groups
+    constexpr int CHB = NBT == 1 ? (S >= 2 ? (HALF ? 16 : 8) : 4) : NBT == 2 ? 4 : 2;
     constexpr int CH = S > CHB ? S : CHB;             // groups per chunk
     constexpr int KC = CH / S;                        // groups per wave per chunk
     constexpr int P = NBT == 1 ? 8 : 4;               // weight window (groups), whole chunks
     static_assert(P % KC == 0, "window must hold whole chunks");
     constexpr int UNR = P / KC < 2 ? 2 : P / KC;      // chunks per unrolled loop body (even)
     static_assert(UNR % 2 == 0 && UNR % (P / KC) == 0, "unroll");
-    constexpr int COLS = 16 * NBT;                    // batch columns of the B operand
+    constexpr int COLS = HALF ? 8 : 16 * NBT;         // staged batch columns (the B operand has 16 * NBT)
     constexpr int XS = CH * 128 + 8;                  // LDS column stride (fp16), padded against bank conflicts
     constexpr int PPC = CH * 16;                      // 16-byte pieces of one column per chunk
     constexpr int NPT = (COLS * PPC + 64 * W - 1) / (64 * W);   // staged pieces per thread (b = COLS)
@@ -772,10 +774,15 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
                     const int gl = s * KC + kk;  // group within the chunk
 #pragma unroll
                     for (int t = 0; t < NBT; ++t) {
-                        const lx_ptr xb = (lx_ptr)&xs[cb & 1][16 * t + m][128 * gl + 32 * c];
                         h8 Bv[4];
+                        if (!HALF || m < COLS) {
+                            const lx_ptr xb = (lx_ptr)&xs[cb & 1][HALF ? m : 16 * t + m][128 * gl + 32 * c];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
+                            for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) Bv[q] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+                        }
 #pragma unroll
                         for (int r = 0; r < RB; ++r) {
                             f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
@@ -945,7 +952,15 @@ hipError_t launch_int8_mfma(const Int8Args& a, int b, hipStream_t s) {
 
 template <int NBT, int T, int S, int RB = 1>
 hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s) {
-    return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB>, dim3((unsigned)woq::ceil_div(tiles, T * RB)),
+    // up to 8 batch columns on long rows: stage 8 columns only, in chunks of
+    // 16 groups (70B down at b = 8: 42.6 -> 37.5 us; on rows of 24 groups the
+    // longer chunks were slower)
+    if constexpr (NBT == 1) {
+        if (b <= 8 && a.G4 >= 64)
+            return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, true>, dim3((unsigned)woq::ceil_div(tiles, T * RB)),
+                                 dim3(64 * T * S), 0, s, a, b);
+    }
+    return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, false>, dim3((unsigned)woq::ceil_div(tiles, T * RB)),
                          dim3(64 * T * S), 0, s, a, b);
 }
 
