@@ -323,6 +323,21 @@ int woq_qgemv_int4o_x_supported(const woq_int4o_geom* g, int64_t b);
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
                     int64_t ldy, void* stream);
 
+/*
+ * woq_qgemm_int4o with the groups of every row split into `splits` K ranges
+ * (1..16) that run as separate workgroups covering more rows each, so that
+ * each staged activation chunk serves more weights; each range's fp32 partial
+ * sums go to workspace (device memory, 16-byte aligned, at least
+ * woq_qgemm_int4o_splitk_workspace(N, b, splits) bytes, owned by the caller;
+ * its contents on return are unspecified), and a second launch adds the
+ * ranges in a fixed order into y.  The same result as woq_qgemm_int4o up to
+ * summation order, deterministic for a given split count.  Calls that share
+ * a workspace must not overlap.
+ */
+int woq_qgemm_int4o_splitk(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy,
+                           int32_t splits, float* workspace, int64_t workspace_bytes, void* stream);
+int64_t woq_qgemm_int4o_splitk_workspace(int64_t N, int64_t b, int32_t splits);
+
 /* --------------------------------------------------------- layer stack */
 
 #define WOQ_FMT_INT8  1

@@ -389,6 +389,43 @@ def test_int4o_mfma_long_rows_small_batch(gpu_lib, b, N, K):
     check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma long rows b={b} {N}x{K}")
 
 
+@pytest.mark.parametrize("b,N,K,splits", [(3, 1000, 16400, 8), (8, 1000, 16400, 2), (17, 300, 16400, 5),
+                                          (32, 2056, 16400, 8), (8, 16, 2000, 16), (5, 33, 1000, 1)])
+def test_int4o_splitk_entry_point(gpu_lib, b, N, K, splits):
+    """The matrix-core product over K ranges with partial sums in a caller
+    workspace: against the oracle on sampled rows, against the single-launch
+    product within rounding, and deterministic from call to call (more splits
+    than groups leave empty ranges)."""
+    import torch
+    _print_case("int4o split-K", b, N, K, splits)
+    rng = np.random.default_rng(b + N + K + splits)
+    g = woq.woq_int4o_geometry(K)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y1, xp_host = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x, force_mfma=True)
+    dw = woq.DeviceInt4o(int4o_parts([W], perm, g.n_out), g)
+    xp = _dev(xp_host.astype(np.float16))
+    nbytes = woq.lib().woq_qgemm_int4o_splitk_workspace(N, b, splits)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = _empty16(b, N)
+    woq.woq_qgemm_int4o_splitk(dw.desc, xp, y, splits, ws)
+    ys = _host(y)
+    woq.woq_qgemm_int4o_splitk(dw.desc, xp, y, splits, ws)
+    np.testing.assert_array_equal(_host(y).view(np.uint16), ys.view(np.uint16))
+    rows = np.unique(np.concatenate([np.arange(min(N, 16)), np.sort(rng.choice(N, min(N, 100), replace=False)),
+                                     np.arange(max(0, N - 16), N)]))
+    check(ys.astype(np.float64)[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"split-K b={b} s={splits}")
+    assert O.normwise_rel_err(ys.astype(np.float64), y1) <= TOL
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_qgemm_int4o_splitk(dw.desc, xp, y, splits, ws[:nbytes // 4 - 1])
+    assert e.value.status == woq.WOQ_EINVAL
+
+
 @pytest.mark.parametrize("N,K", [(1280, 8192), (7168, 8192), (8192, 1024), (8192, 3584)])
 @pytest.mark.parametrize("b", [1, 8, 32])
 def test_int4o_tp8_share_shapes(gpu_lib, N, K, b):

@@ -132,6 +132,43 @@ def test_small_stack_runner_equals_entry_points_and_oracle(gpu_lib, cfg, b):
             assert err <= TOL
 
 
+@pytest.mark.parametrize("b", [3, 8, 20])
+def test_stack_long_rows_use_split_k(gpu_lib, b):
+    """A stack whose down product has rows of 129 groups (intermediate 16500):
+    the runner splits that product's K range (one more launch for the
+    reduction); its outputs equal the split-K entry point composed by hand bit
+    for bit and match the oracle."""
+    import torch
+    _case("long-row stack", b)
+    spec = synth.small_stack_spec(2, layers=1, hidden=384, inter=16500, batches=(b,))
+    rs = build(spec)
+    ins, outs = io(spec, rs, b)
+    runner = rs.make_runner(b)
+    runner.bind(ins, outs)
+    runner.run(b)
+    got = [host(t).copy() for t in outs]
+    names, inp = GROUPS[3]
+    dev = rs.layers[0][3][2]
+    g = dev.geom
+    assert g.G4 >= 128
+    xp = torch.empty(b, g.xp_len, dtype=torch.float16, device="cuda")
+    woq.woq_permute_x(ins[3], rs.perm_dev["m"], g, xp)
+    nbytes = woq.lib().woq_qgemm_int4o_splitk_workspace(dev.N, b, 8)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(outs[3])
+    woq.woq_qgemm_int4o_splitk(dev.desc, xp, y, 8, ws)
+    np.testing.assert_array_equal(host(y).view(np.uint16), got[3].view(np.uint16))
+    # q|k|v and o fold their permutation at b = 3 (one launch each); every
+    # other product is a permutation launch plus a product launch, and the
+    # split down product adds the reduction
+    assert runner.launches(b) == (7 if b == 3 else 9)
+    perms = oracle_perms(spec)
+    for gi, (nm, ip) in enumerate(GROUPS):
+        err = O.normwise_rel_err(got[gi].astype(np.float64), oracle_group(spec, perms, 0, nm, ip, b))
+        print(f"{'|'.join(nm)}: {err:.3e}", flush=True)
+        assert err <= TOL
+
+
 def test_config2_stack_full_size(gpu_lib):
     """The 3B-shaped INT4O stack at full size, batch 1: every output equals the
     two-call form (permute, then product) bit for bit, and sampled rows of

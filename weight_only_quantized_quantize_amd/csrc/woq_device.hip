@@ -147,6 +147,11 @@ struct Int4oArgs {
     const uint16_t* xp;     // [b][xp_len] permuted, split activations
     uint16_t* y;            // [b][ldy]
     int N, G4, no8, xp_len, ldy;
+    // split of the groups over blockIdx.y (matrix-core kernel): 0, or the
+    // groups per split; split s writes its fp32 partial sums to
+    // part[s][b][N] instead of y, and only split 0 adds the outlier columns
+    int gsplit = 0;
+    float* part = nullptr;
 };
 
 // Activations in their natural channel order and the position of every
@@ -438,6 +443,18 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
     }
 }
 
+// y[r][n] = fp16(sum over s of part[s][r][n]), s in order: the split-K
+// partial sums of the matrix-core kernel, added in a fixed order.
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int splits, int b, int N,
+                                                            uint16_t* __restrict__ y, int ldy) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)b * N) return;
+    const int r = (int)(i / N), n = (int)(i % N);
+    float v = *gptr(part + i);
+    for (int q = 1; q < splits; ++q) v += *gptr(part + (int64_t)q * b * N + i);
+    *gptr(y + (int64_t)r * ldy + n) = f_to_h(v);
+}
+
 // ------------------------------------------------ INT8, matrix cores (b >= 3)
 
 // A workgroup of T x S waves owns T tiles of 16 output rows of the row-major
@@ -661,9 +678,14 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
         tile_ok[r] = t16 + r < tiles;
         tb[r] = tile_ok[r] ? t16 + r : 0;
     }
-    const int G4 = a.G4, xp_len = a.xp_len;
+    const int split = blockIdx.y;
+    const int G4s = a.G4;                             // groups per tile row in memory
+    const int gbeg = a.gsplit ? split * a.gsplit : 0; // first group of this launch's K range
+    const int G4 = a.gsplit ? max(0, min(a.gsplit, G4s - gbeg)) : G4s;
+    const int xp_len = a.xp_len;
     const int nchunks = (G4 + CH - 1) / CH;
     const int bgl = 128 * G4;
+    const uint16_t* xpb = a.xp + 128 * gbeg;          // this K range's activations
 
     f4 acc[RB][NBT];
 #pragma unroll
@@ -686,7 +708,7 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
             const int p = tid + i * 64 * W;
             const int col = p / PPC, ch = kk * CH * 128 + 8 * (p % PPC);
             const bool ok = col < b && ch < bgl;
-            r[i] = load_x16((gx_ptr)(a.xp + (ok ? (int64_t)col * xp_len + ch : 0)));
+            r[i] = load_x16((gx_ptr)(ok ? xpb + (int64_t)col * xp_len + ch : a.xp));
         }
     };
     auto stage_store = [&](const uint4 (&r)[NPT], int buf, int k) {
@@ -712,8 +734,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     const uint2* sld[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        wld[r] = a.codes + (int64_t)tb[r] * G4 * 64 + c * 16 + m;
-        sld[r] = reinterpret_cast<const uint2*>(a.scales) + (int64_t)tb[r] * G4 * 4 + c;
+        wld[r] = a.codes + ((int64_t)tb[r] * G4s + gbeg) * 64 + c * 16 + m;
+        sld[r] = reinterpret_cast<const uint2*>(a.scales) + ((int64_t)tb[r] * G4s + gbeg) * 4 + c;
     }
 
     uint4 wq[P][RB];
@@ -806,8 +828,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
 
     // FP16 outlier columns, 32 per k-step, split over the S waves of the tile;
     // up to four k-steps' loads in flight at once
-    const uint16_t* xo_base = a.xp + bgl;
-    const int n_o8 = a.no8 * 8;
+    const uint16_t* xo_base = a.xp + 128 * G4s;
+    const int n_o8 = split == 0 ? a.no8 * 8 : 0;
     for (int st0 = s; st0 * 32 < n_o8; st0 += 4 * S) {
         h8 Av[RB][4], Bo[4][NBT];
 #pragma unroll
@@ -873,7 +895,10 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int n = trow0 + 4 * c + i;
-                    if (bc < b && n < a.N) *gptr(a.y + (int64_t)bc * a.ldy + n) = f_to_h(acc[r][t][i]);
+                    if (bc < b && n < a.N) {
+                        if (a.part) *gptr(a.part + ((int64_t)split * b + bc) * a.N + n) = acc[r][t][i];
+                        else *gptr(a.y + (int64_t)bc * a.ldy + n) = f_to_h(acc[r][t][i]);
+                    }
                 }
             }
         }
@@ -951,17 +976,18 @@ hipError_t launch_int8_mfma(const Int8Args& a, int b, hipStream_t s) {
 }
 
 template <int NBT, int T, int S, int RB = 1>
-hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s) {
+hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s, int splits = 1) {
     // up to 8 batch columns on long rows: stage 8 columns only, in chunks of
     // 16 groups (70B down at b = 8: 42.6 -> 37.5 us; on rows of 24 groups the
     // longer chunks were slower)
     if constexpr (NBT == 1) {
         if (b <= 8 && a.G4 >= 64)
-            return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, true>, dim3((unsigned)woq::ceil_div(tiles, T * RB)),
-                                 dim3(64 * T * S), 0, s, a, b);
+            return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, true>,
+                                 dim3((unsigned)woq::ceil_div(tiles, T * RB), (unsigned)splits), dim3(64 * T * S), 0,
+                                 s, a, b);
     }
-    return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, false>, dim3((unsigned)woq::ceil_div(tiles, T * RB)),
-                         dim3(64 * T * S), 0, s, a, b);
+    return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, false>,
+                         dim3((unsigned)woq::ceil_div(tiles, T * RB), (unsigned)splits), dim3(64 * T * S), 0, s, a, b);
 }
 
 // Tiles per workgroup (T), waves per tile (S) and tiles per wave (RB) of the
@@ -982,6 +1008,25 @@ hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
         if (tiles >= 640) return launch_int4o_mfma_ts<NBT, 4, 2>(a, b, tiles, s);
         if (tiles >= 256) return launch_int4o_mfma_ts<NBT, 2, 4>(a, b, tiles, s);
         return launch_int4o_mfma_ts<NBT, 1, 8>(a, b, tiles, s);
+    }
+}
+
+// Split-K launches: each workgroup covers more rows (fewer workgroups along
+// N, so fewer re-reads of the staged activations) and blockIdx.y picks the K
+// range.
+template <int NBT>
+hipError_t launch_int4o_mfma_split_nbt(const Int4oArgs& a, int b, int splits, hipStream_t s) {
+    const int tiles = (int)woq::ceil_div(a.N, 16);
+    if constexpr (NBT == 2) return launch_int4o_mfma_ts<NBT, 8, 1, 2>(a, b, tiles, s, splits);
+    return launch_int4o_mfma_ts<NBT, 8, 1, 1>(a, b, tiles, s, splits);
+}
+
+hipError_t launch_int4o_mfma_split(const Int4oArgs& a, int b, int splits, hipStream_t s) {
+    switch ((b + 15) / 16) {
+        case 1: return launch_int4o_mfma_split_nbt<1>(a, b, splits, s);
+        case 2: return launch_int4o_mfma_split_nbt<2>(a, b, splits, s);
+        case 3: return launch_int4o_mfma_split_nbt<3>(a, b, splits, s);
+        default: return launch_int4o_mfma_split_nbt<4>(a, b, splits, s);
     }
 }
 
@@ -1084,6 +1129,34 @@ int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_
         case 2: e = launch_int4o_mfma<2>(a, (int)b, s); break;
         case 3: e = launch_int4o_mfma<3>(a, (int)b, s); break;
         default: e = launch_int4o_mfma<4>(a, (int)b, s); break;
+    }
+    return launch_status(e);
+}
+
+int64_t woq_qgemm_int4o_splitk_workspace(int64_t N, int64_t b, int32_t splits) {
+    if (N < 0 || b < 0 || splits < 1) return -1;
+    return (int64_t)splits * b * N * (int64_t)sizeof(float);
+}
+
+int woq_qgemm_int4o_splitk(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy,
+                           int32_t splits, float* workspace, int64_t workspace_bytes, void* stream) {
+    int st = int4o_common_checks(w, xp, b, y, ldy);
+    if (st) return st;
+    if (splits < 1 || splits > 16) return WOQ_EINVAL;
+    if (b == 0 || w->N == 0) return WOQ_OK;
+    if (!workspace || workspace_bytes < woq_qgemm_int4o_splitk_workspace(w->N, b, splits)) return WOQ_EINVAL;
+    if (!woq::aligned16(workspace)) return WOQ_EALIGN;
+    if ((int64_t)splits * b * w->N > INT32_MAX) return WOQ_EUNSUPPORTED;
+    Int4oArgs a = make_int4o_args(w, xp, y, ldy);
+    a.gsplit = (int)woq::ceil_div(w->geom.G4, splits);
+    a.part = workspace;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_int4o_mfma_split(a, (int)b, splits, s);
+    if (e == hipSuccess) {
+        const int64_t n = b * w->N;
+        hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)woq::ceil_div(n, 256)), dim3(256), 0, s,
+                           (const float*)workspace, (int)splits, (int)b, (int)w->N, y, (int)ldy);
+        e = hipGetLastError();
     }
     return launch_status(e);
 }

@@ -91,4 +91,16 @@ inline bool int4o_use_valu(int64_t N, const woq_int4o_geom& g, int64_t b) {
     return b <= 2 || ceil_div(N, 16) < 384;
 }
 
+// K splits the stack runner gives a matrix-core INT4O product (0: none).
+// Rows of 128 groups or more (the 70B-shaped down product, 224 groups) are
+// split in 8: every workgroup then covers 128 rows and one eighth of K, which
+// cuts the activation staging per weight byte (70B down at b = 8: 38 -> 33 us,
+// at b = 32: 62 -> 46 us, the reduction launch included); shorter rows gained
+// nothing.
+constexpr int INT4O_SPLITS = 8;
+inline int int4o_splitk(int64_t N, const woq_int4o_geom& g, int64_t b) {
+    if (int4o_use_valu(N, g, b) || g.G4 < 128 || b > 32) return 0;
+    return INT4O_SPLITS;
+}
+
 }  // namespace woq

@@ -217,6 +217,8 @@ struct woq_stack {
     int64_t max_b = 0;
     int64_t xp_elems = 0;      // per workspace row
     uint16_t* xp = nullptr;    // [max_b][xp_elems]
+    float* part = nullptr;     // split-K partial sums of the long-row INT4O products
+    int64_t part_bytes = 0;
     int device = 0;
     // INT4O: device channel-position table of each step's permutation (null
     // where the row is too long for 16-bit positions); one table per distinct
@@ -242,6 +244,7 @@ int hip_status(hipError_t e) {
 
 void free_stack(woq_stack* st) {
     if (st->xp) (void)hipFree(st->xp);
+    if (st->part) (void)hipFree(st->part);
     if (st->dsteps) (void)hipFree(st->dsteps);
     if (st->sync) (void)hipFree(st->sync);
     for (uint16_t* p : st->pos_owned) (void)hipFree(p);
@@ -313,7 +316,10 @@ int run_step(woq_stack* st, size_t i, const woq_stack_step& s, const uint16_t* x
     }
     // with events, the product launch records them at its own dispatch boundaries
     if (ev) woq::set_launch_events(ev[0], ev[1]);
-    if (s.fmt == WOQ_FMT_INT4O) rc = woq_qgemv_int4o(&s.w4, st->xp, b, y, s.w4.N, stream);
+    const int splits = s.fmt == WOQ_FMT_INT4O ? woq::int4o_splitk(s.w4.N, s.w4.geom, b) : 0;
+    if (splits)
+        rc = woq_qgemm_int4o_splitk(&s.w4, st->xp, b, y, s.w4.N, splits, st->part, st->part_bytes, stream);
+    else if (s.fmt == WOQ_FMT_INT4O) rc = woq_qgemv_int4o(&s.w4, st->xp, b, y, s.w4.N, stream);
     else rc = woq_qgemv_int8(&s.w8, x, s.w8.K, b, y, s.w8.N, stream);
     if (ev) woq::set_launch_events(nullptr, nullptr);
     return rc;
@@ -466,8 +472,17 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
         st->max_xlen = std::max(st->max_xlen, d.xlen);
         st->hsteps[i] = d;
     }
+    for (int i = 0; i < n_steps; ++i) {
+        const woq_stack_step& s = steps[i];
+        if (s.fmt != WOQ_FMT_INT4O) continue;
+        for (int64_t bb = 1; bb <= max_b; ++bb) {
+            const int sp = woq::int4o_splitk(s.w4.N, s.w4.geom, bb);
+            if (sp) st->part_bytes = std::max(st->part_bytes, woq_qgemm_int4o_splitk_workspace(s.w4.N, bb, sp));
+        }
+    }
     hipError_t e = hipGetDevice(&st->device);
     if (e == hipSuccess) e = hipMalloc((void**)&st->xp, (size_t)(max_b * xp_elems * 2));
+    if (e == hipSuccess && st->part_bytes > 0) e = hipMalloc((void**)&st->part, (size_t)st->part_bytes);
     if (e == hipSuccess && n_steps > 0) e = hipMalloc((void**)&st->dsteps, sizeof(DevStep) * n_steps);
     if (e == hipSuccess) e = hipMalloc((void**)&st->sync, sizeof(u64) * SYNC_WORDS);
     if (e == hipSuccess) e = hipMemset(st->sync, 0, sizeof(u64) * SYNC_WORDS);
@@ -489,6 +504,7 @@ int woq_stack_launches(const woq_stack* st, int64_t b, int32_t* launches) {
     for (size_t i = 0; i < st->steps.size(); ++i) {
         const woq_stack_step& s = st->steps[i];
         n += (s.fmt == WOQ_FMT_INT4O && !(st->pos[i] && fold_permutation(s, b))) ? 2 : 1;
+        if (s.fmt == WOQ_FMT_INT4O && woq::int4o_splitk(s.w4.N, s.w4.geom, b)) n += 1;   // the reduction
     }
     *launches = n;
     return WOQ_OK;

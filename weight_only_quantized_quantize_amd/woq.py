@@ -105,6 +105,9 @@ _SIGS = {
     "woq_pool_info": (c_int, [ctypes.c_char_p, POINTER(c_int32), POINTER(c_int64), POINTER(c_int64), c_int32,
                               c_void_p, c_int64]),
     "woq_pool_read_block": (c_int, [ctypes.c_char_p, c_int32, c_void_p, c_int64]),
+    "woq_qgemm_int4o_splitk": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
+                                       c_int64, c_void_p]),
+    "woq_qgemm_int4o_splitk_workspace": (c_int64, [c_int64, c_int64, c_int32]),
     "woq_plan_tiers": (c_int, [c_void_p, c_int32, c_int64, c_void_p, POINTER(c_int64)]),
     "woq_tiered_create": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int64), c_int32, POINTER(StackStep),
                                   c_int32, c_int64, POINTER(c_void_p)]),
@@ -358,6 +361,17 @@ def woq_qgemv_int4o_x(w: Int4oW, x, pos_dev, y, stream=None, b: int | None = Non
 def woq_stream_read(buf, stream=None):
     """Read every byte of a contiguous device tensor (size a multiple of 16)."""
     _check(_lib().woq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)), "woq_stream_read")
+
+
+def woq_qgemm_int4o_splitk(w: Int4oW, xp, y, splits: int, workspace, stream=None, b: int | None = None):
+    """woq_qgemm_int4o over `splits` K ranges; workspace: fp32 device tensor of at
+    least woq_qgemm_int4o_splitk_workspace(N, b, splits) bytes."""
+    b = xp.shape[0] if b is None else b
+    need_rows(b, xp, y)
+    _check(_lib().woq_qgemm_int4o_splitk(ctypes.byref(w), _ptr(xp), b, _ptr(y), y.shape[1], splits, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "woq_qgemm_int4o_splitk")
+    return y
 
 
 def woq_qgemm_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
