@@ -211,6 +211,52 @@ def test_config2_stack_full_size(gpu_lib):
             assert err <= TOL
 
 
+def test_config4_layers_full_size_every_batch(gpu_lib):
+    """Two layers of the 70B-shaped INT4O stack at full size through the
+    runner, in the launch configuration the benchmark times (vector kernel at
+    b = 1, matrix cores at 8 and 32, split-K on down from b = 3): sampled rows
+    of every product against the oracle.  The permutations are the planted
+    sets (the selection is covered elsewhere), which keeps the test short."""
+    spec = synth.stack_spec(4)
+    layers = 2
+    perms = {sp: O.global_perm(spec.space_width(sp), synth.planted_set(spec, sp)).astype(np.int32)
+             for sp in synth.SPACES}
+    _case("config 4 full-size layers")
+    rs = ResidentStack(spec, lambda l, lin, out: synth.weight(spec, l, lin, out=out), None, layers=layers,
+                       perms=perms)
+    runner = rs.make_runner(32)
+    rng = np.random.default_rng(4)
+    # the oracle encodes the sampled rows of every linear once
+    enc = {}
+    for layer in range(layers):
+        for lin in spec.linears():
+            r = np.unique(np.concatenate([[0, lin.N - 1], rng.choice(lin.N, 14, replace=False)]))
+            W = synth.weight(spec, layer, lin)
+            enc[(layer, lin.name)] = (r, O.quantize_int4o(W[r], perms[lin.space], O.n_outliers(lin.K)))
+            del W
+    for b in (1, 8, 32):
+        _case("config 4 full-size layers", b)
+        ins, outs = io(spec, rs, b)
+        runner.bind(ins, outs)
+        runner.run(b)
+        got = [host(t).copy() for t in outs]
+        for layer in range(layers):
+            for gi, (names, inp) in enumerate(GROUPS):
+                x = synth.decode_input(spec, layer, inp, b)
+                refs, offs, cols = [], 0, []
+                for n in names:
+                    lin = spec.linear(n)
+                    r, (c, sc, wo) = enc[(layer, n)]
+                    x_bg, x_out = O.permute_split(x, perms[lin.space], O.n_outliers(lin.K))
+                    refs.append(O.linear_int4o(c, sc, wo, x_bg, x_out))
+                    cols.extend(offs + r)
+                    offs += lin.N
+                err = O.normwise_rel_err(got[4 * layer + gi][:, cols].astype(np.float64), np.concatenate(refs, axis=1))
+                print(f"b={b} layer {layer} {'|'.join(names)}: {err:.3e}", flush=True)
+                assert err <= TOL
+    runner.close()
+
+
 def test_fused_unsupported_batch_falls_back(gpu_lib):
     spec = synth.small_stack_spec(2, layers=1, batches=(8,))
     rs = build(spec)
