@@ -384,9 +384,7 @@ int launch_fused(woq_stack* st, int64_t b, void* stream) {
 }
 
 int prepare_fused(woq_stack* st, int64_t b) {
-    if (!st->fused_ok) return WOQ_EUNSUPPORTED;
-    for (const woq_stack_step& s : st->steps)
-        if (b > 8) return WOQ_EUNSUPPORTED;
+    if (!st->fused_ok || b > 8) return WOQ_EUNSUPPORTED;   // the persistent pass streams INT8 quads, b <= 8
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, st->device);
     if (e != hipSuccess) return hip_status(e);
@@ -552,7 +550,7 @@ int woq_stack_time(woq_stack* st, const uint16_t* const* inputs, uint16_t* const
         *pass_ms = (float)(total / iters);
     }
     for (auto& x : ev)
-        if (x) hipEventDestroy(x);
+        if (x) (void)hipEventDestroy(x);
     if (rc) return rc;
     return hip_status(e);
 }
@@ -609,7 +607,7 @@ int woq_stack_time_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t*
         total += ms;
     }
     for (auto& x : ev)
-        if (x) hipEventDestroy(x);
+        if (x) (void)hipEventDestroy(x);
     if (rc) return rc;
     if (e != hipSuccess) return hip_status(e);
     *pass_ms = (float)(total / iters);
