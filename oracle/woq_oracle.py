@@ -195,7 +195,8 @@ def quantize_int4o(W: np.ndarray, perm: np.ndarray, n_out: int, group: int = GRO
         lo, hi = g * group, min(g * group + group, K_bg)
         blk = Wp[:, lo:hi]
         m = np.max(np.abs(blk), axis=1)                           # fp32, per output row
-        s16 = (m / np.float32(INT4_QMAX)).astype(np.float16)      # fp32 division, then fp16
+        with np.errstate(over="ignore"):                          # overflow is reported just below
+            s16 = (m / np.float32(INT4_QMAX)).astype(np.float16)  # fp32 division, then fp16
         if not np.all(np.isfinite(s16)):
             raise ValueError("group scale overflows fp16")
         s32 = s16.astype(np.float32)
