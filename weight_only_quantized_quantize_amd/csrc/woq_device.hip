@@ -228,20 +228,33 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
         }
     }
 
-    // 2. weight window: this wave's groups s, s + S, ... (J of them)
+    // 2. weight window: this wave's groups s, s + S, ... (J of them), and
+    // the first outlier chunk.  Every load is issued unconditionally (a wave
+    // without groups rereads its tile's group 0; with no groups or no
+    // outliers at all, the loads read the start of the activation row and
+    // are ignored): a load skipped on some path makes the compiler count
+    // every later wait as if it had not been issued, and the activation
+    // staging would then wait for the whole window.
     const int J = G4 > s ? (G4 - 1 - s) / S + 1 : 0;
-    const uint4* wb = a.codes + (int64_t)tb * G4 * 64 + c * 16 + m;
-    const uint16_t* sb = a.scales + (int64_t)tb * G4 * 16 + m;
+    const uint4* dummy = reinterpret_cast<const uint4*>(GATHER ? ga.x : a.xp);
+    const uint4* wb = G4 > 0 ? a.codes + (int64_t)tb * G4 * 64 + c * 16 + m : dummy;
+    // scales are read as the dword holding rows m & ~1 and m | 1, so that
+    // the loaded value needs no zero-extension before it is consumed (a
+    // 16-bit load is followed by a mask, placed where the load arrives)
+    const uint32_t* sb = G4 > 0 ? reinterpret_cast<const uint32_t*>(a.scales + (int64_t)tb * G4 * 16 + (m & ~1))
+                                : reinterpret_cast<const uint32_t*>(dummy);
+    const int sshift = 16 * (m & 1);
     uint4 wq[P];
     uint32_t sq[P];
-    if (J > 0) {
 #pragma unroll
-        for (int u = 0; u < P; ++u) {
-            const int g = s + S * (u < J ? u : J - 1);
-            wq[u] = gload_nt(wb + (int64_t)g * 64);
-            sq[u] = *gptr(sb + g * 16);
-        }
+    for (int u = 0; u < P; ++u) {
+        const int g = G4 > 0 ? (J > 0 ? s + S * (u < J ? u : J - 1) : 0) : 0;
+        wq[u] = gload_nt(wb + (int64_t)g * 64);
+        sq[u] = *gptr(sb + g * 8);
     }
+    const uint4* ob = a.wout + (int64_t)tb * a.no8 * 16 + m;
+    const int i80 = 4 * s + c;
+    const uint4 wo0 = gload_u4(a.no8 > 0 ? ob + (int64_t)(i80 < a.no8 ? i80 : 0) * 16 : dummy);
 
     // 3. activations into LDS
 #pragma unroll
@@ -295,40 +308,52 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
     }
     lds_barrier();
 
-    // 5. background groups
+    // 5. background groups.  A slot is consumed before its refill is issued,
+    // so the refill can land in the same registers: with the old value still
+    // live, the compiler moves refilled slots back at the loop latch, which
+    // waits for every load in flight once per window.  Rows that fit in one
+    // window take no refills at all.
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-    for (int j0 = 0; j0 < J; j0 += P) {
+    auto consume = [&](int j, uint4 w, uint32_t sq1) {
+        const int g = s + S * j;
+        // the scale word is unpacked only here, after the wait for its slot
+        asm volatile("" : "+v"(sq1));
+        const float sc = h_to_f((uint16_t)(sq1 >> sshift));
+        uint4 xg[B][4];
+        float cg[B];
 #pragma unroll
-        for (int u = 0; u < P; ++u) {
-            const int j = j0 + u;
-            const uint4 w = wq[u];
-            const float sc = h_to_f((uint16_t)sq[u]);
-            const int gn = s + S * (j + P < J ? j + P : J - 1);
-            wq[u] = gload_nt(wb + (int64_t)gn * 64);
-            sq[u] = *gptr(sb + gn * 16);
-            if (j < J) {
-                const int g = s + S * j;
-                uint4 xg[B][4];
-                float cg[B];
+        for (int b = 0; b < B; ++b) {
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
+            for (int q = 0; q < 4; ++q) xg[b][q] = load_x16(xl + b * xp_len + 128 * g + 32 * c + 8 * q);
+            cg[b] = corr[b * nq + 4 * g + c];
+        }
+        int4o_row_chunk<B>(w, sc, xg, cg, acc);
+    };
+    if (J <= P) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) xg[b][q] = load_x16(xl + b * xp_len + 128 * g + 32 * c + 8 * q);
-                    cg[b] = corr[b * nq + 4 * g + c];
-                }
-                int4o_row_chunk<B>(w, sc, xg, cg, acc);
+        for (int u = 0; u < P; ++u)
+            if (u < J) consume(u, wq[u], sq[u]);
+    } else {
+        for (int j0 = 0; j0 < J; j0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) {
+                const int j = j0 + u;
+                if (j < J) consume(j, wq[u], sq[u]);
+                const int gn = s + S * (j + P < J ? j + P : J - 1);
+                wq[u] = gload_nt(wb + (int64_t)gn * 64);
+                sq[u] = *gptr(sb + gn * 8);
             }
         }
     }
 
-    // 6. FP16 outlier columns: step st covers outlier chunks 4 st .. 4 st + 3 (lane chunk c)
-    const uint4* ob = a.wout + (int64_t)tb * a.no8 * 16 + m;
+    // 6. FP16 outlier columns: step st covers outlier chunks 4 st .. 4 st + 3
+    // (lane chunk c); the first step's chunk was loaded with the window
     for (int st = s; 32 * st < 8 * a.no8; st += S) {
         const int i8 = 4 * st + c;
         const bool in = i8 < a.no8;
-        const uint4 wo = gload_u4(ob + (int64_t)(in ? i8 : 0) * 16);
+        const uint4 wo = st == s ? wo0 : gload_u4(ob + (int64_t)(in ? i8 : 0) * 16);
         if (in) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
