@@ -416,42 +416,92 @@ struct Int8Args {
     float seg_scale[WOQ_MAX_SEGMENTS];
 };
 
+// One quad of four rows per wave; lane l takes the 16-byte chunks
+// l, l + 64, ... of each row.  The full chunks stream through two register
+// buffers: the loads of chunk i + 1 are in flight while chunk i is consumed,
+// and a buffer is refilled only after it has been consumed, so no register
+// moves (and no waits for loads still in flight) sit at the loop latch.
+// Every load in the loop is unconditional: a lane past the last full chunk
+// rereads it and multiplies it by zero activations.  The chunk that holds the
+// end of a row not a multiple of 16 long is read element by element, by the
+// lane it falls to, after the loop.
 template <int B>
 __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
     const int lane = threadIdx.x;
     const int quad = blockIdx.x;
     const uint4* w0 = a.codes + (int64_t)quad * 4 * a.CPR;
-    const int nchunks = (a.K + 15) >> 4;   // chunks that hold real columns
+    const int nfull = a.K >> 4;            // chunks whose 16 channels are all real
+    const int iters = (nfull + 63) >> 6;   // the same for every lane
     float acc[4][B];
     zero_acc(acc);
-#pragma unroll 2
-    for (int cc = lane; cc < nchunks; cc += 64) {
+    struct Buf {
+        uint4 w[4];
+        uint4 x[B][2];
+    };
+    auto load = [&](Buf& d, int i) {
+        const int c0 = lane + 64 * i;
+        const int cc = c0 < nfull ? c0 : nfull - 1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d.w[r] = gload_nt(w0 + r * a.CPR + cc);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const gx_ptr xs = (gx_ptr)(a.x + (int64_t)b * a.ldx + 16 * cc);
+            d.x[b][0] = load_x16(xs);
+            d.x[b][1] = load_x16(xs + 8);
+        }
+    };
+    auto consume = [&](const Buf& d, int i) {
+        const bool real = lane + 64 * i < nfull;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        uint4 xv[B][2];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            xv[b][0] = real ? d.x[b][0] : z;
+            xv[b][1] = real ? d.x[b][1] : z;
+        }
+        int8_chunk<B>(d.w, xv, acc);
+    };
+    // the scheduling barriers keep each buffer's loads ahead of the other
+    // buffer's waits (the scheduler would otherwise sink them below them)
+    if (iters > 0) {
+        Buf p, q;
+        load(p, 0);
+        int i = 0;
+        for (; i + 2 < iters; i += 2) {
+            load(q, i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(p, i);
+            load(p, i + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(q, i + 1);
+        }
+        if (iters - i == 2) {
+            load(q, i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(p, i);
+            consume(q, i + 1);
+        } else {
+            consume(p, i);
+        }
+    }
+    if (nfull * 16 < a.K && lane == (nfull & 63)) {
         uint4 w[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = gload_nt(w0 + r * a.CPR + cc);
+        for (int r = 0; r < 4; ++r) w[r] = gload_nt(w0 + r * a.CPR + nfull);
         uint4 xv[B][2];
-        const int k0 = 16 * cc;
-        if (k0 + 16 <= a.K) {
+        const int k0 = 16 * nfull;
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const gx_ptr xs = (gx_ptr)(a.x + (int64_t)b * a.ldx + k0);
-                xv[b][0] = load_x16(xs);
-                xv[b][1] = load_x16(xs + 8);
+        for (int b = 0; b < B; ++b) {
+            uint32_t t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = k0 + 2 * j;
+                const uint32_t lo = (k < a.K) ? *gptr(a.x + (int64_t)b * a.ldx + k) : 0u;
+                const uint32_t hi = (k + 1 < a.K) ? *gptr(a.x + (int64_t)b * a.ldx + k + 1) : 0u;
+                t[j] = lo | (hi << 16);
             }
-        } else {
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                uint32_t t[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int k = k0 + 2 * j;
-                    const uint32_t lo = (k < a.K) ? *gptr(a.x + (int64_t)b * a.ldx + k) : 0u;
-                    const uint32_t hi = (k + 1 < a.K) ? *gptr(a.x + (int64_t)b * a.ldx + k + 1) : 0u;
-                    t[j] = lo | (hi << 16);
-                }
-                xv[b][0] = make_uint4(t[0], t[1], t[2], t[3]);
-                xv[b][1] = make_uint4(t[4], t[5], t[6], t[7]);
-            }
+            xv[b][0] = make_uint4(t[0], t[1], t[2], t[3]);
+            xv[b][1] = make_uint4(t[4], t[5], t[6], t[7]);
         }
         int8_chunk<B>(w, xv, acc);
     }
