@@ -588,27 +588,25 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int8_mfma(Int8Args a, int b)
             const int p = tid + i * 64 * W;
             const int col = p / PPC, ch = kk * CH * 64 + 8 * (p % PPC);
             const bool ok = col < b && ch < a.K;
-            uint4 v = load_x16((gx_ptr)(a.x + (ok ? (int64_t)col * a.ldx + ch : 0)));
-            if (ok && ch + 8 > a.K) {                 // the last piece of a row that ends inside it
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            r[i] = load_x16((gx_ptr)(a.x + (ok ? (int64_t)col * a.ldx + ch : 0)));
+        }
+    };
+    // pieces past the row (or past the batch) are zeroed here, when they are
+    // stored, so that no load is waited for as soon as it is issued
+    auto stage_store = [&](const uint4 (&r)[NPT], int buf, int k) {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int p = tid + i * 64 * W;
+            const int col = p / PPC, off = p % PPC, ch = k * CH * 64 + 8 * off;
+            if (col < b) {
+                uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (ch + 2 * j >= a.K) w[j] = 0;
                     else if (ch + 2 * j + 1 >= a.K) w[j] &= 0xFFFFu;
                 }
-                v = make_uint4(w[0], w[1], w[2], w[3]);
+                *(__attribute__((address_space(3))) u32x4*)&xs[buf][col][8 * off] = (u32x4){w[0], w[1], w[2], w[3]};
             }
-            r[i] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-    auto stage_store = [&](const uint4 (&r)[NPT], int buf) {
-#pragma unroll
-        for (int i = 0; i < NPT; ++i) {
-            const int p = tid + i * 64 * W;
-            const int col = p / PPC, off = p % PPC;
-            if (col < b)
-                *(__attribute__((address_space(3))) u32x4*)&xs[buf][col][8 * off] =
-                    (u32x4){r[i].x, r[i].y, r[i].z, r[i].w};
         }
     };
 
@@ -618,49 +616,75 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int8_mfma(Int8Args a, int b)
     auto group_of = [&](int j) { return (j / KC) * CH + s * KC + (j % KC); };
     const uint4* wld = a.codes + (int64_t)row * a.CPR + c;
 
+    // Loads are unconditional and go out in the order the loop keeps them in
+    // (chunk c issues the activation loads of chunk c + 2, then the window
+    // slots of chunk c + WC; the prologue plays chunks -WC .. -1), so every
+    // wait counts loads exactly and the window runs ahead across chunks.
+    // Without groups (K = 0 is refused by the entry points, so never) the
+    // window would reread row 0's first chunk.
+    constexpr int WC = P / KC;
     uint4 wq[P];
-    if (nchunks > 0) {
 #pragma unroll
-        for (int u = 0; u < P; ++u) wq[u] = gload_nt(wld + 4 * (u < J ? group_of(u) : 0));
-        stage_load(stg[0], 0);
-        stage_load(stg[1], 1);
-        stage_store(stg[0], 0);
+    for (int c2 = 0; c2 < 2 - WC; ++c2) {
+        stage_load(stg[c2], c2);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    for (int k0 = 0; k0 < nchunks; k0 += UNR) {
 #pragma unroll
-        for (int cb = 0; cb < UNR; ++cb) {
-            const int k = k0 + cb;
-            if (k < nchunks) {
-                stage_load(stg[cb & 1], k + 2);
+    for (int cp = -WC; cp < 0; ++cp) {
+        if (cp + 2 >= 0) {
+            stage_load(stg[(cp + 2) & 1], cp + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-                for (int kk = 0; kk < KC; ++kk) {
-                    const int u = (cb * KC + kk) % P;
-                    const int j = k * KC + kk;
-                    const bool gv = k * CH + s * KC + kk < G;
-                    const uint4 w = wq[u];
-                    wq[u] = gload_nt(wld + 4 * (j + P < J ? group_of(j + P) : 0));
-                    h2 p0, p1, p2, p3, p4, p5, p6, p7;
-                    int8_pairs(w.x, p0, p1);
-                    int8_pairs(w.y, p2, p3);
-                    int8_pairs(w.z, p4, p5);
-                    int8_pairs(w.w, p6, p7);
-                    const h8 A0 = (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-                    const h8 A1 = (h8){p4[0], p4[1], p5[0], p5[1], p6[0], p6[1], p7[0], p7[1]};
-                    const int gl = s * KC + kk;
-                    const lx_ptr xb = (lx_ptr)&xs[cb & 1][m][64 * gl + 16 * c];
-                    const h8 B0 = __builtin_bit_cast(h8, load_x16(xb));
-                    const h8 B1 = __builtin_bit_cast(h8, load_x16(xb + 8));
-                    if (gv) {
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B0, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B1, acc, 0, 0, 0);
-                    }
-                }
-                if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1);
-                lds_barrier();
-            }
+        for (int kk = 0; kk < KC; ++kk) {
+            const int j = (cp + WC) * KC + kk;
+            wq[j] = gload_nt(wld + 4 * (j < J ? group_of(j) : 0));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    if (nchunks > 0) stage_store(stg[0], 0, 0);
+    lds_barrier();
+    // one chunk; a slot is refilled after its products, into the same registers
+    auto chunk = [&](int k, int cb) {
+        stage_load(stg[cb & 1], k + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+            const int u = (cb * KC + kk) % P;
+            const int j = k * KC + kk;
+            const bool gv = k * CH + s * KC + kk < G;
+            const uint4 w = wq[u];
+            h2 p0, p1, p2, p3, p4, p5, p6, p7;
+            int8_pairs(w.x, p0, p1);
+            int8_pairs(w.y, p2, p3);
+            int8_pairs(w.z, p4, p5);
+            int8_pairs(w.w, p6, p7);
+            const h8 A0 = (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            const h8 A1 = (h8){p4[0], p4[1], p5[0], p5[1], p6[0], p6[1], p7[0], p7[1]};
+            const int gl = s * KC + kk;
+            const lx_ptr xb = (lx_ptr)&xs[cb & 1][m][64 * gl + 16 * c];
+            const h8 B0 = __builtin_bit_cast(h8, load_x16(xb));
+            const h8 B1 = __builtin_bit_cast(h8, load_x16(xb + 8));
+            if (gv) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B1, acc, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            wq[u] = gload_nt(wld + 4 * (j + P < J ? group_of(j + P) : 0));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1, k + 1);
+        lds_barrier();
+    };
+    const int whole = nchunks / UNR;
+    for (int it = 0; it < whole; ++it) {
+#pragma unroll
+        for (int cb = 0; cb < UNR; ++cb) chunk(it * UNR + cb, cb);
+    }
+    const int rest = nchunks - whole * UNR;
+#pragma unroll
+    for (int cb = 0; cb < UNR - 1; ++cb)
+        if (cb < rest) chunk(whole * UNR + cb, cb);
 
     // lane (c, m) holds rows 4c .. 4c + 3 of the tile, batch column m
     if (S > 1) {
@@ -813,93 +837,137 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
         sld[r] = reinterpret_cast<const uint2*>(a.scales) + ((int64_t)tb[r] * G4s + gbeg) * 4 + c;
     }
 
+    // Every load below is unconditional, so each wait counts loads exactly
+    // and the weight window keeps running ahead across chunk boundaries (a
+    // load skipped on some path makes the compiler count every later wait as
+    // if it had not been issued, which drained the window at each chunk).
+    // Without groups (an empty K range) the loads read the activation row.
+    const uint4* dummy = reinterpret_cast<const uint4*>(a.xp);
+    if (nchunks == 0)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            wld[r] = dummy;
+            sld[r] = reinterpret_cast<const uint2*>(dummy);
+        }
+    // The loads go out in the order the loop keeps them in: chunk c issues
+    // the activation loads of chunk c + 2 and then the window slots of chunk
+    // c + WC, so the prologue plays chunks -WC .. -1.  The wait counts at the
+    // loop head then hold for the first pass and for later ones alike.  The
+    // scheduling barriers keep the compiler from reordering the loads.
+    constexpr int WC = P / KC;                        // chunks the window spans
     uint4 wq[P][RB];
     uint2 sc[P][RB];
-    if (nchunks > 0) {                 // G4 > 0: group 0 exists
 #pragma unroll
-        for (int u = 0; u < P; ++u) {
-            const int g = u < J ? group_of(u) : 0;
+    for (int c2 = 0; c2 < 2 - WC; ++c2) {
+        stage_load(stg[c2], c2);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int cp = -WC; cp < 0; ++cp) {
+        if (cp + 2 >= 0) {
+            stage_load(stg[(cp + 2) & 1], cp + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+            const int j = (cp + WC) * KC + kk;
+            const int g = j < J ? group_of(j) : 0;
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                wq[u][r] = gload_nt(wld[r] + (int64_t)g * 64);
-                sc[u][r] = gload_u2(sld[r] + g * 4);
+                wq[j][r] = gload_nt(wld[r] + (int64_t)g * 64);
+                sc[j][r] = gload_u2(sld[r] + g * 4);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        stage_load(stg[0], 0);
-        stage_load(stg[1], 1);
-        stage_store(stg[0], 0, 0);
     }
-    __syncthreads();
+    if (nchunks > 0) stage_store(stg[0], 0, 0);
+    lds_barrier();
     const uint32_t bias = bias_reg();
-    for (int k0 = 0; k0 < nchunks; k0 += UNR) {
+    // one chunk: stage the loads of chunk k + 2, consume this wave's KC groups
+    // (a slot is refilled only after its group's products, so the refill
+    // lands in the same registers), write chunk k + 1 to the other buffer
+    auto chunk = [&](int k, int cb) {
+        stage_load(stg[cb & 1], k + 2);          // chunk k's registers are free again
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cb = 0; cb < UNR; ++cb) {
-            const int k = k0 + cb;     // k & 1 == cb & 1
-            if (k < nchunks) {
-                stage_load(stg[cb & 1], k + 2);          // chunk k's registers are free again
+        for (int kk = 0; kk < KC; ++kk) {
+            const int u = (cb * KC + kk) % P;
+            const int j = k * KC + kk;
+            const int g = k * CH + s * KC + kk;
+            const bool gv = g < G4;
+            h8 A[RB][4];
+            float sf[RB][4];
 #pragma unroll
-                for (int kk = 0; kk < KC; ++kk) {
-                    const int u = (cb * KC + kk) % P;
-                    const int j = k * KC + kk;
-                    const int g = k * CH + s * KC + kk;
-                    const bool gv = g < G4;
-                    const int gn = j + P < J ? group_of(j + P) : 0;
-                    h8 A[RB][4];
-                    float sf[RB][4];
+            for (int r = 0; r < RB; ++r) {
+                const uint32_t wd[4] = {wq[u][r].x, wq[u][r].y, wq[u][r].z, wq[u][r].w};
+                uint32_t s0 = sc[u][r].x, s1 = sc[u][r].y;
+                asm volatile("" : "+v"(s0), "+v"(s1));   // unpacked here, after the slot's wait
+                sf[r][0] = h_to_f((uint16_t)(s0 & 0xFFFF));
+                sf[r][1] = h_to_f((uint16_t)(s0 >> 16));
+                sf[r][2] = h_to_f((uint16_t)(s1 & 0xFFFF));
+                sf[r][3] = h_to_f((uint16_t)(s1 >> 16));
+                Int4Pairs pr[4];
 #pragma unroll
-                    for (int r = 0; r < RB; ++r) {
-                        const uint32_t wd[4] = {wq[u][r].x, wq[u][r].y, wq[u][r].z, wq[u][r].w};
-                        sf[r][0] = h_to_f((uint16_t)(sc[u][r].x & 0xFFFF));
-                        sf[r][1] = h_to_f((uint16_t)(sc[u][r].x >> 16));
-                        sf[r][2] = h_to_f((uint16_t)(sc[u][r].y & 0xFFFF));
-                        sf[r][3] = h_to_f((uint16_t)(sc[u][r].y >> 16));
-                        wq[u][r] = gload_nt(wld[r] + (int64_t)gn * 64);
-                        sc[u][r] = gload_u2(sld[r] + gn * 4);
-                        Int4Pairs pr[4];
+                for (int d = 0; d < 4; ++d) pr[d] = int4_pairs(wd[d], bias);
 #pragma unroll
-                        for (int d = 0; d < 4; ++d) pr[d] = int4_pairs(wd[d], bias);
-#pragma unroll
-                        for (int Pp = 0; Pp < 2; ++Pp) {
-                            const Int4Pairs& e0 = pr[2 * Pp];
-                            const Int4Pairs& e1 = pr[2 * Pp + 1];
-                            A[r][2 * Pp + 0] = (h8){e0.lo0[0], e0.lo0[1], e0.lo1[0], e0.lo1[1],
-                                                    e1.lo0[0], e1.lo0[1], e1.lo1[0], e1.lo1[1]};
-                            A[r][2 * Pp + 1] = (h8){e0.hi0[0], e0.hi0[1], e0.hi1[0], e0.hi1[1],
-                                                    e1.hi0[0], e1.hi0[1], e1.hi1[0], e1.hi1[1]};
-                        }
-                    }
-                    const int gl = s * KC + kk;  // group within the chunk
-#pragma unroll
-                    for (int t = 0; t < NBT; ++t) {
-                        h8 Bv[4];
-                        if (!HALF || m < COLS) {
-                            const lx_ptr xb = (lx_ptr)&xs[cb & 1][HALF ? m : 16 * t + m][128 * gl + 32 * c];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) Bv[q] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
-                        }
-#pragma unroll
-                        for (int r = 0; r < RB; ++r) {
-                            f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
-                            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][0], Bv[0], lo, 0, 0, 0);
-                            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][1], Bv[1], hi, 0, 0, 0);
-                            lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][2], Bv[2], lo, 0, 0, 0);
-                            hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][3], Bv[3], hi, 0, 0, 0);
-                            if (gv)
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    acc[r][t][i] = fmaf(sf[r][i], fmaf(hi[i], 0.0625f, lo[i]), acc[r][t][i]);
-                        }
-                    }
+                for (int Pp = 0; Pp < 2; ++Pp) {
+                    const Int4Pairs& e0 = pr[2 * Pp];
+                    const Int4Pairs& e1 = pr[2 * Pp + 1];
+                    A[r][2 * Pp + 0] = (h8){e0.lo0[0], e0.lo0[1], e0.lo1[0], e0.lo1[1],
+                                            e1.lo0[0], e1.lo0[1], e1.lo1[0], e1.lo1[1]};
+                    A[r][2 * Pp + 1] = (h8){e0.hi0[0], e0.hi0[1], e0.hi1[0], e0.hi1[1],
+                                            e1.hi0[0], e1.hi0[1], e1.hi1[0], e1.hi1[1]};
                 }
-                // chunk k + 1 (loaded during chunk k - 1) into the other buffer, last read in chunk k - 1
-                if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1, k + 1);
-                lds_barrier();
             }
+            const int gl = s * KC + kk;  // group within the chunk
+#pragma unroll
+            for (int t = 0; t < NBT; ++t) {
+                h8 Bv[4];
+                if (!HALF || m < COLS) {
+                    const lx_ptr xb = (lx_ptr)&xs[cb & 1][HALF ? m : 16 * t + m][128 * gl + 32 * c];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) Bv[q] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
+                    lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][0], Bv[0], lo, 0, 0, 0);
+                    hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][1], Bv[1], hi, 0, 0, 0);
+                    lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][2], Bv[2], lo, 0, 0, 0);
+                    hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][3], Bv[3], hi, 0, 0, 0);
+                    if (gv)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[r][t][i] = fmaf(sf[r][i], fmaf(hi[i], 0.0625f, lo[i]), acc[r][t][i]);
+                }
+            }
+            const int gn = j + P < J ? group_of(j + P) : 0;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                wq[u][r] = gload_nt(wld[r] + (int64_t)gn * 64);
+                sc[u][r] = gload_u2(sld[r] + gn * 4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // chunk k + 1 (loaded during chunk k - 1) into the other buffer, last read in chunk k - 1
+        if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1, k + 1);
+        lds_barrier();
+    };
+    // whole unrolled bodies first (k & 1 == cb & 1 and the slots of chunk k
+    // are fixed by cb), then the last nchunks % UNR chunks
+    const int whole = nchunks / UNR;
+    for (int it = 0; it < whole; ++it) {
+#pragma unroll
+        for (int cb = 0; cb < UNR; ++cb) chunk(it * UNR + cb, cb);
     }
+    const int rest = nchunks - whole * UNR;
+#pragma unroll
+    for (int cb = 0; cb < UNR - 1; ++cb)
+        if (cb < rest) chunk(whole * UNR + cb, cb);
 
     // FP16 outlier columns, 32 per k-step, split over the S waves of the tile;
     // up to four k-steps' loads in flight at once
