@@ -257,7 +257,7 @@ int woq_permute_x(const uint16_t* x, int64_t ldx, const int32_t* perm, int64_t b
  * in registers (the reconstruction step of "Open Origin - ELG Stream Layer",
  * fused into the product).  x fp16 [b, ldx], 16-byte aligned, ldx a multiple
  * of 8 and >= K; y fp16 [b, ldy], ldy >= N.  1 <= b <= 8 (b = 0 is a no-op).
- * The vector-ALU kernel runs, except for N >= 16384 at b >= 5 and N >= 8192
+ * The vector-ALU kernel runs, except for N >= 16384 at b >= 4 and N >= 8192
  * at b >= 7, where a matrix-core kernel runs (the faster one on MI355X).
  */
 int woq_qgemv_int8(const woq_int8_w* w, const uint16_t* x, int64_t ldx, int64_t b,

@@ -311,8 +311,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
     // 5. background groups.  A slot is consumed before its refill is issued,
     // so the refill can land in the same registers: with the old value still
     // live, the compiler moves refilled slots back at the loop latch, which
-    // waits for every load in flight once per window.  Rows that fit in one
-    // window take no refills at all.
+    // waits for every load in flight once per window.  The last window (the
+    // only one for rows that fit in one) takes no refills.
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
@@ -331,22 +331,20 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
         }
         int4o_row_chunk<B>(w, sc, xg, cg, acc);
     };
-    if (J <= P) {
+    int j0 = 0;
+    for (; j0 + P < J; j0 += P) {
 #pragma unroll
-        for (int u = 0; u < P; ++u)
-            if (u < J) consume(u, wq[u], sq[u]);
-    } else {
-        for (int j0 = 0; j0 < J; j0 += P) {
-#pragma unroll
-            for (int u = 0; u < P; ++u) {
-                const int j = j0 + u;
-                if (j < J) consume(j, wq[u], sq[u]);
-                const int gn = s + S * (j + P < J ? j + P : J - 1);
-                wq[u] = gload_nt(wb + (int64_t)gn * 64);
-                sq[u] = *gptr(sb + gn * 8);
-            }
+        for (int u = 0; u < P; ++u) {
+            const int j = j0 + u;
+            consume(j, wq[u], sq[u]);
+            const int gn = s + S * (j + P < J ? j + P : J - 1);
+            wq[u] = gload_nt(wb + (int64_t)gn * 64);
+            sq[u] = *gptr(sb + gn * 8);
         }
     }
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+        if (j0 + u < J) consume(j0 + u, wq[u], sq[u]);
 
     // 6. FP16 outlier columns: step st covers outlier chunks 4 st .. 4 st + 3
     // (lane chunk c); the first step's chunk was loaded with the window
@@ -400,11 +398,12 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
 // for every four rows and spends 2 dot2 per 4 weights per batch row, so its
 // time grows with b; the matrix-core kernel's time does not grow with b but
 // its wave loads cover 16 rows x 64 bytes, which streams slower.  The matrix
-// cores win on wide products from b = 5 (9B gate|up, 28672 x 3584: 30 vs
-// 62 us at b = 8) and on mid-size ones from b = 7; narrow ones stay on the vector ALU.
+// cores win on wide products from b = 4 (9B layer at b = 4, gate|up on the
+// matrix cores: 77.3 -> 74.1 us; at b = 3 the two are even) and on mid-size
+// ones from b = 7; narrow ones stay on the vector ALU.
 inline bool int8_use_mfma(int64_t N, int64_t b) {
     const int64_t tiles = (N + 15) / 16;
-    return (tiles >= 1024 && b >= 5) || (tiles >= 512 && b >= 7);
+    return (tiles >= 1024 && b >= 4) || (tiles >= 512 && b >= 7);
 }
 
 struct Int8Args {
