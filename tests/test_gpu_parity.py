@@ -228,6 +228,32 @@ def test_int4o_valu_ragged(gpu_lib, N, K, n_out, b):
     check(y, int4o_ref([W], perm, g.n_out, x), f"int4o {N}x{K} n_out={g.n_out} b={b}")
 
 
+# (rows, channels, groups per tile row, plan T x S): waves of 9, 9 or 8, 5, 8,
+# 18, 10, 17 and 16 groups
+@pytest.mark.parametrize("N,K,G4,plan", [(100, 4655, 36, "1x4"), (100, 8405, 68, "1x8"), (100, 2110, 20, "1x4"),
+                                         (100, 8275, 64, "1x8"), (16400, 4655, 36, "2x2"), (16400, 2100, 20, "2x2"),
+                                         (4100, 8405, 68, "1x4"), (300, 16529, 128, "1x8")])
+@pytest.mark.parametrize("b", [1, 2])
+def test_int4o_valu_window_lengths(gpu_lib, N, K, G4, plan, b):
+    """The vector kernel's weight window holds 8 groups per wave: rows whose
+    waves take fewer, exactly 8, 8 + 1, several whole windows, and whole
+    windows + a remainder, under each tile plan (T tiles x S waves): the last
+    window takes no refills, earlier ones refill each slot after using it."""
+    _print_case("int4o window", N, K, G4, plan, b)
+    rng = np.random.default_rng(N + 3 * K + b)
+    g = woq.woq_int4o_geometry(K)
+    assert g.G4 == G4
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x)
+    check(y, int4o_ref([W], perm, g.n_out, x), f"int4o window {N}x{K} G4={G4} plan {plan} b={b}")
+
+
 @pytest.mark.parametrize("N,K,n_out", [(16, 128, 0), (37, 300, 3), (130, 1000, -1), (64, 3072, -1), (20, 16, 16)])
 @pytest.mark.parametrize("b", [1, 8, 16, 17, 32, 64])
 def test_int4o_mfma_ragged(gpu_lib, N, K, n_out, b):
