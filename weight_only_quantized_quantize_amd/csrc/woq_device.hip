@@ -190,11 +190,12 @@ __device__ __forceinline__ void scatter8(uint16_t* xs, int xp_len, const uint4 (
 // activation rows are staged in LDS once per workgroup - copied from the
 // permuted row, or (GATHER) scattered from the natural-order row through the
 // channel-position table - while the first TILE_WINDOW groups of weights are
-// already in flight.  Weights and scales stream through a window of register
-// slots refilled unconditionally (past the last group the refill rereads it),
-// so every wait on a slot counts loads exactly.  Lane sums meet over the four
-// chunks with cross-lane shuffles and over the S waves in LDS, in a fixed
-// order.
+// already in flight.  Weights and scales stream through a window of
+// TILE_WINDOW register slots; every window but the last refills each slot
+// right after using it, unconditionally (past the last group the refill
+// rereads it), so every wait on a slot counts loads exactly.  Lane sums meet
+// over the four chunks with cross-lane shuffles and over the S waves in LDS,
+// in a fixed order.
 template <int B, int T, int S, bool GATHER>
 __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, GatherArgs ga) {
     extern __shared__ __align__(16) uint16_t xs[];   // [B][xp_len], then float corr[B][4 * G4]
