@@ -158,12 +158,14 @@ def test_int8_ragged(gpu_lib, N, K, b):
 
 
 @pytest.mark.parametrize("N,K,b", [(16389, 3000, 5), (16389, 3000, 8), (8200, 1000, 7), (8200, 1000, 8),
-                                   (28672, 3584, 6), (16384, 3584, 4), (8200, 1004, 6)])
+                                   (28672, 3584, 6), (16384, 3584, 4), (8200, 1004, 6), (16389, 1000, 4),
+                                   (16389, 1000, 3), (16389, 3500, 8), (8200, 3000, 8), (8200, 5000, 7)])
 def test_int8_matrix_core_sizes(gpu_lib, N, K, b):
-    """Products that run the matrix-core INT8 kernel (N >= 16384 from b = 5,
+    """Products that run the matrix-core INT8 kernel (N >= 16384 from b = 4,
     N >= 8192 from b = 7: ragged N and K, K not a multiple of 64, a last piece
-    that ends inside 8 channels) and neighbours on the vector kernel, on
-    sampled rows including the first and last."""
+    that ends inside 8 channels, K chunks that fill the unrolled loop body and
+    ones that leave a remainder under both plans) and neighbours on the vector
+    kernel, on sampled rows including the first and last."""
     _print_case("int8 mfma", N, K, b)
     rng = np.random.default_rng(N + K + b)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -391,6 +393,36 @@ def test_int4o_mfma_wide_batch_wide_product(gpu_lib, b, N, K):
     y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x)
     rows = np.concatenate([np.arange(16), np.sort(rng.choice(N, 200, replace=False)), np.arange(N - 16, N)])
     check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma wide b={b}")
+
+
+# (b, rows, channels): the matrix-core plan, then K chunks per row = whole
+# unrolled loop bodies + a remainder: T1S8 6 = 0 + 6; T1S8 (8 staged columns)
+# 7 = 4 + 3; T1S8, two column tiles 13 = 12 + 1; T2S4 6 = 4 + 2; T2S4, two
+# column tiles 25 = 24 + 1; T4S2 (8 staged columns) 7 = 6 + 1; T2S2, three
+# column tiles 22 = 20 + 2; T8S1 with two tiles per wave, two column tiles
+# 11 = 10 + 1, and one column tile 9 = 8 + 1
+@pytest.mark.parametrize("b,N,K", [(8, 200, 5600), (8, 200, 12800), (24, 200, 12800), (8, 5000, 5600),
+                                   (24, 5000, 12800), (8, 12000, 12800), (40, 12000, 5600), (32, 33000, 5600),
+                                   (8, 33000, 4500)])
+def test_int4o_mfma_chunk_remainders(gpu_lib, b, N, K):
+    """The matrix-core kernel runs whole unrolled bodies of K chunks and then
+    the remaining chunks one by one, with its loads issued in the same order
+    in the prologue as in the loop: every plan, with and without a remainder,
+    checked on sampled rows including the first and last."""
+    _print_case("int4o mfma chunks", b, N, K)
+    rng = np.random.default_rng(b + N + K)
+    g = woq.woq_int4o_geometry(K)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x, force_mfma=True)
+    rows = np.unique(np.concatenate([np.arange(16), np.sort(rng.choice(N, min(N, 150), replace=False)),
+                                     np.arange(N - 16, N)]))
+    check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma chunks b={b} {N}x{K}")
 
 
 @pytest.mark.parametrize("b,N,K", [(3, 6200, 8200), (5, 700, 28700), (8, 4100, 8300), (8, 700, 28700),
