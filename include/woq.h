@@ -286,10 +286,11 @@ int woq_embed_int8(const woq_int8_w* w, const int32_t* ids, int64_t b, uint16_t*
  * architecture diagram: the outlier GEMM and the fused background GEMM added
  * into one FP16 output).  xp from woq_permute_x (fp16 [b, xp_len]); y fp16
  * [b, ldy], ldy >= N.  The vector-ALU kernel runs for b <= 2, and for b <= 4
- * when N < 6144, if b * (2 * xp_len + 16 * G4) bytes (the staged activations
- * and a correction per 32-channel chunk) fit in 62 KB of LDS; otherwise the
- * matrix-core kernel (woq_qgemm_int4o) runs - on MI355X the faster of the two
- * in each case.  1 <= b <= 64 (b = 0 is a no-op).
+ * when N <= 6128 (fewer than 384 tiles of 16 rows), if b * (2 * xp_len +
+ * 16 * G4) bytes (the staged activations and a correction per 32-channel
+ * chunk) fit in 62 KB of LDS; otherwise the matrix-core kernel
+ * (woq_qgemm_int4o) runs - on MI355X the faster of the two in each case.
+ * 1 <= b <= 64 (b = 0 is a no-op).
  */
 int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
                     int64_t ldy, void* stream);
@@ -305,9 +306,9 @@ int woq_perm_positions(const int32_t* perm, const woq_int4o_geom* g, uint16_t* p
 /*
  * woq_permute_x and woq_qgemv_int4o in one launch - the same result bit for
  * bit wherever woq_qgemv_int4o runs its vector kernel (b <= 2, or b <= 4 when
- * N < 6144), the same values up to summation order where it runs the
- * matrix-core kernel: x is read in its natural channel order (fp16 [b, ldx], 16-byte
- * aligned, ldx a multiple of 8 and >= K) and scattered through pos (device
+ * N <= 6128), the same values up to summation order where it runs the
+ * matrix-core kernel: x is read in its natural channel order (fp16 [b, ldx],
+ * 16-byte aligned, ldx a multiple of 8 and >= K) and scattered through pos (device
  * copy of woq_perm_positions, 16-byte aligned) into the permuted, split row,
  * held in on-chip memory while the weights stream; this is the vector-ALU
  * kernel of woq_qgemv_int4o at any 1 <= b <= 4.  WOQ_EUNSUPPORTED unless
@@ -374,11 +375,13 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
 
 /*
  * Run every step once, in order, on `stream`: an INT4O step is one
- * woq_qgemv_int4o_x launch where folding the permutation into the product is
- * the faster form (the vector kernel serves the batch, K is a multiple of 8,
- * the input 16-byte aligned, N <= 16384 and b * xp_len <= 8704), otherwise
- * woq_permute_x followed by woq_qgemv_int4o; an INT8 step is one
- * woq_qgemv_int8 launch.  Both INT4O forms give the same bits.
+ * woq_qgemv_int4o_x launch wherever its vector kernel serves the batch and
+ * that form applies (woq_qgemv_int4o_x_supported, K a multiple of 8, the
+ * input 16-byte aligned), otherwise woq_permute_x followed by the matrix-core
+ * product (woq_qgemm_int4o; on rows of 128 groups or more at 3 <= b <= 32 its
+ * split-K form, woq_qgemm_int4o_splitk with 8 ranges and a runner-owned
+ * workspace, two launches); an INT8 step is one woq_qgemv_int8 launch.  The
+ * one-launch and two-launch vector forms give the same bits.
  * inputs[slot] are fp16 [b, K of the step]
  * activations (rows contiguous), outputs[slot] fp16 [b, N of the step].
  * 1 <= b <= max_b.  Asynchronous; the caller synchronises.
@@ -388,8 +391,8 @@ int woq_stack_run(woq_stack* st, const uint16_t* const* inputs, uint16_t* const*
 
 /*
  * Kernel launches of one woq_stack_run pass at batch b (a folded INT4O step
- * or an INT8 step is one launch, a permute-then-product INT4O step two),
- * assuming 16-byte aligned inputs.
+ * or an INT8 step is one launch, a permute-then-product INT4O step two, three
+ * with the split-K reduction), assuming 16-byte aligned inputs.
  */
 int woq_stack_launches(const woq_stack* st, int64_t b, int32_t* launches);
 
