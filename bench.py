@@ -41,6 +41,7 @@ def algorithmic_bytes(fmt: str, N: int, K: int, b: int) -> int:
 TRAFFIC_PROFILES = {
     # (config, runner, batch) -> committed counter summary of that workload
     (2, "launch", 1): "profiles/qgemv_int4o_tile__3b_int4o_stack_b1__traffic.md",
+    (3, "launch", 1): "profiles/qgemv_int8_valu__9b_int8_stack_b1__kernel_stats_traffic.md",
 }
 
 
