@@ -369,6 +369,19 @@ def main():
     ceiling = stream_read_ceiling(stream)
     result["roofline"]["stream_read_ceiling_gbs"] = round(ceiling, 1)
     result["roofline"]["frac_of_stream_ceiling"] = round(achieved / ceiling, 4)
+    if mode == "launch":
+        # what one launch costs before and after its own work, measured the
+        # way the products' launches are (an empty kernel of one workgroup of
+        # 256 threads per compute unit), and the launch duration a product
+        # would have if it streamed its bytes at the streaming-read rate on
+        # top of that
+        from weight_only_quantized_quantize_amd import woq
+        floor_us = woq.woq_dispatch_floor(256, 256, 200, stream)
+        per_launch = kernel_bytes / launches_per_step
+        model_us = floor_us + per_launch / (ceiling * 1e3)
+        result["roofline"]["dispatch_floor_us"] = round(floor_us, 3)
+        result["roofline"]["floor_plus_stream_us"] = round(model_us, 3)
+        result["roofline"]["frac_of_floor_plus_stream"] = round(model_us / (1e3 * kern_ms / launches_per_step), 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(spec, b)

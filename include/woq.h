@@ -554,6 +554,17 @@ int woq_pool_read_block(const char* path, int32_t i, void* dst, int64_t dst_byte
  */
 int woq_stream_read(const void* buf, int64_t bytes, void* stream);
 
+/*
+ * Launch `iters` empty kernels of `blocks` workgroups of `threads` threads
+ * back to back on `stream`, each with HIP events at its own dispatch
+ * boundaries (the events the stack runner's timing pass records around each
+ * product), and return their mean duration in microseconds: the time a launch
+ * costs before and after its own work, against which the products' launch
+ * durations are read.  Synchronises the stream.  1 <= blocks, 1 <= threads <=
+ * 1024, 1 <= iters <= 100000.
+ */
+int woq_dispatch_floor(int32_t blocks, int32_t threads, int32_t iters, void* stream, float* mean_us);
+
 #ifdef __cplusplus
 }
 #endif

@@ -123,3 +123,16 @@ def test_products_of_one_row_and_one_channel_group(gpu_lib):
         x_bg, x_out = O.permute_split(x, perm, g.n_out)
         err = O.normwise_rel_err(_host(y).astype(np.float64), O.linear_int4o(c, s, wo, x_bg, x_out))
         assert err <= 2e-3, (b, err)
+
+
+def test_dispatch_floor_measurement(gpu_lib):
+    """The empty-launch measurement: positive and finite, not longer than a
+    real product's launch, and argument errors reported."""
+    import torch
+    s = torch.cuda.current_stream()
+    floor = woq.woq_dispatch_floor(256, 256, 50, s)
+    assert 0.0 < floor < 1000.0, floor
+    for bad in ((0, 256, 10), (256, 0, 10), (256, 2048, 10), (256, 256, 0)):
+        with pytest.raises(woq.WoqError) as e:
+            woq.woq_dispatch_floor(*bad, s)
+        assert e.value.status == woq.WOQ_EINVAL

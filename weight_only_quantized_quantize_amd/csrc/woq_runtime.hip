@@ -401,6 +401,10 @@ int prepare_fused(woq_stack* st, int64_t b) {
     return WOQ_OK;
 }
 
+// A kernel that does nothing: its duration between the dispatch-boundary
+// events is the time any launch costs before and after its own work.
+__global__ void empty_kernel() {}
+
 }  // namespace
 
 namespace woq {
@@ -550,6 +554,29 @@ int woq_stack_time(woq_stack* st, const uint16_t* const* inputs, uint16_t* const
     for (auto& x : ev)
         if (x) (void)hipEventDestroy(x);
     if (rc) return rc;
+    return hip_status(e);
+}
+
+int woq_dispatch_floor(int32_t blocks, int32_t threads, int32_t iters, void* stream, float* mean_us) {
+    if (blocks < 1 || threads < 1 || threads > 1024 || iters < 1 || iters > 100000 || !mean_us) return WOQ_EINVAL;
+    std::vector<hipEvent_t> ev(2 * (size_t)iters, nullptr);
+    hipError_t e = hipSuccess;
+    for (auto& x : ev)
+        if (e == hipSuccess) e = hipEventCreate(&x);
+    hipStream_t hs = (hipStream_t)stream;
+    for (int it = 0; it < iters && e == hipSuccess; ++it)
+        e = hipExtLaunchKernel((const void*)&empty_kernel, dim3((unsigned)blocks), dim3((unsigned)threads), nullptr,
+                               0, hs, ev[2 * it], ev[2 * it + 1], 0);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    double total = 0.0;
+    for (int it = 0; it < iters && e == hipSuccess; ++it) {
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, ev[2 * it], ev[2 * it + 1]);
+        total += ms;
+    }
+    if (e == hipSuccess) *mean_us = (float)(1e3 * total / iters);
+    for (auto& x : ev)
+        if (x) (void)hipEventDestroy(x);
     return hip_status(e);
 }
 

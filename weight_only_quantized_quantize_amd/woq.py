@@ -85,6 +85,8 @@ _SIGS = {
     "woq_qgemm_int4o": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
     "woq_perm_positions": (c_int, [c_void_p, POINTER(Int4oGeom), c_void_p]),
     "woq_stream_read": (c_int, [c_void_p, c_int64, c_void_p]),
+    "woq_dispatch_floor": (c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, c_void_p,
+                                   ctypes.POINTER(ctypes.c_float)]),
     "woq_qgemv_int4o_x": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                   c_void_p]),
     "woq_qgemv_int4o_x_supported": (c_int, [POINTER(Int4oGeom), c_int64]),
@@ -361,6 +363,14 @@ def woq_qgemv_int4o_x(w: Int4oW, x, pos_dev, y, stream=None, b: int | None = Non
 def woq_stream_read(buf, stream=None):
     """Read every byte of a contiguous device tensor (size a multiple of 16)."""
     _check(_lib().woq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)), "woq_stream_read")
+
+
+def woq_dispatch_floor(blocks: int, threads: int, iters: int, stream=None) -> float:
+    """Mean duration (us) of `iters` empty launches of blocks x threads between
+    their dispatch-boundary events."""
+    out = ctypes.c_float()
+    _check(_lib().woq_dispatch_floor(blocks, threads, iters, _stream(stream), ctypes.byref(out)), "woq_dispatch_floor")
+    return float(out.value)
 
 
 def woq_qgemm_int4o_splitk(w: Int4oW, xp, y, splits: int, workspace, stream=None, b: int | None = None):
