@@ -433,7 +433,10 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
     const int nfull = a.K >> 4;            // chunks whose 16 channels are all real
     const int iters = (nfull + 63) >> 6;   // the same for every lane
     float acc[4][B];
+    float sx[B];
     zero_acc(acc);
+#pragma unroll
+    for (int b = 0; b < B; ++b) sx[b] = 0.0f;
     struct Buf {
         uint4 w[4];
         uint4 x[B][2];
@@ -459,7 +462,7 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
             xv[b][0] = real ? d.x[b][0] : z;
             xv[b][1] = real ? d.x[b][1] : z;
         }
-        int8_chunk<B>(d.w, xv, acc);
+        int8_chunk<B>(d.w, xv, acc, sx);
     };
     // the scheduling barriers keep each buffer's loads ahead of the other
     // buffer's waits (the scheduler would otherwise sink them below them)
@@ -503,8 +506,9 @@ __global__ __launch_bounds__(64) void qgemv_int8_valu(Int8Args a) {
             xv[b][0] = make_uint4(t[0], t[1], t[2], t[3]);
             xv[b][1] = make_uint4(t[4], t[5], t[6], t[7]);
         }
-        int8_chunk<B>(w, xv, acc);
+        int8_chunk<B>(w, xv, acc, sx);
     }
+    int8_unbias<B>(acc, sx);
     const float out = quad_reduce<B>(acc, lane);
     if (lane < 4 * B) {
         const int r = lane / B, b = lane % B;

@@ -172,15 +172,48 @@ __device__ __forceinline__ float activation_chunk_correction(const uint4 (&xv)[4
     return 1032.0f * sl + 72.0f * sh;
 }
 
-// Dot products of one INT8 chunk (four rows, 16 channels) with B activation rows.
+// INT8 products at b <= 2 run on the biased code values (code + 1152 as
+// fp16, one v_perm per pair and no subtraction); each lane also sums the
+// activations it multiplies, and int8_unbias removes 1152 times that sum once,
+// before the wave reduction.  The products stay exact; the cancellation costs
+// about 1e-5 of a lane's partial sum in fp32.  From b = 3 on, the dot
+// products per batch row outnumber the subtractions they save.
 template <int B>
-__device__ __forceinline__ void int8_chunk(const uint4 (&w)[4], const uint4 (&xv)[B][2], float (&acc)[4][B]) {
+constexpr bool int8_biased() { return B <= 2; }
+
+// fp16 pairs (channels 0,1 and 2,3) of an INT8 device dword, biased: code + 1152.
+__device__ __forceinline__ void int8_pairs_biased(uint32_t w, h2& a, h2& b) {
+    a = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00050004u));
+    b = as_h2(__builtin_amdgcn_perm(w, 0x64646464u, 0x00070006u));
+}
+
+// Dot products of one INT8 chunk (four rows, 16 channels) with B activation
+// rows; sx[b] accumulates the activations' sum where the codes stay biased.
+template <int B>
+__device__ __forceinline__ void int8_chunk(const uint4 (&w)[4], const uint4 (&xv)[B][2], float (&acc)[4][B],
+                                           float (&sx)[B]) {
+    constexpr bool BIASED = int8_biased<B>();
+    if constexpr (BIASED) {
+        const h2 one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const uint32_t xw[8] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
+                                    xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w};
+            float t = sx[b];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t = dot2(as_h2(xw[j]), one, t);
+            sx[b] = t;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
         h2 q[8];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) int8_pairs(wd[d], q[2 * d], q[2 * d + 1]);
+        for (int d = 0; d < 4; ++d) {
+            if constexpr (BIASED) int8_pairs_biased(wd[d], q[2 * d], q[2 * d + 1]);
+            else int8_pairs(wd[d], q[2 * d], q[2 * d + 1]);
+        }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             const uint32_t xw[8] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
@@ -190,6 +223,20 @@ __device__ __forceinline__ void int8_chunk(const uint4 (&w)[4], const uint4 (&xv
             for (int j = 0; j < 8; ++j) t = dot2(q[j], as_h2(xw[j]), t);
             acc[r][b] = t;
         }
+    }
+}
+
+// Remove the bias of int8_chunk's biased products (before the reduction) and
+// clear the activation sums.
+template <int B>
+__device__ __forceinline__ void int8_unbias(float (&acc)[4][B], float (&sx)[B]) {
+    if constexpr (int8_biased<B>()) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = fmaf(-1152.0f, sx[b], acc[r][b]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) sx[b] = 0.0f;
     }
 }
 
@@ -308,7 +355,7 @@ __device__ __forceinline__ void prefetch_items(const QuadTask& t, int lane, Slot
 // (row stride xstride).
 template <int B, class XPtr>
 __device__ __forceinline__ void consume_item(const QuadTask& t, int c, const uint4 (&w)[4], XPtr xs, int xstride,
-                                             float (&acc)[4][B]) {
+                                             float (&acc)[4][B], float (&sx)[B]) {
     if (c < t.nchunks) {
         uint4 xv[B][2];
 #pragma unroll
@@ -316,7 +363,7 @@ __device__ __forceinline__ void consume_item(const QuadTask& t, int c, const uin
             xv[b][0] = load_x16(xs + b * xstride + 16 * c);
             xv[b][1] = load_x16(xs + b * xstride + 16 * c + 8);
         }
-        int8_chunk<B>(w, xv, acc);
+        int8_chunk<B>(w, xv, acc, sx);
     }
 }
 
@@ -330,7 +377,10 @@ __device__ __forceinline__ void stream_task(const QuadTask& t, Slots<U>& s, XPtr
     const int T = t.nq * t.IT;
     if (issued < U) prefetch_items<U>(t, lane, s, issued, U);
     float acc[4][B];
+    float sx[B];
     zero_acc(acc);
+#pragma unroll
+    for (int b = 0; b < B; ++b) sx[b] = 0.0f;
     const int IT = t.IT > 0 ? t.IT : 1;
     ItemCursor use = {0, 0};
     ItemCursor nxt = {U / IT, U % IT};   // item U
@@ -339,10 +389,11 @@ __device__ __forceinline__ void stream_task(const QuadTask& t, Slots<U>& s, XPtr
         for (int u = 0; u < U; ++u) {
             const int item = t0 + u;
             if (item < T) {
-                consume_item<B>(t, lane + 64 * use.i, s.w[u], xs, xstride, acc);
+                consume_item<B>(t, lane + 64 * use.i, s.w[u], xs, xstride, acc, sx);
                 if (item + U < T) issue_item(t, nxt, lane, s.w[u]);
                 nxt.advance(IT);
                 if (use.i == IT - 1) {
+                    int8_unbias<B>(acc, sx);
                     emit(t.q0 + use.j * t.qstride, quad_reduce<B>(acc, lane));
                     zero_acc(acc);
                 }
