@@ -384,7 +384,10 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
  * one-launch and two-launch vector forms give the same bits.
  * inputs[slot] are fp16 [b, K of the step]
  * activations (rows contiguous), outputs[slot] fp16 [b, N of the step].
- * 1 <= b <= max_b.  Asynchronous; the caller synchronises.
+ * 1 <= b <= max_b.  Asynchronous; the caller synchronises.  Every run of
+ * one runner writes the same workspace (permuted activations, split-K
+ * partial sums), so runs of one runner must not overlap: issue them on one
+ * stream, or synchronise between streams.
  */
 int woq_stack_run(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
                   void* stream);
