@@ -159,13 +159,15 @@ def test_int8_ragged(gpu_lib, N, K, b):
 
 @pytest.mark.parametrize("N,K,b", [(16389, 3000, 5), (16389, 3000, 8), (8200, 1000, 7), (8200, 1000, 8),
                                    (28672, 3584, 6), (16384, 3584, 4), (8200, 1004, 6), (16389, 1000, 4),
-                                   (16389, 1000, 3), (16389, 3500, 8), (8200, 3000, 8), (8200, 5000, 7)])
+                                   (16389, 1000, 3), (16389, 3500, 8), (8200, 3000, 8), (8200, 5000, 7),
+                                   (28700, 1000, 8), (40000, 700, 5)])
 def test_int8_matrix_core_sizes(gpu_lib, N, K, b):
     """Products that run the matrix-core INT8 kernel (N >= 16384 from b = 4,
     N >= 8192 from b = 7: ragged N and K, K not a multiple of 64, a last piece
     that ends inside 8 channels, K chunks that fill the unrolled loop body and
-    ones that leave a remainder under both plans) and neighbours on the vector
-    kernel, on sampled rows including the first and last."""
+    ones that leave a remainder under every plan) and neighbours on the vector
+    kernel, on sampled rows including the first and last.  On 256 compute
+    units, 1025-1792 tiles run seven tiles per workgroup, 1794 and 2500 eight."""
     _print_case("int8 mfma", N, K, b)
     rng = np.random.default_rng(N + K + b)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -374,12 +376,16 @@ def test_batch_prefix_invariant(gpu_lib):
 
 
 @pytest.mark.parametrize("b,N,K", [(33, 32800, 200), (64, 32800, 200), (3, 32885, 1000), (8, 32885, 1000),
-                                   (20, 32885, 1000), (32, 32885, 1000)])
+                                   (20, 32885, 1000), (32, 32885, 1000), (8, 57344, 200), (8, 57400, 200),
+                                   (32, 57400, 200)])
 def test_int4o_mfma_wide_batch_wide_product(gpu_lib, b, N, K):
-    """The widest tile plan (N >= 32768 rows: eight waves per workgroup, two
-    tiles per wave for up to two column tiles, one for three and four), with a
-    ragged last workgroup and a partial last tile (N = 32885: 2056 tiles, the
-    last with 5 rows), checked on sampled rows including the first and last."""
+    """The widest tile plan (N >= 32768 rows: one wave per tile, two tiles
+    per wave for up to two column tiles, one for three and four; on 256
+    compute units seven waves per workgroup for up to two column tiles here,
+    eight for more, and eight from 3585 tiles), with a ragged last workgroup
+    and a partial last tile (N = 32885: 2056 tiles, the last with 5 rows;
+    N = 57400: 3588 tiles, the last with 8), checked on sampled rows
+    including the first and last."""
     _print_case("int4o mfma wide", b, N, K)
     rng = np.random.default_rng(b)
     g = woq.woq_int4o_geometry(K)
@@ -399,7 +405,7 @@ def test_int4o_mfma_wide_batch_wide_product(gpu_lib, b, N, K):
 # unrolled loop bodies + a remainder: T1S8 6 = 0 + 6; T1S8 (8 staged columns)
 # 7 = 4 + 3; T1S8, two column tiles 13 = 12 + 1; T2S4 6 = 4 + 2; T2S4, two
 # column tiles 25 = 24 + 1; T4S2 (8 staged columns) 7 = 6 + 1; T2S2, three
-# column tiles 22 = 20 + 2; T8S1 with two tiles per wave, two column tiles
+# column tiles 22 = 20 + 2; T7S1 with two tiles per wave, two column tiles
 # 11 = 10 + 1, and one column tile 9 = 8 + 1
 @pytest.mark.parametrize("b,N,K", [(8, 200, 5600), (8, 200, 12800), (24, 200, 12800), (8, 5000, 5600),
                                    (24, 5000, 12800), (8, 12000, 12800), (40, 12000, 5600), (32, 33000, 5600),

@@ -29,6 +29,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <mutex>
 
 namespace woq {
@@ -1109,6 +1110,32 @@ hipError_t launch_int8_valu(const Int8Args& a, int quads, hipStream_t s) {
     return launch_kernel(qgemv_int8_valu<B>, dim3(quads), dim3(64), 0, s, a);
 }
 
+// Compute units of the current device, read once per device.
+int compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The widest matrix-core plans put eight tiles (each of rb tiles per wave) in
+// a workgroup.  Where that grid leaves compute units idle and seven tiles
+// still give at most one workgroup per compute unit, seven spread the same
+// rows over more of them.  Measured on MI355X: the 70B gate|up product
+// (3584 tiles, two per wave) goes from 224 to 256 workgroups and the 70B
+// step at b = 8 from 9.92 to 9.80 ms (unchanged at b = 32); the 9B INT8
+// gate|up (1792 tiles) likewise, and the 9B step at b = 8 from 2.860 to
+// 2.790 ms.
+bool seven_tiles_fill(int tiles, int rb) {
+    const int cus = compute_units();
+    return woq::ceil_div(tiles, 8 * rb) < cus && woq::ceil_div(tiles, 7 * rb) <= cus;
+}
+
 template <int T, int S>
 hipError_t launch_int8_mfma_ts(const Int8Args& a, int b, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
@@ -1118,7 +1145,10 @@ hipError_t launch_int8_mfma_ts(const Int8Args& a, int b, hipStream_t s) {
 
 hipError_t launch_int8_mfma(const Int8Args& a, int b, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
-    if (tiles >= 1024) return launch_int8_mfma_ts<8, 1>(a, b, s);
+    if (tiles >= 1024) {
+        if (seven_tiles_fill(tiles, 1)) return launch_int8_mfma_ts<7, 1>(a, b, s);
+        return launch_int8_mfma_ts<8, 1>(a, b, s);
+    }
     return launch_int8_mfma_ts<2, 4>(a, b, s);
 }
 
@@ -1148,7 +1178,11 @@ hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_
 template <int NBT>
 hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
-    if (tiles >= 2048) return launch_int4o_mfma_ts<NBT, 8, 1, NBT <= 2 ? 2 : 1>(a, b, tiles, s);
+    if (tiles >= 2048) {
+        constexpr int RB = NBT <= 2 ? 2 : 1;
+        if (seven_tiles_fill(tiles, RB)) return launch_int4o_mfma_ts<NBT, 7, 1, RB>(a, b, tiles, s);
+        return launch_int4o_mfma_ts<NBT, 8, 1, RB>(a, b, tiles, s);
+    }
     if constexpr (NBT >= 3) {
         return launch_int4o_mfma_ts<NBT, 2, 2>(a, b, tiles, s);
     } else {
