@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the weight-only quantised linear stack on one MI355X.
 
-Default workload: the 3B-shaped outlier-INT4 decode stack (hidden 3072,
-intermediate 8192, 28 layers, 24 q / 8 kv heads of 128), batch 1, every weight
-resident in HBM.  One step = one decode pass through every linear of every
-layer (q|k|v, o, gate|up, down per layer; each with its input permutation).
+Default workload: the 70B-shaped outlier-INT4 decode stack (hidden 8192,
+intermediate 28672, 80 layers, 64 q / 8 kv heads of 128), batch 1, every
+weight resident in HBM.  One step = one decode pass through every linear of
+every layer (q|k|v, o, gate|up, down per layer, each with its input
+permutation), each product launched after the previous one has finished.
+``--config 2`` runs the 3B-shaped stack, ``--config 3`` the 9B-shaped INT8
+stack, ``--config 5`` the 9B INT8 stack streamed from pinned host memory and
+``--config 1`` the single INT8 4096 x 4096 linear.
 
 Prints one JSON line.  ``value`` is the achieved algorithmic bandwidth of the
 whole step (bytes the method must move per step / step time); ``decode_tok_s``
 is batch / step time.  ``roofline`` covers the dominant kernel (the product
-kernel), timed with HIP events on its own stream inside the timed region.
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+kernel, every launch of the step), timed with HIP events on the stream it is
+launched on.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -39,27 +44,28 @@ def algorithmic_bytes(fmt: str, N: int, K: int, b: int) -> int:
 
 
 TRAFFIC_PROFILES = {
-    # (config, runner, batch) -> committed counter summary of that workload
-    (2, "launch", 1): "profiles/qgemv_int4o_tile__3b_int4o_stack_b1__traffic.md",
-    (3, "launch", 1): "profiles/qgemv_int8_valu__9b_int8_stack_b1__kernel_stats_traffic.md",
+    # (config, batch) -> committed counter summary of that workload
+    (4, 1): "profiles/qgemv_int4o_tile__70b_int4o_stack_b1__traffic.md",
+    (2, 1): "profiles/qgemv_int4o_tile__3b_int4o_stack_b1__traffic.md",
+    (3, 1): "profiles/qgemv_int8_valu__9b_int8_stack_b1__kernel_stats_traffic.md",
 }
 
 
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("weight_only_quantized_quantize_amd/csrc/woq_gemv.cuh",
+    for f in ("weight_only_quantized_quantize_amd/csrc/woq_gemv.h",
               "weight_only_quantized_quantize_amd/csrc/woq_device.hip"):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg: int, mode: str, b: int):
+def measured_traffic(cfg: int, b: int):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None if there is none for this workload or the kernel sources
     changed since the counters were taken."""
-    path = TRAFFIC_PROFILES.get((cfg, mode, b))
+    path = TRAFFIC_PROFILES.get((cfg, b))
     if not path or not os.path.exists(os.path.join(ROOT, path)):
         return None
     fields = {}
@@ -73,11 +79,26 @@ def measured_traffic(cfg: int, mode: str, b: int):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(spec, b: int, prep_budget_s: float = 12.0, timed_s: float = 10.0):
-    """The oracle, untuned, on a bounded sample: the decode products of layer 0
-    (and more layers while the preparation budget lasts), run in timed passes
-    over those layers until about `timed_s` seconds of products have been
-    timed, scaled to a whole step."""
+def cpu_baseline(spec, b: int, timed_s: float = 10.0, max_rows: int = 1024):
+    """The oracle, untuned, on a bounded sample of the workload: the first
+    ``max_rows`` output rows (all of them where a linear has fewer) of every
+    linear of layer 0.
+
+    prep   - the oracle's encoding of the sample.  INT4O: per input space the
+             column sums of the sampled rows of every linear reading it, the
+             scores against the space's profile, the top-1% selection and the
+             permutation; per linear the group scales, codes, FP16 outlier
+             columns and the 2:1 packing.  INT8: the per-tensor scale and codes
+             of the sampled rows (the scale taken over the sample).
+    decode - the sample's products at batch b, the activations' permutation
+             and split included, repeated for about ``timed_s`` seconds.
+
+    ``value`` is the decode rate in algorithmic bytes per second (the metric's
+    unit), which a whole step would see; ``decode_tok_s`` is batch / the step
+    time at that rate.  The prep rate is in fp32 weight bytes encoded per
+    second.  Both run on all BLAS threads (elementwise NumPy is one thread);
+    ``value_one_core`` repeats one decode pass with BLAS limited to one thread.
+    """
     import numpy as np
     import oracle as O
     import synth
@@ -87,62 +108,77 @@ def cpu_baseline(spec, b: int, prep_budget_s: float = 12.0, timed_s: float = 10.
     except Exception:
         blas_threads = 1
     groups = ((("q", "k", "v"), 0), (("o",), 1), (("gate", "up"), 2), (("down",), 3))
+    Ws, rows = {}, {}
+    for lin in spec.linears():
+        R = min(lin.N, max_rows)
+        Ws[lin.name] = np.ascontiguousarray(synth.weight(spec, 0, lin)[:R])
+        rows[lin.name] = R
+    fp32_bytes = sum(W.nbytes for W in Ws.values())
 
-    def products(prepared):
-        for fmt, qw, perm, x, lin in prepared:
-            if fmt == "int4o":
-                x_bg, x_out = O.permute_split(x, perm, O.n_outliers(lin.K))
-                O.linear_int4o(*qw, x_bg, x_out)
-            else:
-                O.linear_int8(*qw, x)
+    # prep
+    t0 = time.perf_counter()
+    enc, perms = {}, {}
+    if spec.fmt == "int4o":
+        for space in sorted({lin.space for lin in spec.linears()}):
+            K = spec.space_width(space)
+            colabs = O.space_column_abs_sum(Ws[lin.name] for lin in spec.linears() if lin.space == space)
+            scores = O.outlier_scores(colabs, synth.profile(spec, space))
+            perms[space] = O.global_perm(K, O.select_outliers(scores, O.n_outliers(K)))
+        for lin in spec.linears():
+            c, sc, wo = O.quantize_int4o(Ws[lin.name], perms[lin.space], O.n_outliers(lin.K))
+            O.pack_int4(c)
+            enc[lin.name] = (c, sc, wo)
+    else:
+        for lin in spec.linears():
+            enc[lin.name] = O.quantize_int8(Ws[lin.name])
+    prep_s = time.perf_counter() - t0
+    del Ws
 
-    layers = []                       # (prepared products, algorithmic bytes) per sampled layer
-    t_start = time.perf_counter()
-    for layer in range(spec.layers):
-        prepared = []
+    xs = {inp: synth.decode_input(spec, 0, inp, b) for _, inp in groups}
+
+    def one_pass():
         for names, inp in groups:
-            x = synth.decode_input(spec, layer, inp, b)
-            for n in names:
-                lin = spec.linear(n)
-                W = synth.weight(spec, layer, lin)
-                if spec.fmt == "int4o":
-                    perm = O.global_perm(lin.K, synth.planted_set(spec, lin.space))
-                    prepared.append(("int4o", O.quantize_int4o(W, perm, O.n_outliers(lin.K)), perm, x, lin))
-                else:
-                    prepared.append(("int8", O.quantize_int8(W), None, x, lin))
-                del W
-        products(prepared)            # untimed first pass (page faults, thread-pool start)
-        layers.append((prepared, sum(algorithmic_bytes(fmt, lin.N, lin.K, b) for fmt, _, _, _, lin in prepared)))
-        if time.perf_counter() - t_start > prep_budget_s:
-            break
-    t_dec, passes, bytes_done = 0.0, 0, 0
+            x = xs[inp]
+            if spec.fmt == "int4o":
+                lin0 = spec.linear(names[0])
+                x_bg, x_out = O.permute_split(x, perms[lin0.space], O.n_outliers(lin0.K))
+                for n in names:
+                    O.linear_int4o(*enc[n], x_bg, x_out)
+            else:
+                for n in names:
+                    O.linear_int8(*enc[n], x)
+
+    sample_bytes = sum(algorithmic_bytes(spec.fmt, rows[lin.name], lin.K, b) for lin in spec.linears())
+    step_bytes = spec.layers * sum(algorithmic_bytes(spec.fmt, lin.N, lin.K, b) for lin in spec.linears())
+    one_pass()                                       # untimed (page faults, thread-pool start)
+    t_dec, passes = 0.0, 0
     while t_dec < timed_s:
-        for prepared, nbytes in layers:
-            t0 = time.perf_counter()
-            products(prepared)
-            t_dec += time.perf_counter() - t0
-            passes += 1
-            bytes_done += nbytes
-    step_s = t_dec / passes * spec.layers
-    per_step = bytes_done / passes * spec.layers
-    # the same products of layer 0 on one thread
+        t0 = time.perf_counter()
+        one_pass()
+        t_dec += time.perf_counter() - t0
+        passes += 1
+    rate = sample_bytes * passes / t_dec
     one_core = None
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            products(layers[0][0])
-            t1 = (time.perf_counter() - t0) * spec.layers
-        one_core = round(layers[0][1] * spec.layers / t1 / 1e9, 4)
+            one_pass()
+            one_core = round(sample_bytes / (time.perf_counter() - t0) / 1e9, 4)
     except ImportError:
         pass
-    return {"value": round(per_step / step_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle", "value_one_core": one_core,
-            "decode_tok_s": round(b / step_s, 5),
-            "sample": f"float64 NumPy oracle decode products of {len(layers)} of {spec.layers} layers at batch {b} "
-                      f"(weights quantised by the oracle outside the timing; each layer's products run once "
-                      f"untimed, then in {passes} timed layer passes), {t_dec:.1f} s timed, scaled to one step; "
-                      f"host os.cpu_count()={os.cpu_count()}, BLAS threads={blas_threads}"}
+    covered = sample_bytes / (step_bytes / spec.layers)
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "value_one_core": one_core,
+            "decode_tok_s": round(b / (step_bytes / rate), 5),
+            "prep_s": round(prep_s, 3), "prep_fp32_gbs": round(fp32_bytes / prep_s / 1e9, 4),
+            "decode_s": round(t_dec, 2), "decode_passes": passes,
+            "sample": f"float64 NumPy oracle on the first {max_rows} output rows (all rows of shorter linears) of "
+                      f"each of the 7 linears of layer 0 ({covered:.1%} of one layer's algorithmic bytes, "
+                      f"{1 / spec.layers:.2%} of the layers): prep (encoding, {fp32_bytes / 1e6:.0f} MB of fp32 "
+                      f"weights) timed once, {prep_s:.1f} s; decode products at batch {b} in {passes} timed passes, "
+                      f"{t_dec:.1f} s; the decode rate is scaled to a whole step; host os.cpu_count()="
+                      f"{os.cpu_count()}, BLAS threads={blas_threads}"}
 
 
 def stream_read_ceiling(stream, reps: int = 10) -> float:
@@ -225,13 +261,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="1: one INT8 4096x4096 linear; 2: 3B INT4O, 3: 9B INT8, 4: 70B INT4O (resident stacks); "
-                         "5: 9B INT8 streamed from pinned host memory")
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="4 (default): 70B INT4O, 2: 3B INT4O, 3: 9B INT8 (resident stacks); "
+                         "5: 9B INT8 streamed from pinned host memory; 1: one INT8 4096x4096 linear")
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="resident layers (default: all)")
-    ap.add_argument("--mode", choices=["fused", "launch"], default="launch",
-                    help="fused: one persistent launch per step; launch: one launch per permutation and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pool-roundtrip", action="store_true",
                     help="stacks 2-4: encode every layer, save the pool file under $TMPDIR, load it back, run a "
@@ -256,7 +290,7 @@ def main():
     import torch
     import synth
     from weight_only_quantized_quantize_amd import woq
-    from weight_only_quantized_quantize_amd.stack import ResidentStack
+    from weight_only_quantized_quantize_amd.stack import GROUPS, ResidentStack
 
     woq.require_gpu()
     if args.config == 1:
@@ -280,7 +314,7 @@ def main():
 
     inputs, outputs = [], []
     for layer in range(L):
-        for gi, (names, inp) in enumerate(((("q", "k", "v"), 0), (("o",), 1), (("gate", "up"), 2), (("down",), 3))):
+        for names, inp in GROUPS:
             x = synth.decode_input(spec, layer, inp, b)
             inputs.append(torch.from_numpy(x).cuda())
             N = sum(spec.linear(n).N for n in names)
@@ -291,51 +325,47 @@ def main():
 
     shapes = rs.group_shapes()
     step_bytes = sum(algorithmic_bytes(spec.fmt, N, K, b) for N, K, _ in shapes)
-
-    mode = args.mode
-    if mode == "fused":
-        try:
-            runner.run_fused(b, stream)
-            runner.check(stream)
-        except woq.WoqError as e:
-            if e.status != woq.WOQ_EUNSUPPORTED:
-                raise
-            log(f"fused pass unsupported here ({e}); timing the per-launch pass")
-            mode = "launch"
-    run = runner.run_fused if mode == "fused" else runner.run
     for _ in range(args.warmup):
-        run(b, stream)
+        runner.run(b, stream)
     torch.cuda.synchronize()
 
-    if mode == "fused":
-        # timed region: K fused launches, each bracketed by HIP events on the stream
-        t_start = time.perf_counter()
-        launch_ms = runner.time_fused(b, args.steps, stream)
-        wall = time.perf_counter() - t_start
-        kern_ms = launch_ms
-        kname = "stack_fused"
-        launches_per_step = 1
-        kernel_bytes = step_bytes
-    else:
-        # timed region: K passes without instrumentation
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for _ in range(args.steps):
-            run(b, stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_start
-        # product kernels: a second pass of K steps with HIP events around each product launch
-        step_ms, _ = runner.time(b, args.steps, stream)
-        kern_ms = sum(step_ms)
-        if spec.fmt == "int4o":
-            kname = "qgemv_int4o_tile" if b <= 4 else "qgemm_int4o_mfma"
-        else:
-            kname = "qgemv_int8_valu" if b < 4 else "qgemv_int8_valu + qgemm_int8_mfma (N >= 16384 at b >= 4, N >= 8192 at b >= 7)"
-        launches_per_step = len(shapes)
-        kernel_bytes = step_bytes
+    # timed region: K passes without instrumentation
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        runner.run(b, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    achieved = kernel_bytes / (kern_ms * 1e-3) / 1e9
+    # the same K passes with HIP events at every step's own dispatch
+    # boundaries (from the start of its first launch to the end of its last)
+    step_ms, pass_ms = runner.time(b, args.steps, stream)
+    launches = runner.launches(b)
+    kern_ms = sum(step_ms)
+    if spec.fmt == "int4o":
+        kname = ("qgemv_int4o_tile (vector kernel; permutation folded in)" if b <= 2 else
+                 "woq_permute_x + qgemm_int4o_mfma (+ split-K reduction)")
+    else:
+        kname = "qgemv_int8_valu" if b < 4 else "qgemv_int8_valu + qgemm_int8_mfma"
+    # Dispatch-boundary spans of consecutive launches overlap by part of the
+    # dispatch, so their sum can exceed the pass.  The per-launch figure is
+    # used only when it fits inside the measured step; otherwise the step
+    # itself is the kernel time (an upper bound on it).
+    if kern_ms <= ms_per_step:
+        basis, kernel_ms = "launch", kern_ms
+    else:
+        basis, kernel_ms = "step", ms_per_step
+    achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # per product of a layer: mean span over the layers and its rate
+    per_product = []
+    for gi, (names, _) in enumerate(GROUPS):
+        idx = range(gi, len(shapes), len(GROUPS))
+        N, K, _ = shapes[gi]
+        by = algorithmic_bytes(spec.fmt, N, K, b)
+        us = 1e3 * sum(step_ms[i] for i in idx) / len(idx)
+        per_product.append({"product": "|".join(names), "N": N, "K": K, "algorithmic_bytes": by,
+                            "mean_us": round(us, 3), "gbs": round(by / (us * 1e-6) / 1e9, 1),
+                            "frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -349,39 +379,43 @@ def main():
         "vs_baseline": None,
         "dtype": "f16xf16->f32 on int4 codes" if spec.fmt == "int4o" else "f16xf16->f32 on int8 codes",
         "data": "synthetic",
-        "config": {"workload": f"{spec.name}, batch {b}" + (f", {L} layers resident" if L != spec.layers else ""),
+        "config": {"workload": f"{spec.name}, batch {b}" + (f", {L} layers resident" if L != spec.layers else
+                                                            ", every layer resident in HBM"),
                    "format": spec.fmt, "layers": L, "hidden": spec.hidden, "intermediate": spec.inter,
                    "q_heads": spec.q_heads, "kv_heads": spec.kv_heads, "head_dim": spec.head_dim,
-                   "batch": b, "runner": mode,
-                   "launches_per_step": 1 if mode == "fused" else runner.launches(b),
+                   "batch": b, "launches_per_step": launches, "products_per_step": len(shapes),
                    "algorithmic_bytes_per_step": step_bytes},
         "decode_tok_s": round(b / (ms_per_step * 1e-3), 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.config, mode, b),
-                     "launches_per_step": launches_per_step,
-                     "mean_launch_us": round(1e3 * kern_ms / launches_per_step, 3),
-                     "mean_algorithmic_bytes_per_launch": kernel_bytes // launches_per_step},
+                     "traffic": measured_traffic(args.config, b),
+                     "basis": basis,
+                     "launches_per_step": launches,
+                     "sum_of_step_spans_ms": round(kern_ms, 5), "events_pass_ms": round(pass_ms, 5),
+                     "mean_launch_us": round(1e3 * kernel_ms / launches, 3),
+                     "mean_algorithmic_bytes_per_launch": step_bytes // launches,
+                     "per_product": per_product},
     }
     if spec.fmt == "int4o" and not args.no_vocab:
-        result["vocab"] = bench_vocab(args, spec, rs, b, run, stream, log)
+        result["vocab"] = bench_vocab(args, spec, rs, b, runner.run, stream, log)
     ceiling = stream_read_ceiling(stream)
     result["roofline"]["stream_read_ceiling_gbs"] = round(ceiling, 1)
     result["roofline"]["frac_of_stream_ceiling"] = round(achieved / ceiling, 4)
-    if mode == "launch":
-        # what one launch costs before and after its own work, measured the
-        # way the products' launches are (an empty kernel of one workgroup of
-        # 256 threads per compute unit), and the launch duration a product
-        # would have if it streamed its bytes at the streaming-read rate on
-        # top of that
-        from weight_only_quantized_quantize_amd import woq
-        floor_us = woq.woq_dispatch_floor(256, 256, 200, stream)
-        per_launch = kernel_bytes / launches_per_step
-        model_us = floor_us + per_launch / (ceiling * 1e3)
-        result["roofline"]["dispatch_floor_us"] = round(floor_us, 3)
-        result["roofline"]["floor_plus_stream_us"] = round(model_us, 3)
-        result["roofline"]["frac_of_floor_plus_stream"] = round(model_us / (1e3 * kern_ms / launches_per_step), 4)
+    # What a dependent launch costs before its own work, measured on an empty
+    # kernel of one 256-thread workgroup per compute unit: the mean interval of
+    # such launches back to back (no per-launch events).  The latency model of
+    # a step is one interval per launch plus the step's bytes at the
+    # streaming-read rate; the step reaches frac_of_interval_plus_stream of it.
+    span_us, interval_us = woq.woq_dispatch_floor(256, 256, 200, stream)
+    model_ms = launches * interval_us * 1e-3 + step_bytes / (ceiling * 1e9) * 1e3
+    result["roofline"]["empty_launch_span_us"] = round(span_us, 3)
+    result["roofline"]["empty_launch_interval_us"] = round(interval_us, 3)
+    result["roofline"]["interval_plus_stream_ms"] = round(model_ms, 5)
+    result["roofline"]["frac_of_interval_plus_stream"] = round(model_ms / ms_per_step, 4)
+    runner.close()
+    del rs
+    torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(spec, b)
@@ -523,11 +557,8 @@ def bench_prep(args, spec, log):
     if spec.fmt == "int4o":
         # the selector over this layer's linears (the stack selects over all layers)
         for sp in sorted({lin.space for lin in lins}):
-            acc = np.zeros(spec.space_width(sp))
-            for lin, W in zip(lins, Ws):
-                if lin.space == sp:
-                    woq.woq_colabs_accumulate(W, acc)
-            perms[sp] = woq.woq_outlier_select(acc, synth.profile(spec, sp))
+            perms[sp] = woq.woq_outlier_perm([W for lin, W in zip(lins, Ws) if lin.space == sp],
+                                             synth.profile(spec, sp))
     stream = torch.cuda.current_stream()
     dev_out, host_out = [], []
     Wd = [torch.from_numpy(W).cuda() for W in Ws]

@@ -35,6 +35,11 @@
  *    work.  Vector-loaded pointers must be 16-byte aligned (WOQ_EALIGN
  *    otherwise).  A launch failure returns WOQ_EHIP (see woq_last_hip_error);
  *    a fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - Buffer extents: a device entry point sees only pointers, so it cannot
+ *    check the size of a buffer.  Every activation or output buffer must hold
+ *    at least the b rows of its leading dimension that the call names (b * ld
+ *    fp16 values, the last row at least its used width); a shorter buffer is
+ *    read or written out of bounds by the kernel.
  *  - The library allocates no memory visible to the caller, except inside the
  *    opaque runtime objects, which own their buffers until destroyed.
  */
@@ -56,7 +61,6 @@ extern "C" {
 #define WOQ_EHIP         (-4)  /* a HIP call failed; woq_last_hip_error() gives its code */
 #define WOQ_EUNSUPPORTED (-5)  /* valid request that the library does not implement */
 #define WOQ_ERANGE       (-6)  /* value not representable: non-finite weight, fp16 scale overflow */
-#define WOQ_ETIMEOUT     (-7)  /* a fused stack run gave up waiting at a step boundary */
 #define WOQ_EIO          (-8)  /* a file could not be opened, read or written */
 #define WOQ_EFORMAT      (-9)  /* not a pool file, or a damaged one (magic, version, sizes or checksum) */
 
@@ -117,10 +121,33 @@ int woq_colabs_accumulate(const float* W, int64_t N, int64_t K, double* colsum);
  * colsum[j] in float64 (xprof fp16 [T, K], T >= 1); the n_out channels with the
  * largest score (ties to the lower index) are the outliers.  perm (int32 [K])
  * receives the background channels in ascending order followed by the outlier
- * channels in ascending order.  n_out < 0 selects ceil(K/100).
+ * channels in ascending order.  n_out < 0 selects ceil(K/100).  WOQ_ERANGE if
+ * a profile value or a score is not finite.
  */
 int woq_outlier_select(const double* colsum, const uint16_t* xprof, int64_t T, int64_t K,
                        int64_t n_out, int32_t* perm);
+
+/*
+ * The whole selection for one input space in one call (item 3's single table
+ * for the model): colsum = the sum over the n_lin linears that read the space
+ * (every layer) of their column sums sum_n |W_l[n, j]|, each linear's sum
+ * formed from zero in row order and the linears added in the order given,
+ * all in float64; then woq_outlier_select.  Ws[l] is float32 [Ns[l], K].
+ * Bit-identical to woq_outlier_perm_sums over woq_colabs_accumulate sums of
+ * the same linears, in the same order, each into a zeroed buffer.
+ */
+int woq_outlier_perm(const float* const* Ws, const int64_t* Ns, int32_t n_lin, int64_t K, const uint16_t* xprof,
+                     int64_t T, int64_t n_out, int32_t* perm);
+
+/*
+ * woq_outlier_perm for callers that cannot hold every weight of the space at
+ * once (a model generated or loaded layer by layer): parts[i] (float64 [K])
+ * are per-linear column sums, each from woq_colabs_accumulate into a zeroed
+ * buffer; they are added in the order given (parts[0] first), then the
+ * selection runs as woq_outlier_select.  n_parts >= 1.
+ */
+int woq_outlier_perm_sums(const double* const* parts, int32_t n_parts, int64_t K, const uint16_t* xprof,
+                          int64_t T, int64_t n_out, int32_t* perm);
 
 /*
  * Outlier-aware INT4 encoding of W (float32 [N, K], original channel order)
@@ -246,7 +273,8 @@ typedef struct {
  * xp[r, k] = x[r, perm[k]] for k < K_bg, 0 for K_bg <= k < 128*G4,
  * xp[r, 128*G4 + i] = x[r, perm[K_bg + i]] for i < n_out, 0 up to n_out8.
  * x fp16 [b, ldx] (ldx >= K), perm int32 [K] in device memory, xp fp16
- * [b, g->xp_len] (16-byte aligned).  b = 0 is a no-op.
+ * [b, g->xp_len] (16-byte aligned); x and xp must hold all b rows.  b = 0 is
+ * a no-op.
  */
 int woq_permute_x(const uint16_t* x, int64_t ldx, const int32_t* perm, int64_t b,
                   const woq_int4o_geom* g, uint16_t* xp, void* stream);
@@ -256,7 +284,8 @@ int woq_permute_x(const uint16_t* x, int64_t ldx, const int32_t* perm, int64_t b
  * fp32 accumulation, reading the INT8 codes once from HBM and converting them
  * in registers (the reconstruction step of "Open Origin - ELG Stream Layer",
  * fused into the product).  x fp16 [b, ldx], 16-byte aligned, ldx a multiple
- * of 8 and >= K; y fp16 [b, ldy], ldy >= N.  1 <= b <= 8 (b = 0 is a no-op).
+ * of 8 and >= K; y fp16 [b, ldy], ldy >= N; x and y must hold all b rows.
+ * 1 <= b <= 8 (b = 0 is a no-op).
  * The vector-ALU kernel runs, except for N >= 16384 at b >= 4 and N >= 8192
  * at b >= 7, where a matrix-core kernel runs (the faster one on MI355X).
  */
@@ -285,8 +314,8 @@ int woq_embed_int8(const woq_int8_w* w, const int32_t* ids, int64_t b, uint16_t*
  * with fp32 accumulation ("On-The-Fly Weight Synthesizer (OTF-LLM Engine)",
  * architecture diagram: the outlier GEMM and the fused background GEMM added
  * into one FP16 output).  xp from woq_permute_x (fp16 [b, xp_len]); y fp16
- * [b, ldy], ldy >= N.  The vector-ALU kernel runs for b <= 2, and for b <= 4
- * when N <= 6128 (fewer than 384 tiles of 16 rows), if b * (2 * xp_len +
+ * [b, ldy], ldy >= N; xp and y must hold all b rows.  The vector-ALU kernel
+ * runs for b <= 2, and for b <= 4 when N <= 6128 (fewer than 384 tiles of 16 rows), if b * (2 * xp_len +
  * 16 * G4) bytes (the staged activations and a correction per 32-channel
  * chunk) fit in 62 KB of LDS; otherwise the matrix-core kernel
  * (woq_qgemm_int4o) runs - on MI355X the faster of the two in each case.
@@ -308,7 +337,8 @@ int woq_perm_positions(const int32_t* perm, const woq_int4o_geom* g, uint16_t* p
  * bit wherever woq_qgemv_int4o runs its vector kernel (b <= 2, or b <= 4 when
  * N <= 6128), the same values up to summation order where it runs the
  * matrix-core kernel: x is read in its natural channel order (fp16 [b, ldx],
- * 16-byte aligned, ldx a multiple of 8 and >= K) and scattered through pos (device
+ * all b rows, 16-byte aligned, ldx a multiple of 8 and >= K; y as for
+ * woq_qgemv_int4o) and scattered through pos (device
  * copy of woq_perm_positions, 16-byte aligned) into the permuted, split row,
  * held in on-chip memory while the weights stream; this is the vector-ALU
  * kernel of woq_qgemv_int4o at any 1 <= b <= 4.  WOQ_EUNSUPPORTED unless
@@ -320,7 +350,8 @@ int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, cons
                       int64_t b, uint16_t* y, int64_t ldy, void* stream);
 int woq_qgemv_int4o_x_supported(const woq_int4o_geom* g, int64_t b);
 
-/* The matrix-core (MFMA) kernel of woq_qgemv_int4o for any 1 <= b <= 64. */
+/* The matrix-core (MFMA) kernel of woq_qgemv_int4o for any 1 <= b <= 64
+ * (xp and y as there: all b rows). */
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,
                     int64_t ldy, void* stream);
 
@@ -383,7 +414,9 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
  * workspace, two launches); an INT8 step is one woq_qgemv_int8 launch.  The
  * one-launch and two-launch vector forms give the same bits.
  * inputs[slot] are fp16 [b, K of the step]
- * activations (rows contiguous), outputs[slot] fp16 [b, N of the step].
+ * activations (rows contiguous), outputs[slot] fp16 [b, N of the step]; the
+ * two pointer arrays must have an entry for every slot a step names, and each
+ * buffer must hold those b rows (the runner sees pointers only).
  * 1 <= b <= max_b.  Asynchronous; the caller synchronises.  Every run of
  * one runner writes the same workspace (permuted activations, split-K
  * partial sums), so runs of one runner must not overlap: issue them on one
@@ -400,40 +433,18 @@ int woq_stack_run(woq_stack* st, const uint16_t* const* inputs, uint16_t* const*
 int woq_stack_launches(const woq_stack* st, int64_t b, int32_t* launches);
 
 /*
- * woq_stack_run repeated `iters` times with a pair of HIP events recorded on
- * `stream` around every product launch and around every pass.  On return
- * (the stream is synchronised) step_ms[i] (n_steps floats) holds the mean
- * duration of step i's product kernel and *pass_ms the mean duration of one
- * pass.  For measurement only; iters >= 1.
+ * woq_stack_run repeated `iters` times with a pair of HIP events around every
+ * step and around every pass.  A step's events take the dispatch timestamps
+ * of its own launches: the start of its first launch (the permutation, where
+ * one precedes the product) and the end of its last (the split-K reduction,
+ * where one follows).  On return (the stream is synchronised) step_ms[i]
+ * (n_steps floats) holds the mean duration of step i and *pass_ms the mean
+ * duration of one pass.  Dispatch-boundary spans of consecutive launches can
+ * overlap by part of the dispatch time, so the step durations may add up to
+ * a little more than the pass.  For measurement only; iters >= 1.
  */
 int woq_stack_time(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
                    void* stream, int32_t iters, float* step_ms, float* pass_ms);
-
-/*
- * The same pass as woq_stack_run in ONE persistent kernel launch: every
- * workgroup stays resident (cooperative launch), steps run in order, and a
- * device-side barrier separates consecutive steps, so no step starts its
- * products before every workgroup has finished the previous step.  Each step
- * stages its activations in LDS.  Supports stacks of INT8 steps with b <= 8;
- * a stack with an INT4O step, or a larger batch, returns WOQ_EUNSUPPORTED (use
- * woq_stack_run, which is also the faster pass on MI355X).  The barrier counters live in the
- * runner and are reset by the kernel itself before it exits, so consecutive
- * runs on one stream need no host action.  Runs of one runner must not
- * overlap (same stream, or synchronise).  A barrier that waits longer than a
- * fixed bound makes every workgroup exit early; woq_stack_check reports it.
- */
-int woq_stack_run_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
-                        void* stream);
-
-/* Synchronise `stream`; WOQ_ETIMEOUT if a fused run since the last check gave
- * up at a barrier (the flag is cleared), WOQ_OK otherwise. */
-int woq_stack_check(woq_stack* st, void* stream);
-
-/* woq_stack_run_fused repeated `iters` times, each launch bracketed by a pair
- * of HIP events on `stream`; *pass_ms = mean launch duration.  Synchronises,
- * then reports like woq_stack_check. */
-int woq_stack_time_fused(woq_stack* st, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
-                         void* stream, int32_t iters, float* pass_ms);
 
 /* Release the runner and its workspace (after the stream has finished). */
 int woq_stack_destroy(woq_stack* st);
@@ -558,15 +569,17 @@ int woq_pool_read_block(const char* path, int32_t i, void* dst, int64_t dst_byte
 int woq_stream_read(const void* buf, int64_t bytes, void* stream);
 
 /*
- * Launch `iters` empty kernels of `blocks` workgroups of `threads` threads
- * back to back on `stream`, each with HIP events at its own dispatch
- * boundaries (the events the stack runner's timing pass records around each
- * product), and return their mean duration in microseconds: the time a launch
- * costs before and after its own work, against which the products' launch
- * durations are read.  Synchronises the stream.  1 <= blocks, 1 <= threads <=
- * 1024, 1 <= iters <= 100000.
+ * Launch `iters` empty kernels of `blocks` workgroups of `threads` threads on
+ * `stream` twice over and report, in microseconds: *span_us, the mean time
+ * between each launch's own dispatch-boundary events (the events the stack
+ * runner's timing pass records around each step; consecutive spans overlap by
+ * part of the dispatch), and *interval_us, the mean time per launch when they
+ * run back to back with one pair of events around all of them (what each
+ * dependent launch adds to a pass before its own work).  Synchronises the
+ * stream.  1 <= blocks, 1 <= threads <= 1024, 1 <= iters <= 100000.
  */
-int woq_dispatch_floor(int32_t blocks, int32_t threads, int32_t iters, void* stream, float* mean_us);
+int woq_dispatch_floor(int32_t blocks, int32_t threads, int32_t iters, void* stream, float* span_us,
+                       float* interval_us);
 
 #ifdef __cplusplus
 }

@@ -97,6 +97,13 @@ def linear_int8(q: np.ndarray, s, x: np.ndarray) -> np.ndarray:
     return np.asarray(x, np.float64) @ dequantize_int8(q, s).T
 
 
+def linear_int8_abs(q: np.ndarray, s, x: np.ndarray) -> np.ndarray:
+    """sum_k |q[n, k] * s| * |x[b, k]| in float64 [b, N]: the scale of the
+    rounding error a floating-point evaluation of linear_int8 can make in
+    element (b, n) (the denominator of the componentwise error)."""
+    return np.abs(np.asarray(x, np.float64)) @ np.abs(dequantize_int8(q, s)).T
+
+
 def embed_int8(q: np.ndarray, s, ids) -> np.ndarray:
     """[OTF] item 4 (INT8 vocabulary tables) with the [ELG] "FP16 On-The-Fly
     GPU Reconstruction" applied to the looked-up rows.
@@ -142,6 +149,16 @@ def int4o_geometry(K: int, n_out: int | None = None, group: int = GROUP) -> dict
 def column_abs_sum(W: np.ndarray) -> np.ndarray:
     """sum_n |W[n, j]| in float64 for every input channel j of one linear."""
     return np.abs(np.asarray(W, np.float64)).sum(axis=0)
+
+
+def space_column_abs_sum(Ws) -> np.ndarray:
+    """[OTF] item 3 over a whole model: the float64 sum, over every linear in
+    ``Ws`` (all reading one input space, all layers), of column_abs_sum."""
+    Ws = list(Ws)
+    total = np.zeros(np.asarray(Ws[0]).shape[1], np.float64)
+    for W in Ws:
+        total = total + column_abs_sum(W)
+    return total
 
 
 def outlier_scores(colabs: np.ndarray, xprof: np.ndarray) -> np.ndarray:
@@ -261,6 +278,14 @@ def linear_int4o(codes, scales, w_out, x_bg, x_out, group: int = GROUP) -> np.nd
     return y_out + y_bg
 
 
+def linear_int4o_abs(codes, scales, w_out, x_bg, x_out, group: int = GROUP) -> np.ndarray:
+    """linear_int4o with every term taken in absolute value, float64 [b, N]:
+    sum_i |w_out[n, i] x_out[i]| + sum_k |deq[n, k] x_bg[k]|."""
+    y_bg = np.abs(np.asarray(x_bg, np.float64)) @ np.abs(dequantize_int4o(codes, scales, group)).T
+    y_out = np.abs(np.asarray(x_out, np.float64)) @ np.abs(np.asarray(w_out, np.float64)).T
+    return y_out + y_bg
+
+
 def reconstruct_int4o(codes, scales, w_out, perm, group: int = GROUP) -> np.ndarray:
     """The dequantised weight matrix in original channel order, float64 [N, K]."""
     N = codes.shape[0]
@@ -299,3 +324,17 @@ def normwise_rel_err(y, yref) -> float:
     if den == 0:
         return 0.0 if num == 0 else float("inf")
     return float(num / den)
+
+
+def componentwise_rel_err(y, yref, absref) -> float:
+    """max over the elements with absref > 0 of |y - yref| / absref, where
+    absref is the sum of the absolute terms of each output (linear_*_abs):
+    the componentwise relative error of a summation.  Elements whose terms are
+    all zero are left out (0 when none remain)."""
+    y = np.asarray(y, np.float64)
+    yref = np.asarray(yref, np.float64)
+    absref = np.asarray(absref, np.float64)
+    m = absref > 0
+    if not np.any(m):
+        return 0.0
+    return float(np.max(np.abs(y - yref)[m] / absref[m]))

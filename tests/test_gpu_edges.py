@@ -130,8 +130,9 @@ def test_dispatch_floor_measurement(gpu_lib):
     real product's launch, and argument errors reported."""
     import torch
     s = torch.cuda.current_stream()
-    floor = woq.woq_dispatch_floor(256, 256, 50, s)
-    assert 0.0 < floor < 1000.0, floor
+    span, interval = woq.woq_dispatch_floor(256, 256, 50, s)
+    assert 0.0 < span < 1000.0, span
+    assert 0.0 < interval < 1000.0, interval
     for bad in ((0, 256, 10), (256, 0, 10), (256, 2048, 10), (256, 256, 0)):
         with pytest.raises(woq.WoqError) as e:
             woq.woq_dispatch_floor(*bad, s)

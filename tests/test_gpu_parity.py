@@ -2,7 +2,13 @@
 
 Outputs are compared element by element with the float64 oracle on the same
 seeded inputs; the gate is the normwise relative error
-max|y - y_ref| / max|y_ref| <= 2e-3 (fp32 accumulation, fp16 output).  The
+max|y - y_ref| / max|y_ref| <= 2e-3 (fp32 accumulation, fp16 output).  Where
+the oracle also gives the sum of absolute terms A = sum_k |w_nk x_k| of every
+output, the componentwise error max |y - y_ref| / A is reported and held to
+2^-10: the fp16 rounding of the output contributes at most 2^-11 (|fp32 sum|
+<= A), and the fp32 accumulation of exact fp16 products (including the
+kernels' biased-code products and their once-per-chunk correction) is
+allowed as much again.  The
 permutation kernel is integer work and must match bit for bit.  Full-size
 shapes are checked on sampled output rows, which the oracle can compute one by
 one because every output row depends only on its own weight row.
@@ -17,6 +23,7 @@ from weight_only_quantized_quantize_amd import woq
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+CW_TOL = 2.0 ** -10
 
 
 def _dev(a):
@@ -53,8 +60,10 @@ def int8_case(W_parts, x):
     xd = _dev(xpad)
     y = _empty16(x.shape[0], dw.N)
     woq.woq_qgemv_int8(dw.desc, xd, y)
-    ref = np.concatenate([O.linear_int8(*O.quantize_int8(W), x) for W in W_parts], axis=1)
-    return _host(y).astype(np.float64), ref
+    qs = [O.quantize_int8(W) for W in W_parts]
+    ref = np.concatenate([O.linear_int8(*qw, x) for qw in qs], axis=1)
+    absref = np.concatenate([O.linear_int8_abs(*qw, x) for qw in qs], axis=1)
+    return _host(y).astype(np.float64), (ref, absref)
 
 
 def int4o_parts(W_list, perm, n_out):
@@ -99,19 +108,28 @@ def one_launch(dw, g, perm, x, ldx=None):
 
 
 def int4o_ref(W_list, perm, n_out, x):
+    """(oracle output, sum of absolute terms) of the linears in W_list, stacked along N."""
     x_bg, x_out = O.permute_split(x, perm, n_out)
-    ys = []
+    ys, abs_ = [], []
     for W in W_list:
         c, s, wo = O.quantize_int4o(W, perm, n_out)
         ys.append(O.linear_int4o(c, s, wo, x_bg, x_out))
-    return np.concatenate(ys, axis=1)
+        abs_.append(O.linear_int4o_abs(c, s, wo, x_bg, x_out))
+    return np.concatenate(ys, axis=1), np.concatenate(abs_, axis=1)
 
 
 def check(y, ref, what):
+    """ref is the oracle's output, or (output, sum of absolute terms)."""
+    absref = None
+    if isinstance(ref, tuple):
+        ref, absref = ref
     err = O.normwise_rel_err(y, ref)
-    print(f"{what}: normwise rel err {err:.3e}", flush=True)
+    cw = O.componentwise_rel_err(y, ref, absref) if absref is not None else None
+    print(f"{what}: normwise rel err {err:.3e}" + (f", componentwise {cw:.3e}" if cw is not None else ""), flush=True)
     assert np.all(np.isfinite(y)), what
     assert err <= TOL, (what, err)
+    if cw is not None:
+        assert cw <= CW_TOL, (what, "componentwise", cw)
     return err
 
 
@@ -181,7 +199,8 @@ def test_int8_matrix_core_sizes(gpu_lib, N, K, b):
     woq.woq_qgemv_int8(dw.desc, _dev(xpad), y)
     rows = np.concatenate([np.arange(16), np.sort(rng.choice(N, 100, replace=False)), np.arange(N - 16, N)])
     qo, so = O.quantize_int8(W, rows=rows)
-    check(_host(y)[:, rows].astype(np.float64), O.linear_int8(qo, so, x), f"int8 mfma {N}x{K} b={b}")
+    check(_host(y)[:, rows].astype(np.float64), (O.linear_int8(qo, so, x), O.linear_int8_abs(qo, so, x)),
+          f"int8 mfma {N}x{K} b={b}")
 
 
 def test_int8_fused_segments(gpu_lib):
@@ -208,7 +227,7 @@ def test_int8_config3_full_shapes_sampled(gpu_lib):
             woq.woq_qgemv_int8(dw.desc, _dev(x[:b]), y)
             rows = np.sort(rng.choice(lin.N, 64, replace=False))
             qo, so = O.quantize_int8(W, rows=rows)
-            ref = O.linear_int8(qo, so, x[:b])
+            ref = (O.linear_int8(qo, so, x[:b]), O.linear_int8_abs(qo, so, x[:b]))
             check(_host(y)[:, rows].astype(np.float64), ref, f"int8 cfg3 {lin.name} b={b}")
 
 
@@ -321,7 +340,8 @@ def test_int4o_full_shapes_sampled(gpu_lib, cfg):
             _print_case("int4o full", cfg, lin.name, lin.N, K, b)
             y, _ = int4o_run([part], g, perm, x[:b])
             x_bg, x_out = O.permute_split(x[:b], perm, g.n_out)
-            check(y[:, rows], O.linear_int4o(c, s, wo, x_bg, x_out), f"cfg{cfg} {lin.name} b={b}")
+            check(y[:, rows], (O.linear_int4o(c, s, wo, x_bg, x_out), O.linear_int4o_abs(c, s, wo, x_bg, x_out)),
+                  f"cfg{cfg} {lin.name} b={b}")
 
 
 @pytest.mark.parametrize("N,K,b,ldx", [(1, 8, 1, 8), (5, 300, 3, 320), (4100, 1000, 2, 1000 + 24),

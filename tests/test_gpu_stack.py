@@ -1,12 +1,11 @@
-"""GPU tests of the layer-stack runner (per-launch pass, and the fused
-persistent pass of INT8 stacks).
+"""GPU tests of the layer-stack runner.
 
 The runner's launches are the public entry points, so its outputs must equal
-those entry points composed by hand bit for bit; the fused INT8 pass uses the
-vector kernel's per-quad arithmetic and must agree bit for bit where the
-launches run the vector kernel too (b <= 2), within tolerance above.  Everything is also
-checked against the oracle, whose weights and permutations are computed by the
-oracle itself from the same seeded inputs.
+those entry points composed by hand bit for bit.  Everything is also checked
+against the oracle, whose weights and permutations are computed by the oracle
+itself from the same seeded inputs.  A chain of steps where each step reads
+the previous step's output (a real decode's dependency) checks that the
+runner's stream order delivers every output before the next product reads it.
 """
 import numpy as np
 import pytest
@@ -90,23 +89,6 @@ def test_small_stack_runner_equals_entry_points_and_oracle(gpu_lib, cfg, b):
     for _ in range(2):
         runner.run(b)
     ref_launch = [host(t).copy() for t in outs]
-    if spec.fmt == "int8":
-        for t in outs:
-            t.fill_(7.0)
-        for _ in range(3):                       # repeated runs: the barrier counters reset themselves
-            runner.run_fused(b)
-        runner.check()
-        for i, (a, t) in enumerate(zip(ref_launch, outs)):
-            if b < 3:
-                # both run the vector kernel's arithmetic: identical bits
-                np.testing.assert_array_equal(a.view(np.uint16), host(t).view(np.uint16), err_msg=f"fused step {i}")
-            else:
-                # the per-launch pass runs the matrix-core product from b = 3: summation order differs
-                assert O.normwise_rel_err(host(t).astype(np.float64), a.astype(np.float64)) <= TOL, f"fused step {i}"
-    else:
-        with pytest.raises(woq.WoqError) as e:   # the persistent pass streams INT8 only
-            runner.run_fused(b)
-        assert e.value.status == woq.WOQ_EUNSUPPORTED
     # the public entry points composed by hand give the same bits
     import torch
     for layer in range(spec.layers):
@@ -257,19 +239,64 @@ def test_config4_layers_full_size_every_batch(gpu_lib):
     runner.close()
 
 
-def test_fused_unsupported_batch_falls_back(gpu_lib):
-    spec = synth.small_stack_spec(2, layers=1, batches=(8,))
-    rs = build(spec)
-    ins, outs = io(spec, rs, 8)
-    runner = rs.make_runner(8)
-    runner.bind(ins, outs)
-    with pytest.raises(woq.WoqError) as e:
-        runner.run_fused(8)
-    assert e.value.status == woq.WOQ_EUNSUPPORTED
-    runner.run(8)                          # the per-launch pass takes the matrix-core kernel
-    perms = oracle_perms(spec)
-    ref = oracle_group(spec, perms, 0, ("q", "k", "v"), 0, 8)
-    assert O.normwise_rel_err(host(outs[0]).astype(np.float64), ref) <= TOL
+@pytest.mark.parametrize("fmt,b", [("int4o", 1), ("int4o", 2), ("int4o", 8), ("int8", 1), ("int8", 4)])
+def test_chained_steps_read_the_previous_output(gpu_lib, fmt, b):
+    """Six square linears (768 x 768) where step i reads slot i and writes
+    slot i + 1: each output is the next input.  Equal bit for bit to the entry
+    points called one by one, and each step within tolerance of the oracle
+    applied to the step's actual (GPU) input."""
+    import torch
+    _case("chained steps", fmt, b)
+    rng = np.random.default_rng(1234)
+    K = 768
+    steps, devs, refs = [], [], []
+    for i in range(6):
+        W = (rng.standard_normal((K, K)) * 0.05).astype(np.float32)
+        if fmt == "int4o":
+            g = woq.woq_int4o_geometry(K)
+            outs_ = np.sort(rng.choice(K, g.n_out, replace=False))
+            perm = O.global_perm(K, outs_)
+            dev = woq.DeviceInt4o([woq.woq_quantize_int4o(W, perm)], g)
+            perm_d = torch.from_numpy(perm).cuda()
+            devs.append((dev, perm_d))
+            steps.append(woq.step_int4o(dev, perm_d, i, i + 1))
+            refs.append(("int4o", O.quantize_int4o(W, perm, g.n_out), perm))
+        else:
+            dev = woq.DeviceInt8([woq.woq_quantize_int8(W)])
+            devs.append((dev, None))
+            steps.append(woq.step_int8(dev, i, i + 1))
+            refs.append(("int8", O.quantize_int8(W), None))
+    x0 = rng.standard_normal((b, K)).astype(np.float16)
+    slots = [torch.from_numpy(x0).cuda()] + [torch.full((b, K), 7.0, dtype=torch.float16, device="cuda")
+                                               for _ in range(6)]
+    runner = woq.Stack(steps, b)
+    runner.bind(slots, slots)
+    for _ in range(3):
+        runner.run(b)
+    got = [host(t).copy() for t in slots]
+    # the entry points one by one
+    y = [slots[0]]
+    for i, (dev, perm_d) in enumerate(devs):
+        out = torch.empty(b, K, dtype=torch.float16, device="cuda")
+        if fmt == "int4o":
+            xp = torch.empty(b, dev.geom.xp_len, dtype=torch.float16, device="cuda")
+            woq.woq_permute_x(y[-1], perm_d, dev.geom, xp)
+            woq.woq_qgemv_int4o(dev.desc, xp, out)
+        else:
+            woq.woq_qgemv_int8(dev.desc, y[-1], out)
+        y.append(out)
+    for i in range(1, 7):
+        np.testing.assert_array_equal(got[i].view(np.uint16), host(y[i]).view(np.uint16), err_msg=f"slot {i}")
+        kind, qw, perm = refs[i - 1]
+        xin = got[i - 1]
+        if kind == "int4o":
+            n_out = O.n_outliers(K)
+            ref = O.linear_int4o(*qw, *O.permute_split(xin, perm, n_out))
+        else:
+            ref = O.linear_int8(*qw, xin)
+        err = O.normwise_rel_err(got[i].astype(np.float64), ref)
+        assert err <= TOL, (i, err)
+    runner.close()
 
 
 def test_runner_launch_count(gpu_lib):

@@ -118,6 +118,52 @@ def test_outlier_select_matches_oracle_planted():
         np.testing.assert_array_equal(np.sort(perm[-O.n_outliers(K):]), synth.planted_set(spec, space))
 
 
+@pytest.mark.parametrize("cfg,layers", [(2, 2), (4, 1)])
+def test_outlier_perm_full_width_spaces_match_oracle(cfg, layers):
+    """The single-call selection (woq_outlier_perm over every linear of the
+    first layers that reads a space, full widths of the 3B- and 70B-shaped
+    stacks) is bit-identical to the oracle's selection over the same linears;
+    the per-linear sums form (woq_outlier_perm_sums) gives the same table."""
+    spec = synth.stack_spec(cfg)
+    for space in synth.SPACES:
+        K = spec.space_width(space)
+        Ws = [synth.weight(spec, layer, lin) for layer in range(layers) for lin in spec.linears()
+              if lin.space == space]
+        xprof = synth.profile(spec, space)
+        perm = woq.woq_outlier_perm(Ws, xprof)
+        parts = [woq.woq_colabs_accumulate(W, np.zeros(K)) for W in Ws]
+        np.testing.assert_array_equal(woq.woq_outlier_perm_sums(parts, xprof), perm)
+        co = O.space_column_abs_sum(Ws)
+        del Ws, parts
+        po = O.global_perm(K, O.select_outliers(O.outlier_scores(co, xprof), O.n_outliers(K)))
+        np.testing.assert_array_equal(perm, po, err_msg=f"cfg {cfg} space {space}")
+        np.testing.assert_array_equal(np.sort(perm[-O.n_outliers(K):]), synth.planted_set(spec, space))
+
+
+def test_outlier_perm_orders_and_errors():
+    """Hand case: the sums of two linears decide the selection (either alone
+    would pick another channel); argument errors are refused."""
+    K = 4
+    W1 = np.array([[9, 0, 1, 0]], np.float32)          # channel 0 alone would win
+    W2 = np.array([[0, 5, 1, 0], [0, 5, 1, 0]], np.float32)
+    xprof = np.array([[1, 1, 2, 1]], np.float16)       # channel 2 scores 2 * 2 = 4 x profile
+    # column sums: [9, 10, 3, 0]; scores: [9, 10, 6, 0] -> top-1 is channel 1
+    perm = woq.woq_outlier_perm([W1, W2], xprof, 1)
+    np.testing.assert_array_equal(perm, [0, 2, 3, 1])
+    assert woq.woq_outlier_perm([W1], xprof, 1)[-1] == 0
+    parts = [woq.woq_colabs_accumulate(W, np.zeros(K)) for W in (W1, W2)]
+    np.testing.assert_array_equal(woq.woq_outlier_perm_sums(parts, xprof, 1), perm)
+    L = woq.lib()
+    p = np.empty(K, np.int32)
+    xp = np.ascontiguousarray(xprof).view(np.uint16)
+    assert L.woq_outlier_perm(None, None, 0, K, xp.ctypes.data, 1, 1, p.ctypes.data) == woq.WOQ_EINVAL
+    assert L.woq_outlier_perm_sums(None, 0, K, xp.ctypes.data, 1, 1, p.ctypes.data) == woq.WOQ_EINVAL
+    bad = np.array([np.nan, 1, 1, 1], np.float64)
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_outlier_perm_sums([bad], xprof, 1)
+    assert e.value.status == woq.WOQ_ERANGE
+
+
 def test_outlier_select_ties_and_all_or_none():
     cs = np.array([3, 5, 5, 1, 5, 0], np.float64)
     xprof = np.ones((2, 6), np.float16)
@@ -403,6 +449,45 @@ def test_binding_refuses_batches_larger_than_buffers():
         woq.need_rows(8, x, y)
     with pytest.raises(ValueError):
         woq.woq_qgemv_int8(woq.Int8W(), x, y, b=8)
+
+
+def test_binding_refuses_unbound_or_mismatched_slots():
+    """Stack.bind / Pager.bind refuse, before any pointer reaches the library,
+    a slot list that misses a slot a step names, and a tensor that is not
+    fp16, not contiguous, not 2-D, not on the GPU, or not exactly as wide as
+    the step's input (K) or output (N)."""
+    import torch
+    widths = [(0, 64, 1, 32), (1, 32, 2, 48)]        # step 1 reads step 0's output
+
+    def t(r, c, **kw):
+        return torch.zeros(r, c, dtype=kw.get("dtype", torch.float16))
+
+    good_in = [t(2, 64), t(2, 32)]
+    good_out = [t(2, 8), t(2, 32), t(2, 48)]
+    good_out[1] = good_in[1]                        # the chained slot is one tensor
+    woq.check_slots(widths, good_in, good_out, device_type="cpu")
+    bad_cases = [
+        ([t(2, 64)], good_out),                                 # input slot 1 missing
+        (good_in, good_out[:2]),                                # output slot 2 missing
+        ([t(2, 64, dtype=torch.float32), good_in[1]], good_out),
+        ([t(2, 65), good_in[1]], good_out),                     # wider than K
+        ([t(2, 64), good_in[1]], [t(2, 8), good_in[1], t(2, 47)]),
+        ([t(2, 128)[:, ::2], good_in[1]], good_out),            # strided view
+        ([torch.zeros(128, dtype=torch.float16), good_in[1]], good_out),
+    ]
+    for ins, outs in bad_cases:
+        with pytest.raises(ValueError):
+            woq.check_slots(widths, ins, outs, device_type="cpu")
+    with pytest.raises(ValueError, match="not on the GPU"):
+        woq.check_slots(widths, good_in, good_out)
+    # the widths the binding derives from runner and pager steps
+    st = woq.StackStep()
+    st.fmt, st.in_slot, st.out_slot = woq.FMT_INT8, 3, 5
+    st.w8.N, st.w8.K = 48, 64
+    ps = woq.PagerStep()
+    ps.w.N, ps.w.K = 16, 24
+    assert woq.slot_widths([st]) == [(3, 64, 5, 48)]
+    assert woq.slot_widths([ps, ps]) == [(0, 24, 0, 16), (1, 24, 1, 16)]
 
 
 def test_decode_input_rows_for_any_batch():

@@ -395,3 +395,60 @@ def test_int4o_3b_footprint_matches_page_total():
 def test_normwise_error_helper():
     assert O.normwise_rel_err([1.0, 2.0], [1.0, 2.0]) == 0
     assert O.normwise_rel_err([1.0, 2.002], [1.0, 2.0]) == pytest.approx(1e-3)
+
+
+def test_space_column_sum_is_the_stacked_column_sum():
+    """Summing column_abs_sum over the linears of a space equals the column
+    sums of the linears stacked along N (integer-valued weights: exact)."""
+    rng = np.random.default_rng(11)
+    Ws = [rng.integers(-9, 10, (n, 13)).astype(np.float32) for n in (1, 4, 7)]
+    np.testing.assert_array_equal(O.space_column_abs_sum(Ws), O.column_abs_sum(np.concatenate(Ws)))
+    # a column whose signed sum cancels still counts its magnitude
+    W = np.array([[3, -1], [-3, 1]], np.float32)
+    np.testing.assert_array_equal(O.space_column_abs_sum([W, -W]), [12, 4])
+
+
+def test_absolute_term_sums_brute_force_and_special_cases():
+    """linear_*_abs against explicit loops over |w x| on tiny cases; for
+    non-negative codes, scales and activations they equal the products
+    themselves; flipping the sign of any activation leaves them unchanged."""
+    rng = np.random.default_rng(5)
+    # INT8
+    q = rng.integers(-127, 128, (3, 5)).astype(np.int8)
+    s = np.float32(0.03125)
+    x = rng.standard_normal((2, 5)).astype(np.float16)
+    want = np.zeros((2, 3))
+    for b in range(2):
+        for n in range(3):
+            want[b, n] = sum(abs(float(q[n, k]) * float(s) * float(x[b, k])) for k in range(5))
+    np.testing.assert_allclose(O.linear_int8_abs(q, s, x), want, rtol=1e-15)
+    qp = np.abs(q).astype(np.int8)
+    np.testing.assert_array_equal(O.linear_int8_abs(qp, s, np.abs(x)), O.linear_int8(qp, s, np.abs(x)))
+    flip = x * np.where(rng.random(5) < 0.5, -1, 1).astype(np.float16)
+    np.testing.assert_array_equal(O.linear_int8_abs(q, s, flip), O.linear_int8_abs(q, s, x))
+    # INT4O, K = 130 with 2 outliers: 128 background channels, one group
+    K, n_out = 130, 2
+    perm = O.global_perm(K, np.array([7, 99]))
+    W = rng.standard_normal((3, K)).astype(np.float32)
+    c, sc, wo = O.quantize_int4o(W, perm, n_out)
+    xf = rng.standard_normal((1, K)).astype(np.float16)
+    x_bg, x_out = O.permute_split(xf, perm, n_out)
+    got = O.linear_int4o_abs(c, sc, wo, x_bg, x_out)
+    for n in range(3):
+        t = sum(abs(float(c[n, k]) * float(sc[n, k // 128]) * float(x_bg[0, k])) for k in range(c.shape[1]))
+        t += sum(abs(float(wo[n, i]) * float(x_out[0, i])) for i in range(n_out))
+        assert got[0, n] == pytest.approx(t, rel=1e-14)
+    cp, scp, wop = np.abs(c).astype(np.int8), np.abs(sc), np.abs(wo)
+    np.testing.assert_allclose(O.linear_int4o_abs(cp, scp, wop, np.abs(x_bg), np.abs(x_out)),
+                               O.linear_int4o(cp, scp, wop, np.abs(x_bg), np.abs(x_out)), rtol=1e-15)
+    # always an upper bound of the product's magnitude
+    assert np.all(got >= np.abs(O.linear_int4o(c, sc, wo, x_bg, x_out)) * (1 - 1e-15))
+
+
+def test_componentwise_error_helper():
+    y = np.array([[1.0, 2.0, 0.0, 5.0]])
+    ref = np.array([[1.5, 2.0, 0.0, 4.0]])
+    absref = np.array([[10.0, 2.0, 0.0, 100.0]])
+    assert O.componentwise_rel_err(y, ref, absref) == pytest.approx(0.05)
+    assert O.componentwise_rel_err(ref, ref, absref) == 0.0
+    assert O.componentwise_rel_err(y[:, 2:3], ref[:, 2:3], absref[:, 2:3]) == 0.0   # no terms at all

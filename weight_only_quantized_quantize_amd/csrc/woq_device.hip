@@ -24,7 +24,7 @@
 // partial products added into one FP16 output).
 #include <hip/hip_runtime.h>
 
-#include "woq_gemv.cuh"
+#include "woq_gemv.h"
 #include "woq_internal.h"
 
 #include <hip/hip_ext.h>
@@ -1053,13 +1053,19 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     }
 }
 
-// Launch a kernel; with timing events set, through hipExtLaunchKernel so the
-// events take the dispatch's own start and end timestamps.
+// Launch a kernel; with timing events set (set_launch_events), through
+// hipExtLaunchKernel so the events take dispatch timestamps: the first launch
+// after the events were set records the start event at its own start (and
+// clears it), every launch records the stop event at its end, so a sequence of
+// launches (permutation, product, reduction) is bracketed as a whole.
 template <class K, class... A>
 hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, A... args) {
     void* argv[] = {(void*)&args...};
-    if (woq::g_ev_start)
-        return hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, s, woq::g_ev_start, woq::g_ev_stop, 0);
+    if (woq::g_ev_start || woq::g_ev_stop) {
+        hipEvent_t start = woq::g_ev_start;
+        woq::g_ev_start = nullptr;
+        return hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, s, start, woq::g_ev_stop, 0);
+    }
     return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, s);
 }
 
@@ -1256,9 +1262,9 @@ int woq_permute_x(const uint16_t* x, int64_t ldx, const int32_t* perm, int64_t b
     if (b > 65535 || g->xp_len > INT32_MAX) return WOQ_EUNSUPPORTED;
     const int threads = 256;
     int blocks = (int)std::min<int64_t>(woq::ceil_div(g->xp_len, threads), 1024);
-    hipLaunchKernelGGL(permute_x_kernel, dim3(blocks, (unsigned)b), dim3(threads), 0, (hipStream_t)stream, x, ldx,
-                       perm, (int)g->K, (int)g->K_bg, (int)g->n_out, (int)(128 * g->G4), (int)g->xp_len, xp);
-    return launch_status(hipGetLastError());
+    return launch_status(launch_kernel(permute_x_kernel, dim3(blocks, (unsigned)b), dim3(threads), 0,
+                                       (hipStream_t)stream, x, ldx, perm, (int)g->K, (int)g->K_bg, (int)g->n_out,
+                                       (int)(128 * g->G4), (int)g->xp_len, xp));
 }
 
 int woq_qgemv_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy, void* stream) {
@@ -1335,9 +1341,8 @@ int woq_qgemm_int4o_splitk(const woq_int4o_w* w, const uint16_t* xp, int64_t b, 
     hipError_t e = launch_int4o_mfma_split(a, (int)b, splits, s);
     if (e == hipSuccess) {
         const int64_t n = b * w->N;
-        hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)woq::ceil_div(n, 256)), dim3(256), 0, s,
-                           (const float*)workspace, (int)splits, (int)b, (int)w->N, y, (int)ldy);
-        e = hipGetLastError();
+        e = launch_kernel(reduce_splits_kernel, dim3((unsigned)woq::ceil_div(n, 256)), dim3(256), 0, s,
+                          (const float*)workspace, (int)splits, (int)b, (int)w->N, y, (int)ldy);
     }
     return launch_status(e);
 }

@@ -1,5 +1,5 @@
-// Device building blocks shared by the single-launch kernels and the
-// persistent stack kernel: the per-quad dequantise-and-dot loops.
+// Device building blocks shared by the product kernels: code unpacking,
+// the dequantise-and-dot inner loops and the cross-lane reductions.
 //
 // A "quad" is four consecutive output rows handled by one wave.  Lane l owns
 // the 16-byte chunks l, l + 64, ... of each of the four rows (a chunk is 32
@@ -289,118 +289,6 @@ __device__ __forceinline__ float sum_over_chunks(float v) {
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     return v;
-}
-
-// ---------------------------------------------------------------------------
-// Pipelined streaming of a wave's INT8 quads.
-//
-// A wave owns quads q0, q0 + qstride, ... (nq of them).  Each quad is a
-// sequence of chunk iterations: iteration i covers the 16-byte chunk
-// c = lane + 64 i of each of the quad's four rows, c < nchunks.  The wave
-// walks the flat sequence of (quad, iteration) items through a window of U
-// register slots: the loads of item t + U are issued as soon as item t has
-// been consumed, so U items are always in flight.  The first items can be
-// issued early (prefetch) because the weights do not depend on the
-// activations.
-//
-// Loads are issued unconditionally: a lane whose chunk lies outside the row
-// reads a valid dummy address and ignores the result, so no slot register is
-// written on a divergent path (merging such writes would force a wait for the
-// load).
-struct QuadTask {
-    const uint4* codes;      // quad-major rows of CPR chunks
-    int CPR, nchunks;        // chunks per row; chunks holding real columns
-    int q0, qstride, nq, IT; // IT: iterations per quad
-};
-
-template <int U>
-struct Slots {
-    uint4 w[U][4];
-};
-
-// Cursor over (quad, iteration) items.
-struct ItemCursor {
-    int j, i;
-    __device__ __forceinline__ void advance(int IT) {
-        if (++i == IT) {
-            i = 0;
-            ++j;
-        }
-    }
-};
-
-__device__ __forceinline__ void issue_item(const QuadTask& t, ItemCursor cur, int lane, uint4 (&w)[4]) {
-    const int q = t.q0 + cur.j * t.qstride;
-    const int c = lane + 64 * cur.i;
-    const bool ok = c < t.nchunks;
-    const uint4* base = ok ? t.codes + ((int64_t)q * 4 * t.CPR + c) : t.codes;
-    const int rs = ok ? t.CPR : 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = gload_nt(base + r * rs);
-}
-
-// Issue items [from, to) of the window (to <= U), counting from item 0.
-template <int U>
-__device__ __forceinline__ void prefetch_items(const QuadTask& t, int lane, Slots<U>& s, int from = 0, int to = U) {
-    const int T = t.nq * t.IT;
-    ItemCursor cur = {0, 0};
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (u >= from && u < to && u < T) issue_item(t, cur, lane, s.w[u]);
-        cur.advance(t.IT);
-    }
-}
-
-// Consume the item in slot w: chunk c of the quad; xs holds the activations
-// (row stride xstride).
-template <int B, class XPtr>
-__device__ __forceinline__ void consume_item(const QuadTask& t, int c, const uint4 (&w)[4], XPtr xs, int xstride,
-                                             float (&acc)[4][B], float (&sx)[B]) {
-    if (c < t.nchunks) {
-        uint4 xv[B][2];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            xv[b][0] = load_x16(xs + b * xstride + 16 * c);
-            xv[b][1] = load_x16(xs + b * xstride + 16 * c + 8);
-        }
-        int8_chunk<B>(w, xv, acc, sx);
-    }
-}
-
-// Stream every item of the task; slots must hold the first `issued` items
-// already issued (prefetch_items); the rest of the window is issued here.
-// emit(quad, out) is called once per quad with the wave-reduced sums (lane
-// r * B + b holds row r, batch row b).
-template <int B, int U, class XPtr, class Emit>
-__device__ __forceinline__ void stream_task(const QuadTask& t, Slots<U>& s, XPtr xs, int xstride, int lane,
-                                            int issued, Emit&& emit) {
-    const int T = t.nq * t.IT;
-    if (issued < U) prefetch_items<U>(t, lane, s, issued, U);
-    float acc[4][B];
-    float sx[B];
-    zero_acc(acc);
-#pragma unroll
-    for (int b = 0; b < B; ++b) sx[b] = 0.0f;
-    const int IT = t.IT > 0 ? t.IT : 1;
-    ItemCursor use = {0, 0};
-    ItemCursor nxt = {U / IT, U % IT};   // item U
-    for (int t0 = 0; t0 < T; t0 += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int item = t0 + u;
-            if (item < T) {
-                consume_item<B>(t, lane + 64 * use.i, s.w[u], xs, xstride, acc, sx);
-                if (item + U < T) issue_item(t, nxt, lane, s.w[u]);
-                nxt.advance(IT);
-                if (use.i == IT - 1) {
-                    int8_unbias<B>(acc, sx);
-                    emit(t.q0 + use.j * t.qstride, quad_reduce<B>(acc, lane));
-                    zero_acc(acc);
-                }
-                use.advance(IT);
-            }
-        }
-    }
 }
 
 }  // namespace woqk

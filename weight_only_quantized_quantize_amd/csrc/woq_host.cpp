@@ -109,7 +109,6 @@ const char* woq_strerror(int status) {
         case WOQ_EHIP: return "HIP runtime error";
         case WOQ_EUNSUPPORTED: return "unsupported request";
         case WOQ_ERANGE: return "value out of range (non-finite weight or fp16 scale overflow)";
-        case WOQ_ETIMEOUT: return "timed out waiting at a step boundary";
         case WOQ_EIO: return "file input/output error";
         case WOQ_EFORMAT: return "not a pool file, or a damaged one";
         default: return "unknown status";
@@ -226,6 +225,44 @@ int woq_outlier_select(const double* colsum, const uint16_t* xprof, int64_t T, i
     for (int64_t j = 0; j < K; ++j)
         if (is_out[j]) perm[p++] = (int32_t)j;
     return WOQ_OK;
+}
+
+int woq_outlier_perm_sums(const double* const* parts, int32_t n_parts, int64_t K, const uint16_t* xprof,
+                          int64_t T, int64_t n_out, int32_t* perm) {
+    if (!parts || n_parts < 1 || K < 1 || !xprof || !perm || T < 1) return WOQ_EINVAL;
+    for (int32_t i = 0; i < n_parts; ++i)
+        if (!parts[i]) return WOQ_EINVAL;
+    // the parts in the order given, channel by channel (the split over
+    // threads decides only which thread adds which channels)
+    std::vector<double> total((size_t)K, 0.0);
+    woq::parallel_for(
+        K,
+        [&](int64_t c0, int64_t c1) {
+            for (int32_t i = 0; i < n_parts; ++i) {
+                const double* p = parts[i];
+                for (int64_t j = c0; j < c1; ++j) total[j] += p[j];
+            }
+        },
+        256);
+    return woq_outlier_select(total.data(), xprof, T, K, n_out, perm);
+}
+
+int woq_outlier_perm(const float* const* Ws, const int64_t* Ns, int32_t n_lin, int64_t K, const uint16_t* xprof,
+                     int64_t T, int64_t n_out, int32_t* perm) {
+    if (!Ws || !Ns || n_lin < 1 || K < 1 || !xprof || !perm || T < 1) return WOQ_EINVAL;
+    for (int32_t i = 0; i < n_lin; ++i)
+        if (Ns[i] < 0 || (Ns[i] > 0 && !Ws[i])) return WOQ_EINVAL;
+    // each linear's column sums from zero, then the same ordered addition as
+    // woq_outlier_perm_sums
+    std::vector<std::vector<double>> sums((size_t)n_lin);
+    std::vector<const double*> parts((size_t)n_lin);
+    for (int32_t i = 0; i < n_lin; ++i) {
+        sums[i].assign((size_t)K, 0.0);
+        const int rc = woq_colabs_accumulate(Ws[i], Ns[i], K, sums[i].data());
+        if (rc) return rc;
+        parts[i] = sums[i].data();
+    }
+    return woq_outlier_perm_sums(parts.data(), n_lin, K, xprof, T, n_out, perm);
 }
 
 int woq_quantize_int4o(const float* W, int64_t N, int64_t K, const int32_t* perm, int64_t n_out,

@@ -10,7 +10,7 @@
 // does not depend on how the work is split.
 #include <hip/hip_runtime.h>
 
-#include "woq_gemv.cuh"
+#include "woq_gemv.h"
 #include "woq_internal.h"
 
 namespace {

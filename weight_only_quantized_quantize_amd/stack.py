@@ -83,11 +83,9 @@ class _QuantisedStack:
             sums = _map_weights(spec, jobs, weight_fn, colsum, self.threads)
             for space in spaces:
                 K = spec.space_width(space)
-                acc = np.zeros(K)
-                for (layer, lin), cs in zip(jobs, sums):      # fixed (layer, linear) order
-                    if lin.space == space:
-                        acc += cs
-                perm = woq.woq_outlier_select(acc, profile_fn(space))
+                # the library adds the per-linear sums in (layer, linear) order and selects
+                parts = [cs for (layer, lin), cs in zip(jobs, sums) if lin.space == space]
+                perm = woq.woq_outlier_perm_sums(parts, profile_fn(space))
                 self.perm_host[space] = perm
                 self.perm_dev[space] = torch.from_numpy(perm).to(device)
                 self.geom[space] = woq.woq_int4o_geometry(K)

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_uint8, c_uint16, c_void_p
 
 import numpy as np
@@ -18,7 +19,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwoq.so")
 
-WOQ_OK, WOQ_EINVAL, WOQ_EALIGN, WOQ_ENOMEM, WOQ_EHIP, WOQ_EUNSUPPORTED, WOQ_ERANGE, WOQ_ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
+WOQ_OK, WOQ_EINVAL, WOQ_EALIGN, WOQ_ENOMEM, WOQ_EHIP, WOQ_EUNSUPPORTED, WOQ_ERANGE = 0, -1, -2, -3, -4, -5, -6
 WOQ_EIO, WOQ_EFORMAT = -8, -9
 MAX_SEGMENTS = 8
 
@@ -70,6 +71,9 @@ _SIGS = {
     "woq_quantize_int8": (c_int, [c_void_p, c_int64, c_int64, c_void_p, POINTER(c_float)]),
     "woq_colabs_accumulate": (c_int, [c_void_p, c_int64, c_int64, c_void_p]),
     "woq_outlier_select": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
+    "woq_outlier_perm": (c_int, [POINTER(c_void_p), POINTER(c_int64), c_int32, c_int64, c_void_p, c_int64, c_int64,
+                                 c_void_p]),
+    "woq_outlier_perm_sums": (c_int, [POINTER(c_void_p), c_int32, c_int64, c_void_p, c_int64, c_int64, c_void_p]),
     "woq_quantize_int4o": (c_int, [c_void_p, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
     "woq_unpack_int4": (c_int, [c_void_p, c_int64, c_int64, c_void_p]),
     "woq_int8_dev_bytes": (c_int64, [c_int64, c_int64]),
@@ -86,7 +90,7 @@ _SIGS = {
     "woq_perm_positions": (c_int, [c_void_p, POINTER(Int4oGeom), c_void_p]),
     "woq_stream_read": (c_int, [c_void_p, c_int64, c_void_p]),
     "woq_dispatch_floor": (c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, c_void_p,
-                                   ctypes.POINTER(ctypes.c_float)]),
+                                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
     "woq_qgemv_int4o_x": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                   c_void_p]),
     "woq_qgemv_int4o_x_supported": (c_int, [POINTER(Int4oGeom), c_int64]),
@@ -95,10 +99,6 @@ _SIGS = {
     "woq_stack_launches": (c_int, [c_void_p, c_int64, POINTER(c_int32)]),
     "woq_stack_time": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
                                POINTER(c_float), POINTER(c_float)]),
-    "woq_stack_run_fused": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
-    "woq_stack_check": (c_int, [c_void_p, c_void_p]),
-    "woq_stack_time_fused": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_int32,
-                                     POINTER(c_float)]),
     "woq_stack_destroy": (c_int, [c_void_p]),
     "woq_quantize_int8_dev": (c_int, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
     "woq_quantize_int4o_dev": (c_int, [c_void_p, c_int64, c_void_p, POINTER(Int4oGeom), c_void_p, c_void_p,
@@ -207,6 +207,36 @@ def woq_outlier_select(colsum: np.ndarray, xprof: np.ndarray, n_out: int = -1) -
     perm = np.empty(K, np.int32)
     _check(_lib().woq_outlier_select(_ptr(colsum), _ptr(xprof.view(np.uint16)), T, K, n_out, _ptr(perm)),
            "woq_outlier_select")
+    return perm
+
+
+def woq_outlier_perm(Ws, xprof: np.ndarray, n_out: int = -1) -> np.ndarray:
+    """Global permutation of one input space from every linear that reads it
+    (float32 [N_l, K] each, in the order given) and its fp16 profile [T, K]."""
+    Ws = [np.ascontiguousarray(W, np.float32) for W in Ws]
+    xprof = np.ascontiguousarray(xprof, np.float16)
+    T, K = xprof.shape
+    assert Ws and all(W.ndim == 2 and W.shape[1] == K for W in Ws)
+    ptrs = (c_void_p * len(Ws))(*[_ptr(W) for W in Ws])
+    ns = (c_int64 * len(Ws))(*[W.shape[0] for W in Ws])
+    perm = np.empty(K, np.int32)
+    _check(_lib().woq_outlier_perm(ptrs, ns, len(Ws), K, _ptr(xprof.view(np.uint16)), T, n_out, _ptr(perm)),
+           "woq_outlier_perm")
+    return perm
+
+
+def woq_outlier_perm_sums(parts, xprof: np.ndarray, n_out: int = -1) -> np.ndarray:
+    """Global permutation of one input space from per-linear column sums
+    (float64 [K] each, from woq_colabs_accumulate into zeroed buffers), added
+    by the library in the order given."""
+    parts = [np.ascontiguousarray(p, np.float64) for p in parts]
+    xprof = np.ascontiguousarray(xprof, np.float16)
+    T, K = xprof.shape
+    assert parts and all(p.shape == (K,) for p in parts)
+    ptrs = (c_void_p * len(parts))(*[_ptr(p) for p in parts])
+    perm = np.empty(K, np.int32)
+    _check(_lib().woq_outlier_perm_sums(ptrs, len(parts), K, _ptr(xprof.view(np.uint16)), T, n_out, _ptr(perm)),
+           "woq_outlier_perm_sums")
     return perm
 
 
@@ -365,12 +395,14 @@ def woq_stream_read(buf, stream=None):
     _check(_lib().woq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)), "woq_stream_read")
 
 
-def woq_dispatch_floor(blocks: int, threads: int, iters: int, stream=None) -> float:
-    """Mean duration (us) of `iters` empty launches of blocks x threads between
-    their dispatch-boundary events."""
-    out = ctypes.c_float()
-    _check(_lib().woq_dispatch_floor(blocks, threads, iters, _stream(stream), ctypes.byref(out)), "woq_dispatch_floor")
-    return float(out.value)
+def woq_dispatch_floor(blocks: int, threads: int, iters: int, stream=None):
+    """(span_us, interval_us) of `iters` empty launches of blocks x threads:
+    the mean time between each launch's dispatch-boundary events, and the
+    mean time per launch back to back."""
+    span, interval = ctypes.c_float(), ctypes.c_float()
+    _check(_lib().woq_dispatch_floor(blocks, threads, iters, _stream(stream), ctypes.byref(span),
+                                     ctypes.byref(interval)), "woq_dispatch_floor")
+    return float(span.value), float(interval.value)
 
 
 def woq_qgemm_int4o_splitk(w: Int4oW, xp, y, splits: int, workspace, stream=None, b: int | None = None):
@@ -469,7 +501,10 @@ class Stack:
         return (c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
 
     def bind(self, inputs, outputs):
-        """Fix the input/output slot tensors (keeps references)."""
+        """Fix the input/output slot tensors (keeps references).  Every slot a
+        step names must be present, and each tensor must be a contiguous fp16
+        GPU tensor exactly as wide as the steps that use it (ValueError)."""
+        check_slots(slot_widths(self.steps), inputs, outputs)
         self._in, self._out = list(inputs), list(outputs)
         self._pin, self._pout = self._ptrs(self._in), self._ptrs(self._out)
 
@@ -481,21 +516,6 @@ class Stack:
         n = c_int32()
         _check(_lib().woq_stack_launches(self.handle, b, ctypes.byref(n)), "woq_stack_launches")
         return n.value
-
-    def run_fused(self, b: int, stream=None):
-        need_rows(b, *self._in, *self._out)
-        _check(_lib().woq_stack_run_fused(self.handle, self._pin, self._pout, b, _stream(stream)),
-               "woq_stack_run_fused")
-
-    def check(self, stream=None):
-        _check(_lib().woq_stack_check(self.handle, _stream(stream)), "woq_stack_check")
-
-    def time_fused(self, b: int, iters: int, stream=None) -> float:
-        need_rows(b, *self._in, *self._out)
-        pass_ms = c_float()
-        _check(_lib().woq_stack_time_fused(self.handle, self._pin, self._pout, b, _stream(stream), iters,
-                                           ctypes.byref(pass_ms)), "woq_stack_time_fused")
-        return pass_ms.value
 
     def time(self, b: int, iters: int, stream=None):
         need_rows(b, *self._in, *self._out)
@@ -511,10 +531,57 @@ class Stack:
             self.handle = None
 
     def __del__(self):
+        # at interpreter shutdown the HIP runtime (or a profiler attached to
+        # it) may already be torn down: leave the memory to process exit
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
             pass
+
+
+def slot_widths(steps):
+    """(in_slot, K, out_slot, N) of every step: StackStep, or PagerStep (an
+    all-streamed INT8 pager: step i uses slot i both ways)."""
+    out = []
+    for i, st in enumerate(steps):
+        if isinstance(st, PagerStep):
+            out.append((i, int(st.w.K), i, int(st.w.N)))
+        elif st.fmt == FMT_INT4O:
+            out.append((int(st.in_slot), int(st.w4.geom.K), int(st.out_slot), int(st.w4.N)))
+        else:
+            out.append((int(st.in_slot), int(st.w8.K), int(st.out_slot), int(st.w8.N)))
+    return out
+
+
+def check_slots(widths, inputs, outputs, device_type: str = "cuda"):
+    """Raise ValueError unless every slot a step names is bound to a
+    contiguous 2-D fp16 tensor on the GPU (``device_type``) whose rows are
+    exactly as wide as that step's input (K) or output (N): the C runner sees
+    pointers only, so a missing slot, a narrow or strided tensor would be read
+    or written out of bounds on the device."""
+    import torch
+
+    def ok(t, width, what, slot):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{what} slot {slot}: not a torch tensor")
+        if t.device.type != device_type:
+            raise ValueError(f"{what} slot {slot}: not on the GPU")
+        if t.dtype != torch.float16:
+            raise ValueError(f"{what} slot {slot}: dtype {t.dtype}, expected float16")
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{what} slot {slot}: must be a contiguous [rows, width] tensor")
+        if t.shape[1] != width:
+            raise ValueError(f"{what} slot {slot}: width {t.shape[1]}, the step needs {width}")
+
+    for i, (si, K, so, N) in enumerate(widths):
+        if not 0 <= si < len(inputs):
+            raise ValueError(f"step {i} reads input slot {si}; {len(inputs)} inputs bound")
+        if not 0 <= so < len(outputs):
+            raise ValueError(f"step {i} writes output slot {so}; {len(outputs)} outputs bound")
+        ok(inputs[si], K, "input", si)
+        ok(outputs[so], N, "output", so)
 
 
 def step_int4o(dev: "DeviceInt4o", perm_dev, in_slot: int, out_slot: int) -> StackStep:
@@ -596,6 +663,9 @@ class Pager:
         self.handle = h
 
     def bind(self, inputs, outputs):
+        """As Stack.bind; an all-streamed INT8 pager's step i reads input slot
+        i and writes output slot i."""
+        check_slots(slot_widths(self.steps), inputs, outputs)
         self._in, self._out = list(inputs), list(outputs)
         self._pin = (c_void_p * len(self._in))(*[t.data_ptr() for t in self._in])
         self._pout = (c_void_p * len(self._out))(*[t.data_ptr() for t in self._out])
@@ -611,6 +681,8 @@ class Pager:
             self.handle = None
 
     def __del__(self):
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
