@@ -370,6 +370,23 @@ int woq_qgemm_int4o_splitk(const woq_int4o_w* w, const uint16_t* xp, int64_t b, 
                            int32_t splits, float* workspace, int64_t workspace_bytes, void* stream);
 int64_t woq_qgemm_int4o_splitk_workspace(int64_t N, int64_t b, int32_t splits);
 
+/*
+ * woq_qgemm_int4o_splitk for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The partial sums go to a fixed workspace of
+ * WOQ_SPLITK_NOALLOC_BYTES that the library keeps in device memory of its own
+ * (one per device, held from the library's first use of that device until the
+ * process ends); the call allocates nothing.  splits * b * N * 4 bytes must fit
+ * in it: WOQ_EUNSUPPORTED otherwise (8 MiB holds 8 splits of the 70B-shaped
+ * down product, N = 8192, up to b = 32).  Every call on one device shares that
+ * workspace, which keeps the last call's partial sums: calls that overlap on
+ * one device (different streams without synchronisation, or threads) race
+ * and give wrong results.  Same results as woq_qgemm_int4o_splitk bit for bit.
+ */
+#define WOQ_SPLITK_NOALLOC_BYTES (8 << 20)
+int woq_qgemm_int4o_splitk_noalloc(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y, int64_t ldy,
+                                   int32_t splits, void* stream);
+
 /* --------------------------------------------------------- layer stack */
 
 #define WOQ_FMT_INT8  1

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libwoq.so")
 ARCH = os.environ.get("WOQ_OFFLOAD_ARCH", "gfx950")
 
 HOST_SOURCES = ["woq_host.cpp", "woq_pool.cpp"]
-DEVICE_SOURCES = ["woq_device.hip", "woq_runtime.hip", "woq_pager.cpp", "woq_prep.hip"]
+DEVICE_SOURCES = ["woq_device.hip", "woq_runtime.hip", "woq_pager.cpp", "woq_prep.hip", "woq_noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 # packed-fp32 VALU ops are kept out of the device code

@@ -110,6 +110,8 @@ _SIGS = {
     "woq_qgemm_int4o_splitk": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
                                        c_int64, c_void_p]),
     "woq_qgemm_int4o_splitk_workspace": (c_int64, [c_int64, c_int64, c_int32]),
+    "woq_qgemm_int4o_splitk_noalloc": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                                               c_void_p]),
     "woq_plan_tiers": (c_int, [c_void_p, c_int32, c_int64, c_void_p, POINTER(c_int64)]),
     "woq_tiered_create": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int64), c_int32, POINTER(StackStep),
                                   c_int32, c_int64, POINTER(c_void_p)]),
@@ -414,6 +416,18 @@ def woq_qgemm_int4o_splitk(w: Int4oW, xp, y, splits: int, workspace, stream=None
                                          workspace.numel() * workspace.element_size(), _stream(stream)),
            "woq_qgemm_int4o_splitk")
     return y
+
+
+SPLITK_NOALLOC_BYTES = 8 << 20
+
+
+def woq_qgemm_int4o_splitk_noalloc(w: Int4oW, xp, y, splits: int, stream=None, b: int | None = None):
+    """woq_qgemm_int4o_splitk with the library's fixed per-device workspace
+    (no allocation; calls on one device must not overlap)."""
+    b = xp.shape[0] if b is None else b
+    need_rows(b, xp, y)
+    _check(_lib().woq_qgemm_int4o_splitk_noalloc(ctypes.byref(w), _ptr(xp), b, _ptr(y), y.shape[1], splits,
+                                                 _stream(stream)), "woq_qgemm_int4o_splitk_noalloc")
 
 
 def woq_qgemm_int4o(w: Int4oW, xp, y, stream=None, b: int | None = None):
