@@ -797,6 +797,22 @@ def bench_streamed(args, spec, b, log):
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
     streamed_out = [t.cpu() for t in outputs]
+    # per-copy timeline of a few more passes: HIP events on the copy stream
+    # around every block copy (no tracer, nothing dropped)
+    copy_passes = []
+    for _ in range(3):
+        waits, starts, ends, pass_ms = pager.time(b, compute, copy)
+        dur = [e - s for s, e in zip(starts, ends)]
+        gaps = [starts[j + 1] - ends[j] for j in range(len(ends) - 1)]
+        slot_waits = [s - w for w, s in zip(waits, starts)]
+        copy_passes.append({"pass_ms": round(pass_ms, 3), "first_copy_start_ms": round(starts[0], 3),
+                            "last_copy_end_ms": round(ends[-1], 3),
+                            "copy_busy_ms": round(sum(dur), 3),
+                            "copy_gbs": round(L * ss.block_bytes / (sum(dur) * 1e-3) / 1e9, 2),
+                            "gaps_between_copies_ms": round(sum(gaps), 3),
+                            "max_gap_ms": round(max(gaps) if gaps else 0.0, 3),
+                            "waits_for_a_free_slot_ms": round(sum(slot_waits), 3),
+                            "min_copy_ms": round(min(dur), 3), "max_copy_ms": round(max(dur), 3)})
 
     # compute alone: the same products over a device-resident copy of the pool
     dev_pool = ss.pool.to("cuda")
@@ -854,7 +870,8 @@ def bench_streamed(args, spec, b, log):
                      "overlap_efficiency_vs_copy_pass": round(copy_pass_ms / ms_per_step, 4),
                      "compute_only_ms": round(compute_ms, 4), "overlap_efficiency": round(eta, 4),
                      "step_minus_copy_per_block_ms": round((ms_per_step - copy_serial_ms) / L, 4),
-                     "bit_identical_to_resident": bool(same)},
+                     "bit_identical_to_resident": bool(same),
+                     "copy_timeline": copy_passes},
         "roofline": {"bound": "hbm", "kernel": "qgemv_int8_valu", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "launches_per_step": len(steps),

@@ -541,6 +541,23 @@ int woq_pager_create(const void* pinned_pool, const int64_t* layer_off, const in
 int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
                   void* compute_stream, void* copy_stream);
 
+/* Number of streamed (tier B) layers of a pager. */
+int woq_pager_streamed_layers(const woq_pager* p, int32_t* n);
+
+/*
+ * One woq_pager_run pass with HIP events on the copy stream around every
+ * block copy (for measurement).  For the j-th streamed layer, wait_ms[j] is
+ * when the copy stream reached it (before waiting for its slot), copy_ms[j]
+ * when the copy started (the slot was free) and end_ms[j] when the copy had
+ * landed, all in milliseconds from the pass's start on the compute stream;
+ * *pass_ms is the pass's duration on the compute stream.  The arrays hold
+ * woq_pager_streamed_layers entries (null when there are none).  Synchronises
+ * both streams.
+ */
+int woq_pager_time(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                   void* compute_stream, void* copy_stream, float* wait_ms, float* copy_ms, float* end_ms,
+                   float* pass_ms);
+
 /* Release the slots, events and workspace (after both streams have finished). */
 int woq_pager_destroy(woq_pager* p);
 

@@ -299,6 +299,32 @@ def test_chained_steps_read_the_previous_output(gpu_lib, fmt, b):
     runner.close()
 
 
+def test_create_destroy_releases_every_buffer(gpu_lib):
+    """A runner whose step is the 70B-shaped down product (8192 x 28672, up to
+    b = 32: 8 MB of split-K partial sums plus the permuted activations),
+    created and destroyed 20 times, leaves the device's free memory where it
+    started (a buffer left behind would show as 20 x 8 MB)."""
+    import torch
+    K, N = 28672, 8192
+    g = woq.woq_int4o_geometry(K)
+    perm = torch.arange(K, dtype=torch.int32, device="cuda")       # read back once at create
+    dummy = torch.zeros(16, dtype=torch.uint8, device="cuda")      # weights are not read at create
+    st = woq.StackStep()
+    st.fmt, st.in_slot, st.out_slot = woq.FMT_INT4O, 0, 0
+    st.w4.codes = st.w4.scales = st.w4.w_out = dummy.data_ptr()
+    st.w4.N, st.w4.geom = N, g
+    st.perm = perm.data_ptr()
+    assert woq.lib().woq_qgemm_int4o_splitk_workspace(N, 32, 8) == 8 * 32 * N * 4
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    for _ in range(20):
+        woq.Stack([st], 32).close()
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    print(f"free memory before {free0}, after {free1}", flush=True)
+    assert free1 >= free0 - (4 << 20), (free0, free1)
+
+
 def test_runner_launch_count(gpu_lib):
     """One launch per folded INT4O step (small widths, b <= 2), two where the
     permutation runs separately (b = 8, matrix-core kernel), one per INT8 step."""

@@ -1,13 +1,16 @@
 // Device building blocks shared by the product kernels: code unpacking,
 // the dequantise-and-dot inner loops and the cross-lane reductions.
 //
-// A "quad" is four consecutive output rows handled by one wave.  Lane l owns
-// the 16-byte chunks l, l + 64, ... of each of the four rows (a chunk is 32
-// INT4O background channels, or 16 INT8 channels), so every wave-wide weight
-// load is one contiguous kilobyte of a row.  Codes become exact fp16 numbers
-// with the exponent-bias trick (an offset-binary code u in the low mantissa
-// bits of 0x6400 is 1024 + u) and are multiplied with v_dot2_f32_f16 (exact
-// fp16 products, fp32 accumulation).
+// Codes become exact fp16 numbers with the exponent-bias ("magic number")
+// conversion that published weight-only INT4/INT8 GEMM kernels use (e.g.
+// Kim et al., 2022, "Who Says Elephants Can't Run: Bringing Large Scale MoE
+// Models into Cloud Scale Production", arXiv:2211.10017): an offset-binary
+// code u placed in the low mantissa bits of the fp16 number 1024 (bits
+// 0x6400) reads as 1024 + u, so one AND-OR per pair of codes gives two fp16
+// values; the offset is removed by one subtraction, or (INT4O vector kernel,
+// INT8 at b <= 2) once per chunk from the sum instead.  Products use
+// v_dot2_f32_f16 (exact fp16 products, fp32 accumulation) or the fp16 matrix
+// cores.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -189,8 +189,16 @@ int woq_pager_create(const void* pinned_pool, const int64_t* layer_off, const in
     return woq_tiered_create(pinned_pool, layer_off, layer_bytes, n_layers, st.data(), steps_per_layer, max_b, out);
 }
 
-int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
-                  void* compute_stream, void* copy_stream) {
+}  // extern "C"
+
+namespace {
+
+// One pass; with cev (3 events per streamed layer) the copy stream records,
+// for streamed layer j, cev[3j] before its wait for the slot, cev[3j + 1]
+// when that wait is over (the copy starts) and cev[3j + 2] when the copy has
+// landed.
+int pager_pass(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+               void* compute_stream, void* copy_stream, hipEvent_t* cev) {
     if (!p || !inputs || !outputs || b < 1 || b > p->max_b) return WOQ_EINVAL;
     const int nB = (int)p->streamed.size();
     if (nB > 0 && compute_stream == copy_stream) return WOQ_EINVAL;
@@ -199,10 +207,13 @@ int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* 
     auto issue_copy = [&](int j) -> hipError_t {
         const int s = j & 1, l = p->streamed[j];
         hipError_t r = hipSuccess;
-        if (j >= 2) r = hipStreamWaitEvent(xs, p->released[s], 0);
+        if (cev) r = hipEventRecord(cev[3 * j], xs);
+        if (r == hipSuccess && j >= 2) r = hipStreamWaitEvent(xs, p->released[s], 0);
+        if (r == hipSuccess && cev) r = hipEventRecord(cev[3 * j + 1], xs);
         if (r == hipSuccess)
             r = hipMemcpyAsync(p->slot[s], p->pool + p->off[l], (size_t)p->bytes[l], hipMemcpyHostToDevice, xs);
         if (r == hipSuccess) r = hipEventRecord(p->copied[s], xs);
+        if (r == hipSuccess && cev) r = hipEventRecord(cev[3 * j + 2], xs);
         return r;
     };
     if (nB > 0) {
@@ -239,6 +250,52 @@ int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* 
         }
     }
     return WOQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int woq_pager_run(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                  void* compute_stream, void* copy_stream) {
+    return pager_pass(p, inputs, outputs, b, compute_stream, copy_stream, nullptr);
+}
+
+int woq_pager_streamed_layers(const woq_pager* p, int32_t* n) {
+    if (!p || !n) return WOQ_EINVAL;
+    *n = (int32_t)p->streamed.size();
+    return WOQ_OK;
+}
+
+int woq_pager_time(woq_pager* p, const uint16_t* const* inputs, uint16_t* const* outputs, int64_t b,
+                   void* compute_stream, void* copy_stream, float* wait_ms, float* copy_ms, float* end_ms,
+                   float* pass_ms) {
+    if (!p || !pass_ms) return WOQ_EINVAL;
+    const int nB = (int)p->streamed.size();
+    if (nB > 0 && (!wait_ms || !copy_ms || !end_ms)) return WOQ_EINVAL;
+    hipStream_t cs = (hipStream_t)compute_stream;
+    std::vector<hipEvent_t> ev(3 * (size_t)nB + 2, nullptr);
+    hipError_t e = hipSuccess;
+    for (auto& x : ev)
+        if (e == hipSuccess) e = hipEventCreate(&x);
+    hipEvent_t* pass = ev.data() + 3 * (size_t)nB;
+    int rc = WOQ_OK;
+    // the pass's start on the compute stream: the copy stream starts behind it
+    if (e == hipSuccess) e = hipEventRecord(pass[0], cs);
+    if (e == hipSuccess) rc = pager_pass(p, inputs, outputs, b, compute_stream, copy_stream, ev.data());
+    if (e == hipSuccess && rc == WOQ_OK) e = hipEventRecord(pass[1], cs);
+    if (e == hipSuccess && rc == WOQ_OK) e = hipStreamSynchronize(cs);
+    if (e == hipSuccess && rc == WOQ_OK && nB > 0) e = hipStreamSynchronize((hipStream_t)copy_stream);
+    for (int j = 0; j < nB && e == hipSuccess && rc == WOQ_OK; ++j) {
+        e = hipEventElapsedTime(&wait_ms[j], pass[0], ev[3 * j]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&copy_ms[j], pass[0], ev[3 * j + 1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&end_ms[j], pass[0], ev[3 * j + 2]);
+    }
+    if (e == hipSuccess && rc == WOQ_OK) e = hipEventElapsedTime(pass_ms, pass[0], pass[1]);
+    for (auto& x : ev)
+        if (x) (void)hipEventDestroy(x);
+    if (rc) return rc;
+    return hip_status(e);
 }
 
 int woq_pager_destroy(woq_pager* p) {

@@ -119,6 +119,9 @@ _SIGS = {
                                  c_int64, POINTER(c_void_p)]),
     "woq_pager_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_void_p]),
     "woq_pager_destroy": (c_int, [c_void_p]),
+    "woq_pager_streamed_layers": (c_int, [c_void_p, POINTER(c_int32)]),
+    "woq_pager_time": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p, c_void_p,
+                               POINTER(c_float), POINTER(c_float), POINTER(c_float), POINTER(c_float)]),
 }
 
 # symbols the header declares (checked by the CPU tests)
@@ -688,6 +691,23 @@ class Pager:
         need_rows(b, *self._in, *self._out)
         _check(_lib().woq_pager_run(self.handle, self._pin, self._pout, b, _stream(compute_stream),
                                     _stream(copy_stream)), "woq_pager_run")
+
+    def streamed_layers(self) -> int:
+        n = c_int32()
+        _check(_lib().woq_pager_streamed_layers(self.handle, ctypes.byref(n)), "woq_pager_streamed_layers")
+        return n.value
+
+    def time(self, b: int, compute_stream, copy_stream):
+        """One pass with events around every block copy: (wait, start, end)
+        times of each streamed layer's copy in ms from the pass's start, and
+        the pass's duration."""
+        need_rows(b, *self._in, *self._out)
+        n = max(1, self.streamed_layers())
+        w, c, e, p = (c_float * n)(), (c_float * n)(), (c_float * n)(), c_float()
+        _check(_lib().woq_pager_time(self.handle, self._pin, self._pout, b, _stream(compute_stream),
+                                     _stream(copy_stream), w, c, e, ctypes.byref(p)), "woq_pager_time")
+        k = self.streamed_layers()
+        return [w[i] for i in range(k)], [c[i] for i in range(k)], [e[i] for i in range(k)], p.value
 
     def close(self):
         if getattr(self, "handle", None):
