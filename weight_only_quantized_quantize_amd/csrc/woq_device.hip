@@ -203,7 +203,10 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
     __shared__ float red[S > 1 ? T * S : 1][B][16];
     constexpr int W = T * S, NT = 64 * W, P = TILE_WINDOW;
     constexpr int SC = 4;                            // staged pieces per thread issued before the weights
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform across the wave: read it into a scalar
+    // register, so that everything derived from it (the tile, the groups, the
+    // weight and scale addresses of every refill) is scalar arithmetic
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int tile = wave / S, s = wave % S;
     const int m = lane & 15, c = lane >> 4;
     const int tiles = (a.N + 15) >> 4;
@@ -239,20 +242,29 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
     // staging would then wait for the whole window.
     const int J = G4 > s ? (G4 - 1 - s) / S + 1 : 0;
     const uint4* dummy = reinterpret_cast<const uint4*>(GATHER ? ga.x : a.xp);
-    const uint4* wb = G4 > 0 ? a.codes + (int64_t)tb * G4 * 64 + c * 16 + m : dummy;
-    // scales are read as the dword holding rows m & ~1 and m | 1, so that
-    // the loaded value needs no zero-extension before it is consumed (a
-    // 16-bit load is followed by a mask, placed where the load arrives)
-    const uint32_t* sb = G4 > 0 ? reinterpret_cast<const uint32_t*>(a.scales + (int64_t)tb * G4 * 16 + (m & ~1))
-                                : reinterpret_cast<const uint32_t*>(dummy);
-    const int sshift = 16 * (m & 1);
+    // weight and scale addresses: a scalar base per (tile, group) plus a
+    // 32-bit per-lane byte offset (lane (m, c): 16 bytes of the 1 KB block,
+    // and the 16-bit scale of row m), so a refill costs no vector address
+    // arithmetic (measured on MI355X: the 70B-shaped step at b = 1 from about
+    // 90.8 to 85.8 us per layer, with the plans below and the biased-sum seed
+    // of int4o_row_chunk; the 3B-shaped step 24.2 -> 23.7 us per layer)
+    const char* wtile = reinterpret_cast<const char*>(G4 > 0 ? a.codes + (int64_t)tb * G4 * 64 : dummy);
+    const char* stile = reinterpret_cast<const char*>(G4 > 0 ? a.scales + (int64_t)tb * G4 * 16 : (const uint16_t*)dummy);
+    const uint32_t woff = G4 > 0 ? (uint32_t)(c * 16 + m) * 16u : 0u;
+    const uint32_t soff = G4 > 0 ? (uint32_t)m * 2u : 0u;
+    auto wload = [&](int g) {
+        return gload_nt(reinterpret_cast<const uint4*>(wtile + (size_t)(uint32_t)g * 1024u + woff));
+    };
+    auto sload = [&](int g) {
+        return (uint32_t)*gptr(reinterpret_cast<const uint16_t*>(stile + (size_t)(uint32_t)g * 32u + soff));
+    };
     uint4 wq[P];
     uint32_t sq[P];
 #pragma unroll
     for (int u = 0; u < P; ++u) {
         const int g = G4 > 0 ? (J > 0 ? s + S * (u < J ? u : J - 1) : 0) : 0;
-        wq[u] = gload_nt(wb + (int64_t)g * 64);
-        sq[u] = *gptr(sb + g * 8);
+        wq[u] = wload(g);
+        sq[u] = sload(g);
     }
     const uint4* ob = a.wout + (int64_t)tb * a.no8 * 16 + m;
     const int i80 = 4 * s + c;
@@ -306,7 +318,7 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
         uint4 xq[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) xq[k] = load_x16(xl + b * xp_len + 32 * q + 8 * k);
-        corr[e] = activation_chunk_correction(xq);
+        corr[e] = -activation_chunk_correction(xq);     // negated: it seeds the low-nibble sums
     }
     lds_barrier();
 
@@ -318,11 +330,12 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    const uint32_t bias = bias_reg();
     auto consume = [&](int j, uint4 w, uint32_t sq1) {
         const int g = s + S * j;
         // the scale word is unpacked only here, after the wait for its slot
         asm volatile("" : "+v"(sq1));
-        const float sc = h_to_f((uint16_t)(sq1 >> sshift));
+        const float sc = h_to_f((uint16_t)sq1);
         uint4 xg[B][4];
         float cg[B];
 #pragma unroll
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
             for (int q = 0; q < 4; ++q) xg[b][q] = load_x16(xl + b * xp_len + 128 * g + 32 * c + 8 * q);
             cg[b] = corr[b * nq + 4 * g + c];
         }
-        int4o_row_chunk<B>(w, sc, xg, cg, acc);
+        int4o_row_chunk<B>(w, sc, xg, cg, acc, bias);
     };
     int j0 = 0;
     for (; j0 + P < J; j0 += P) {
@@ -340,8 +353,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
             const int j = j0 + u;
             consume(j, wq[u], sq[u]);
             const int gn = s + S * (j + P < J ? j + P : J - 1);
-            wq[u] = gload_nt(wb + (int64_t)gn * 64);
-            sq[u] = *gptr(sb + gn * 8);
+            wq[u] = wload(gn);
+            sq[u] = sload(gn);
         }
     }
 #pragma unroll
@@ -1086,15 +1099,18 @@ template <int B, bool GATHER>
 hipError_t launch_int4o_tile(const Int4oArgs& a, const GatherArgs& ga, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
     const size_t lds = (size_t)woq::int4o_valu_lds_bytes(a.xp_len, 4 * (int64_t)a.G4, B);
-    // plans from in-stack sweeps on MI355X (b = 1): long rows on few tiles
-    // (3B down, 70B down) want eight waves per tile so every SIMD streams;
-    // wide products with long rows (70B gate|up) one tile per workgroup; wide
-    // products with short rows (3B gate|up, the 128256-row head) two tiles of
-    // two waves; the rest one tile of four waves
+    // plans from whole-stack sweeps on MI355X (b = 1): rows of 128 groups or
+    // more on 512 tiles or more (70B down) run two tiles of eight waves per
+    // workgroup (70B down 23.1 -> 22.3 us); long rows on few tiles (3B down)
+    // one tile of eight waves, so every SIMD streams; 1024 tiles or more (3B
+    // and 70B gate|up, the 128256-row heads) two tiles of two waves, one
+    // staged copy of the activations for both (70B gate|up 40.8 -> 40.1 us);
+    // the rest one tile of four waves
+    if (a.G4 >= 128 && tiles >= 512)
+        return launch_kernel(qgemv_int4o_tile<B, 2, 8, GATHER>, dim3((unsigned)woq::ceil_div(tiles, 2)), dim3(1024),
+                             lds, s, a, ga);
     if (a.G4 >= 48 && (tiles < 256 || a.G4 >= 128))
         return launch_kernel(qgemv_int4o_tile<B, 1, 8, GATHER>, dim3((unsigned)tiles), dim3(512), lds, s, a, ga);
-    if (tiles >= 2048 && a.G4 >= 48)
-        return launch_kernel(qgemv_int4o_tile<B, 1, 4, GATHER>, dim3((unsigned)tiles), dim3(256), lds, s, a, ga);
     if (tiles >= 1024)
         return launch_kernel(qgemv_int4o_tile<B, 2, 2, GATHER>, dim3((unsigned)woq::ceil_div(tiles, 2)), dim3(256),
                              lds, s, a, ga);

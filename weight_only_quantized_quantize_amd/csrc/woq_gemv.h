@@ -117,14 +117,15 @@ __device__ __forceinline__ void zero_acc(float (&acc)[4][B]) {
 // high-nibble pairs 16 code + 1152, so the chunk's sum of code * x is
 // lo + hi / 16 - corr, with corr = 1032 (sum of x over the low-nibble
 // channels) + 72 (sum of x over the high-nibble channels), computed once per
-// chunk and batch row (activation_chunk_correction).  Skipping the bias
+// chunk and batch row (activation_chunk_correction); ncorr = -corr is passed
+// in and seeds the low-nibble sum, which saves a subtraction and a register
+// clear per chunk.  bias holds 0x64006400 in a vector register.  Skipping the bias
 // subtraction saves one packed add per weight pair; products stay exact and
 // the cancellation costs about 1e-5 of the chunk's magnitude in fp32.  The
 // group scale s multiplies the chunk's sum.
 template <int B>
-__device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&xv)[B][4], const float (&corr)[B],
-                                                float (&acc)[B]) {
-    const uint32_t bias = bias_reg();
+__device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&xv)[B][4], const float (&ncorr)[B],
+                                                float (&acc)[B], uint32_t bias) {
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     h2 lo0[4], lo1[4], hi0[4], hi1[4];
 #pragma unroll
@@ -141,7 +142,7 @@ __device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&
                                  xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w,
                                  xv[b][2].x, xv[b][2].y, xv[b][2].z, xv[b][2].w,
                                  xv[b][3].x, xv[b][3].y, xv[b][3].z, xv[b][3].w};
-        float lo = 0.0f, hi = 0.0f;
+        float lo = ncorr[b], hi = 0.0f;
 #pragma unroll
         for (int P = 0; P < 2; ++P) {
 #pragma unroll
@@ -153,7 +154,7 @@ __device__ __forceinline__ void int4o_row_chunk(uint4 w, float s, const uint4 (&
                 hi = dot2(hi1[d], as_h2(xw[8 * P + 4 + 2 * e + 1]), hi);
             }
         }
-        acc[b] = fmaf(s, fmaf(hi, 0.0625f, lo) - corr[b], acc[b]);
+        acc[b] = fmaf(s, fmaf(hi, 0.0625f, lo), acc[b]);
     }
 }
 
