@@ -775,12 +775,15 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     constexpr int PPC = CH * 16;                      // 16-byte pieces of one column per chunk
     constexpr int NPT = (COLS * PPC + 64 * W - 1) / (64 * W);   // staged pieces per thread (b = COLS)
     constexpr int RED = 4 * W * RB * NBT * 16 * 17;
-    constexpr int XSB = 2 * 2 * COLS * XS;
+    // with HALF, lanes of batch columns 8..15 read an extra column that
+    // holds zeros for the whole kernel (no branch, no register clears)
+    constexpr int XCOLS = HALF ? COLS + 1 : COLS;
+    constexpr int XSB = 2 * 2 * XCOLS * XS;
     __shared__ __align__(16) uint16_t lds[(XSB > RED ? XSB : RED) / 2];
-    uint16_t (*xs)[COLS][XS] = reinterpret_cast<uint16_t (*)[COLS][XS]>(lds);
+    uint16_t (*xs)[XCOLS][XS] = reinterpret_cast<uint16_t (*)[XCOLS][XS]>(lds);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int tile = wave / S, s = wave % S;
     const int m = lane & 15;           // row within the tile (A) / batch column (B)
     const int c = lane >> 4;           // 32-channel chunk of the group / k-block
@@ -810,9 +813,9 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
 #pragma unroll
         for (int t = 0; t < NBT; ++t) acc[r][t] = (f4){0.f, 0.f, 0.f, 0.f};
 
-    // columns b .. COLS-1 of both buffers hold zeros for the whole kernel
-    for (int e = tid; e < 2 * COLS * XS; e += 64 * W) {
-        const int col = (e / XS) % COLS;
+    // columns b .. XCOLS-1 of both buffers hold zeros for the whole kernel
+    for (int e = tid; e < 2 * XCOLS * XS; e += 64 * W) {
+        const int col = (e / XS) % XCOLS;
         if (col >= b) lds[e] = 0;
     }
 
@@ -847,26 +850,36 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     auto group_of = [&](int j) { return (j / KC) * CH + s * KC + (j % KC); };
     // tile layout: lane (m, c) reads 16 bytes of the tile's 1 KB block of group g,
     // and the scales of D rows 4c .. 4c + 3 (8 contiguous bytes)
-    const uint4* wld[RB];
-    const uint2* sld[RB];
+    // a scalar base per tile and group plus a 32-bit per-lane byte offset,
+    // with the wave index in a scalar register: no vector address arithmetic
+    // per refill (with the zero column below, the 70B-shaped step at b = 4
+    // went from 119 to 115 us per layer and at b = 8 from 123 to 120 us; no
+    // change at b = 32)
+    const char* wtb[RB];
+    const char* stb[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        wld[r] = a.codes + ((int64_t)tb[r] * G4s + gbeg) * 64 + c * 16 + m;
-        sld[r] = reinterpret_cast<const uint2*>(a.scales) + ((int64_t)tb[r] * G4s + gbeg) * 4 + c;
+        wtb[r] = reinterpret_cast<const char*>(a.codes + ((int64_t)tb[r] * G4s + gbeg) * 64);
+        stb[r] = reinterpret_cast<const char*>(a.scales + ((int64_t)tb[r] * G4s + gbeg) * 16);
     }
+    uint32_t woff = (uint32_t)(c * 16 + m) * 16u, soff = (uint32_t)c * 8u;
 
     // Every load below is unconditional, so each wait counts loads exactly
     // and the weight window keeps running ahead across chunk boundaries (a
     // load skipped on some path makes the compiler count every later wait as
     // if it had not been issued, which drained the window at each chunk).
     // Without groups (an empty K range) the loads read the activation row.
-    const uint4* dummy = reinterpret_cast<const uint4*>(a.xp);
-    if (nchunks == 0)
+    if (nchunks == 0) {
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            wld[r] = dummy;
-            sld[r] = reinterpret_cast<const uint2*>(dummy);
-        }
+        for (int r = 0; r < RB; ++r) wtb[r] = stb[r] = reinterpret_cast<const char*>(a.xp);
+        woff = soff = 0;
+    }
+    auto wload = [&](int r, int g) {
+        return gload_nt(reinterpret_cast<const uint4*>(wtb[r] + (size_t)(uint32_t)g * 1024u + woff));
+    };
+    auto sload = [&](int r, int g) {
+        return gload_u2(reinterpret_cast<const uint2*>(stb[r] + (size_t)(uint32_t)g * 32u + soff));
+    };
     // The loads go out in the order the loop keeps them in: chunk c issues
     // the activation loads of chunk c + 2 and then the window slots of chunk
     // c + WC, so the prologue plays chunks -WC .. -1.  The wait counts at the
@@ -892,8 +905,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
             const int g = j < J ? group_of(j) : 0;
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                wq[j][r] = gload_nt(wld[r] + (int64_t)g * 64);
-                sc[j][r] = gload_u2(sld[r] + g * 4);
+                wq[j][r] = wload(r, g);
+                sc[j][r] = sload(r, g);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -941,13 +954,11 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
 #pragma unroll
             for (int t = 0; t < NBT; ++t) {
                 h8 Bv[4];
-                if (!HALF || m < COLS) {
-                    const lx_ptr xb = (lx_ptr)&xs[cb & 1][HALF ? m : 16 * t + m][128 * gl + 32 * c];
+                {
+                    const int col = HALF ? (m < COLS ? m : COLS) : 16 * t + m;
+                    const lx_ptr xb = (lx_ptr)&xs[cb & 1][col][128 * gl + 32 * c];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) Bv[q] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
                 }
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
@@ -966,8 +977,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                wq[u][r] = gload_nt(wld[r] + (int64_t)gn * 64);
-                sc[u][r] = gload_u2(sld[r] + gn * 4);
+                wq[u][r] = wload(r, gn);
+                sc[u][r] = sload(r, gn);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
