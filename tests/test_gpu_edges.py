@@ -137,3 +137,53 @@ def test_dispatch_floor_measurement(gpu_lib):
         with pytest.raises(woq.WoqError) as e:
             woq.woq_dispatch_floor(*bad, s)
         assert e.value.status == woq.WOQ_EINVAL
+
+
+def test_allocation_failures_are_reported_and_release_everything(gpu_lib):
+    """Allocation failure paths, forced from the host with requests larger
+    than the device: a runner whose permuted-activation workspace would need
+    about 1 TB, and a pager whose two slots would need 1 TB each, return
+    WOQ_ENOMEM from create, and the device's free memory is where it was (the
+    buffers allocated before the failing one are released)."""
+    import ctypes
+    import torch
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    # runner: one INT4O step over an input space of 2^33 channels at max_b = 64
+    K = 1 << 33
+    g = woq.woq_int4o_geometry(K)
+    assert 64 * g.xp_len * 2 > 2 * torch.cuda.get_device_properties(0).total_memory
+    dummy = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    st = woq.StackStep()
+    st.fmt, st.in_slot, st.out_slot = woq.FMT_INT4O, 0, 0
+    st.w4.codes = st.w4.scales = st.w4.w_out = dummy.data_ptr()
+    st.w4.N, st.w4.geom = 16, g
+    st.perm = dummy.data_ptr()
+    h = ctypes.c_void_p()
+    steps = (woq.StackStep * 1)(st)
+    assert woq.lib().woq_stack_create(steps, 1, 64, ctypes.byref(h)) == woq.WOQ_ENOMEM
+    assert not h.value
+    # pager: one streamed INT8 layer whose block (and so each slot) is 1 TB
+    pool = torch.zeros(4096, dtype=torch.uint8).pin_memory()
+    q = np.zeros((64, 64), np.int8)
+    ps = woq.PagerStep()
+    ps.code_offset = 0
+    ps.w.N, ps.w.K, ps.w.nseg = 64, 64, 1
+    ps.w.seg_end[0], ps.w.seg_scale[0] = 64, 1.0
+    off = (ctypes.c_int64 * 1)(0)
+    nbytes = (ctypes.c_int64 * 1)(1 << 40)
+    psteps = (woq.PagerStep * 1)(ps)
+    hp = ctypes.c_void_p()
+    rc = woq.lib().woq_pager_create(ctypes.c_void_p(pool.data_ptr()), off, nbytes, 1, psteps, 1, 1, ctypes.byref(hp))
+    assert rc == woq.WOQ_ENOMEM, rc
+    assert not hp.value
+    assert woq.lib().woq_last_hip_error() == 2          # hipErrorOutOfMemory, kept by the library
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    print(f"free memory before {free0}, after {free1}", flush=True)
+    assert free1 >= free0 - (4 << 20), (free0, free1)
+    # the runtime's own error state is clear: the caller's next HIP work is unaffected
+    t = torch.ones(1 << 20, device="cuda")
+    torch.cuda.synchronize()
+    assert float(t.sum()) == float(1 << 20)
+    del q, t

@@ -34,7 +34,14 @@
 
 namespace woq {
 static thread_local int g_last_hip_error = 0;
-void set_hip_error(int code) { g_last_hip_error = code; }
+// Record a failing HIP call's error for woq_last_hip_error and clear the HIP
+// runtime's own last-error state: the failure is reported through the
+// library's status code, and a pending runtime error would otherwise be
+// picked up by the caller's next, unrelated, error check.
+void set_hip_error(int code) {
+    g_last_hip_error = code;
+    (void)hipGetLastError();
+}
 static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 void set_launch_events(void* start, void* stop) {
     g_ev_start = (hipEvent_t)start;

@@ -447,8 +447,8 @@ int woq_layout_int4o_inverse(const uint8_t* dev_codes, const uint16_t* dev_scale
         N,
         [&](int64_t r0, int64_t r1) {
             for (int64_t r = r0; r < r1; ++r) {
-                uint8_t* out = packed + r * half;
-                std::memset(out, 0, (size_t)half);
+                uint8_t* out = packed + r * half;     // not read when the space has no background (half = 0)
+                if (half) std::memset(out, 0, (size_t)half);
                 for (int64_t gi = 0; gi < G; ++gi) {
                     for (int c = 0; c < 4; ++c) {
                         uint32_t dw[4];
