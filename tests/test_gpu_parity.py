@@ -345,6 +345,7 @@ def test_int4o_full_shapes_sampled(gpu_lib, cfg):
 
 
 @pytest.mark.parametrize("N,K,b,ldx", [(1, 8, 1, 8), (5, 300, 3, 320), (4100, 1000, 2, 1000 + 24),
+                                       (4100, 1000, 1, 1000), (11205, 1000, 1, 1000 + 8),
                                        (16500, 3072, 1, 3072), (33, 8192, 3, 8192), (17, 28672, 1, 28672 + 8)])
 def test_int4o_one_launch_matches_oracle(gpu_lib, N, K, b, ldx):
     """The permutation folded into the product, including row strides above K,

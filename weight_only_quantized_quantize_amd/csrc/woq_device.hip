@@ -190,6 +190,39 @@ __device__ __forceinline__ void scatter8(uint16_t* xs, int xp_len, const uint4 (
     }
 }
 
+// Dword i of the result is dword (i + r) & 3 of v (r in 0..3).
+__device__ __forceinline__ uint4 rot_dwords(uint4 v, int r) {
+    const bool r2 = (r & 2) != 0, r1 = (r & 1) != 0;
+    const uint32_t t0 = r2 ? v.z : v.x, t1 = r2 ? v.w : v.y, t2 = r2 ? v.x : v.z, t3 = r2 ? v.y : v.w;
+    return make_uint4(r1 ? t1 : t0, r1 ? t2 : t1, r1 ? t3 : t2, r1 ? t0 : t3);
+}
+
+// scatter8 for a piece whose eight positions all lie in the row (every piece
+// of a position table but the last when K is not a multiple of 8), without
+// branches.  Lanes rotate their piece by r dwords first: with 16-byte pieces
+// on consecutive lanes, the j-th write of every lane would otherwise hit only
+// eight of the 32 LDS banks; rotating by (lane / 8) % 4 spreads it over all.
+// Measured on MI355X: the scatter of the 70B-shaped q|k|v product's row from
+// 1.3 to 1.0 us per wave (median), the 70B-shaped step at b = 1 1.3% and the
+// 3B-shaped step 1.9% faster.
+template <int B>
+__device__ __forceinline__ void scatter8_full(uint16_t* xs, int xp_len, const uint4 (&xv)[B], uint4 pv, int r) {
+    const uint4 pr = rot_dwords(pv, r);
+    const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
+    uint32_t xw[B][4];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const uint4 t = rot_dwords(xv[b], r);
+        xw[b][0] = t.x; xw[b][1] = t.y; xw[b][2] = t.z; xw[b][3] = t.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int p = (int)((pw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+#pragma unroll
+        for (int b = 0; b < B; ++b) xs[b * xp_len + p] = (uint16_t)(xw[b][j >> 1] >> (16 * (j & 1)));
+    }
+}
+
 // A workgroup of T x S waves owns T tiles of 16 rows; the S waves of a tile
 // take the groups g = s, s + S, ... of every row.  Lane l holds row l & 15 of
 // its tile and chunk c = l >> 4 (32 channels) of each of its groups, so a
@@ -286,7 +319,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
                 uint4 x1[B];
 #pragma unroll
                 for (int b = 0; b < B; ++b) x1[b] = xv[i][b];
-                scatter8<B>(xs, xp_len, x1, pv[i]);
+                if (p == npieces - 1 && (ga.K & 7)) scatter8<B>(xs, xp_len, x1, pv[i]);
+                else scatter8_full<B>(xs, xp_len, x1, pv[i], (lane >> 3) & 3);
             } else {
                 *(__attribute__((address_space(3))) u32x4*)&xs[8 * p] =
                     (u32x4){xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w};
@@ -299,7 +333,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
             const uint4 p1 = as_uint4(((const g_u32x4*)ga.pos)[p]);
 #pragma unroll
             for (int b = 0; b < B; ++b) x1[b] = as_uint4(((const g_u32x4*)ga.x)[b * ldx16 + p]);
-            scatter8<B>(xs, xp_len, x1, p1);
+            if (p == npieces - 1 && (ga.K & 7)) scatter8<B>(xs, xp_len, x1, p1);
+            else scatter8_full<B>(xs, xp_len, x1, p1, (lane >> 3) & 3);
         } else {
             const uint4 v = as_uint4(((const g_u32x4*)a.xp)[p]);
             *(__attribute__((address_space(3))) u32x4*)&xs[8 * p] = (u32x4){v.x, v.y, v.z, v.w};
@@ -1108,31 +1143,54 @@ int launch_status(hipError_t e) {
     return WOQ_OK;
 }
 
+int compute_units();
+
 // Tiles per workgroup and waves per tile of the vector kernel (measured on
 // MI355X over the 3B- and 70B-shaped products): narrow products split each
 // tile's groups over four waves so that enough loads are in flight on every
 // compute unit; from 1024 tiles on, two tiles share a workgroup (one staged
 // copy of the activations) and each tile takes two waves.
+template <int B, int T, int S, bool GATHER>
+hipError_t launch_int4o_plan(const Int4oArgs& a, const GatherArgs& ga, size_t lds, hipStream_t s) {
+    const int tiles = (int)woq::ceil_div(a.N, 16);
+    return launch_kernel(qgemv_int4o_tile<B, T, S, GATHER>, dim3((unsigned)woq::ceil_div(tiles, T)), dim3(64 * T * S),
+                         lds, s, a, ga);
+}
+
 template <int B, bool GATHER>
 hipError_t launch_int4o_tile(const Int4oArgs& a, const GatherArgs& ga, hipStream_t s) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
     const size_t lds = (size_t)woq::int4o_valu_lds_bytes(a.xp_len, 4 * (int64_t)a.G4, B);
-    // plans from whole-stack sweeps on MI355X (b = 1): rows of 128 groups or
-    // more on 512 tiles or more (70B down) run two tiles of eight waves per
-    // workgroup (70B down 23.1 -> 22.3 us); long rows on few tiles (3B down)
-    // one tile of eight waves, so every SIMD streams; 1024 tiles or more (3B
-    // and 70B gate|up, the 128256-row heads) two tiles of two waves, one
-    // staged copy of the activations for both (70B gate|up 40.8 -> 40.1 us);
-    // the rest one tile of four waves
-    if (a.G4 >= 128 && tiles >= 512)
-        return launch_kernel(qgemv_int4o_tile<B, 2, 8, GATHER>, dim3((unsigned)woq::ceil_div(tiles, 2)), dim3(1024),
-                             lds, s, a, ga);
-    if (a.G4 >= 48 && (tiles < 256 || a.G4 >= 128))
-        return launch_kernel(qgemv_int4o_tile<B, 1, 8, GATHER>, dim3((unsigned)tiles), dim3(512), lds, s, a, ga);
-    if (tiles >= 1024)
-        return launch_kernel(qgemv_int4o_tile<B, 2, 2, GATHER>, dim3((unsigned)woq::ceil_div(tiles, 2)), dim3(256),
-                             lds, s, a, ga);
-    return launch_kernel(qgemv_int4o_tile<B, 1, 4, GATHER>, dim3((unsigned)tiles), dim3(256), lds, s, a, ga);
+    // plans from whole-stack sweeps on MI355X: rows of 128 groups or more on
+    // 512 tiles or more (70B down) run two tiles of eight waves per workgroup
+    // (70B down 23.1 -> 22.3 us); 1024 tiles or more (3B and 70B gate|up, the
+    // 128256-row heads) two tiles of two waves, one staged copy of the
+    // activations for both (70B gate|up 40.8 -> 40.1 us)
+    if (a.G4 >= 128 && tiles >= 512) return launch_int4o_plan<B, 2, 8, GATHER>(a, ga, lds, s);
+    if constexpr (B == 1) {
+        // b = 1: long rows on few tiles one tile of eight waves, so every SIMD
+        // streams.  Otherwise one tile of four waves per workgroup, unless
+        // that leaves some compute units a workgroup more than others: then
+        // two tiles of two waves, or three of four, so that every compute unit
+        // runs at most one workgroup (70B q|k|v, 640 tiles: 10.9 -> 10.4 us
+        // with three tiles; 3B q|k|v, 320 tiles: 5.6 -> 5.2 us with two; 70B
+        // o, 512 tiles, and 3B o, 192, stay at one).  3B down (192 tiles of 64
+        // groups) measured 6.4 -> 6.0 us with four waves instead of eight.
+        if (a.G4 >= 128) return launch_int4o_plan<B, 1, 8, GATHER>(a, ga, lds, s);
+        if (tiles >= 1024) return launch_int4o_plan<B, 2, 2, GATHER>(a, ga, lds, s);
+        const int cus = compute_units();
+        if (tiles > cus && tiles % cus != 0) {
+            if (tiles <= 2 * cus) return launch_int4o_plan<B, 2, 2, GATHER>(a, ga, lds, s);
+            if (tiles <= 3 * cus) return launch_int4o_plan<B, 3, 4, GATHER>(a, ga, lds, s);
+        }
+        return launch_int4o_plan<B, 1, 4, GATHER>(a, ga, lds, s);
+    } else {
+        // b = 2..4: long rows on few tiles one tile of eight waves, 1024
+        // tiles or more two tiles of two waves, the rest one tile of four
+        if (a.G4 >= 48 && (tiles < 256 || a.G4 >= 128)) return launch_int4o_plan<B, 1, 8, GATHER>(a, ga, lds, s);
+        if (tiles >= 1024) return launch_int4o_plan<B, 2, 2, GATHER>(a, ga, lds, s);
+        return launch_int4o_plan<B, 1, 4, GATHER>(a, ga, lds, s);
+    }
 }
 
 template <bool GATHER>
