@@ -309,6 +309,14 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
     const uint4* ob = a.wout + (int64_t)tb * a.no8 * 16 + m;
     const int i80 = 4 * s + c;
     const uint4 wo0 = gload_u4(a.no8 > 0 ? ob + (int64_t)(i80 < a.no8 ? i80 : 0) * 16 : dummy);
+    // a wave with a second outlier step (more than 4 S chunks of outlier
+    // columns, e.g. 288 columns over eight waves) loads it here too, so that
+    // no wave ends on a memory round trip; the load is unconditional (a wave
+    // without a second step rereads its first chunk, a line already in
+    // flight), since a load on one path only would make the compiler wait for
+    // every load in flight where the paths join
+    const int i81 = 4 * (s + S) + c;
+    const uint4 wo1 = gload_u4(a.no8 > 0 ? ob + (int64_t)(i81 < a.no8 ? i81 : (i80 < a.no8 ? i80 : 0)) * 16 : dummy);
 
     // 3. activations into LDS
 #pragma unroll
@@ -404,11 +412,12 @@ __global__ __launch_bounds__(64 * T * S) void qgemv_int4o_tile(Int4oArgs a, Gath
         if (j0 + u < J) consume(j0 + u, wq[u], sq[u]);
 
     // 6. FP16 outlier columns: step st covers outlier chunks 4 st .. 4 st + 3
-    // (lane chunk c); the first step's chunk was loaded with the window
+    // (lane chunk c); the chunks of the first two steps were loaded with the
+    // window
     for (int st = s; 32 * st < 8 * a.no8; st += S) {
         const int i8 = 4 * st + c;
         const bool in = i8 < a.no8;
-        const uint4 wo = st == s ? wo0 : gload_u4(ob + (int64_t)(in ? i8 : 0) * 16);
+        const uint4 wo = st == s ? wo0 : st == s + S ? wo1 : gload_u4(ob + (int64_t)(in ? i8 : 0) * 16);
         if (in) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
