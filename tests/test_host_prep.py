@@ -5,6 +5,7 @@ on the host, so they are checked here without a GPU; the ABI checks confirm the
 built library exports every function the header declares.
 """
 import os
+import sys
 import re
 
 import numpy as np
@@ -582,3 +583,12 @@ def test_perm_positions_rejects_non_permutations():
     assert woq.woq_qgemv_int4o_x_supported(woq.woq_int4o_geometry(28672), 1)
     assert not woq.woq_qgemv_int4o_x_supported(woq.woq_int4o_geometry(28672), 2)
     assert not woq.woq_qgemv_int4o_x_supported(woq.woq_int4o_geometry(3072), 8)
+
+
+def test_library_loads_after_torchs_hip_runtime():
+    """torch ships its own HIP runtime; the binding imports torch before it
+    loads the library, so that both use one runtime."""
+    import subprocess
+    code = ("import sys; from weight_only_quantized_quantize_amd import woq; "
+            "assert 'torch' not in sys.modules; woq.lib(); assert 'torch' in sys.modules")
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True, timeout=300)

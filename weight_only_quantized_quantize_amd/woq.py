@@ -134,6 +134,13 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libwoq.so is not built ({LIB_PATH}); run "
                                "`python -m weight_only_quantized_quantize_amd.build`")
+        # torch ships its own HIP runtime: load it before the library, so that
+        # the library binds to that runtime instead of loading a second one
+        # (with two in one process the GPU was reported missing on MI355X)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(lib, name)
