@@ -824,12 +824,14 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     constexpr int CHB = NBT == 1 ? (S >= 2 ? (HALF ? 16 : 8) : 4) : NBT == 2 ? 4 : 2;
     constexpr int CH = S > CHB ? S : CHB;             // groups per chunk
     constexpr int KC = CH / S;                        // groups per wave per chunk
-    // weight window (groups, whole chunks): four with 8 staged columns where
-    // whole chunks allow it, as in the vector kernel a shallower window lets
-    // the staged activations arrive sooner (measured on MI355X over the
-    // 70B-shaped layer: 122.3 -> 120.2 us at b = 8, 117.5 -> 115.9 us at
-    // b = 4); eight otherwise for one column tile, four for more
-    constexpr int P = NBT == 1 ? ((HALF && 4 % KC == 0) ? 4 : 8) : 4;
+    // weight window (groups, whole chunks): as in the vector kernel a
+    // shallower window lets the staged activations arrive sooner.  Where
+    // whole chunks allow it, four groups for one column tile and two for two
+    // (measured on MI355X over the 70B-shaped layer: 122.3 -> 120.2 us at
+    // b = 8, 117.5 -> 115.9 us at b = 4, 132.7 -> 128.6 us at b = 16 with
+    // four instead of eight; 176.2 -> 174.5 us at b = 32 with two instead of
+    // four); otherwise eight for one column tile, four for more
+    constexpr int P = NBT == 1 ? (4 % KC == 0 ? 4 : 8) : (NBT == 2 && 2 % KC == 0 ? 2 : 4);
     static_assert(P % KC == 0, "window must hold whole chunks");
     constexpr int UNR = P / KC < 2 ? 2 : P / KC;      // chunks per unrolled loop body (even)
     static_assert(UNR % 2 == 0 && UNR % (P / KC) == 0, "unroll");
