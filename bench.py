@@ -343,7 +343,7 @@ def main():
     kern_ms = sum(step_ms)
     if spec.fmt == "int4o":
         kname = ("qgemv_int4o_tile (vector kernel; permutation folded in)" if b <= 2 else
-                 "woq_permute_x + qgemm_int4o_mfma (+ split-K reduction)")
+                 "woq_permute_x + qgemm_int4o_mfma" + (" + split-K reduction" if launches > 2 * len(shapes) else ""))
     else:
         kname = "qgemv_int8_valu" if b < 4 else "qgemv_int8_valu + qgemm_int8_mfma"
     # Dispatch-boundary spans of consecutive launches overlap by part of the

@@ -426,7 +426,7 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
  * woq_qgemv_int4o_x launch wherever its vector kernel serves the batch and
  * that form applies (woq_qgemv_int4o_x_supported, K a multiple of 8, the
  * input 16-byte aligned), otherwise woq_permute_x followed by the matrix-core
- * product (woq_qgemm_int4o; on rows of 128 groups or more at 3 <= b <= 32 its
+ * product (woq_qgemm_int4o; on rows of 128 groups or more at 9 <= b <= 32 its
  * split-K form, woq_qgemm_int4o_splitk with 8 ranges and a runner-owned
  * workspace, two launches); an INT8 step is one woq_qgemv_int8 launch.  The
  * one-launch and two-launch vector forms give the same bits.

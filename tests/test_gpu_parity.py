@@ -453,13 +453,17 @@ def test_int4o_mfma_chunk_remainders(gpu_lib, b, N, K):
 
 
 @pytest.mark.parametrize("b,N,K", [(3, 6200, 8200), (5, 700, 28700), (8, 4100, 8300), (8, 700, 28700),
-                                   (6, 300, 10000), (8, 16, 8100), (7, 10250, 8300)])
+                                   (6, 300, 10000), (8, 16, 8100), (7, 10250, 8300), (5, 8190, 8300),
+                                   (8, 12300, 8300), (4, 8200, 8300)])
 def test_int4o_mfma_long_rows_small_batch(gpu_lib, b, N, K):
     """Matrix-core products on rows of 64 groups or more at b <= 8, which stage
     only 8 activation columns in chunks of 16 groups: ragged row counts, a
-    partial last chunk (and, N = 10250, the four-tile plan of 641 tiles with
-    one tile of 10 rows in its last workgroup), on sampled rows including the
-    first and last."""
+    partial last chunk, and every plan of one workgroup per compute unit on
+    256 of them - two tiles of eight waves (N = 4100, 8190: 512 tiles, the
+    last of 14 rows; 8200: 513 tiles, three per workgroup), three of four
+    (N = 10250: 641 tiles, the last of 10 rows), four of four (N = 12300: 769
+    tiles, the last of 12 rows) - on sampled rows including the first and
+    last."""
     _print_case("int4o mfma long rows", b, N, K)
     rng = np.random.default_rng(b * 7 + N + K)
     g = woq.woq_int4o_geometry(K)

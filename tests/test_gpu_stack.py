@@ -114,12 +114,13 @@ def test_small_stack_runner_equals_entry_points_and_oracle(gpu_lib, cfg, b):
             assert err <= TOL
 
 
-@pytest.mark.parametrize("b", [3, 8, 20])
+@pytest.mark.parametrize("b", [3, 8, 9, 20])
 def test_stack_long_rows_use_split_k(gpu_lib, b):
     """A stack whose down product has rows of 129 groups (intermediate 16500):
-    the runner splits that product's K range (one more launch for the
-    reduction); its outputs equal the split-K entry point composed by hand bit
-    for bit and match the oracle."""
+    above b = 8 the runner splits that product's K range (one more launch for
+    the reduction), at b <= 8 it runs the unsplit matrix-core product; either
+    way its outputs equal the entry point composed by hand bit for bit and
+    match the oracle."""
     import torch
     _case("long-row stack", b)
     spec = synth.small_stack_spec(2, layers=1, hidden=384, inter=16500, batches=(b,))
@@ -135,15 +136,19 @@ def test_stack_long_rows_use_split_k(gpu_lib, b):
     assert g.G4 >= 128
     xp = torch.empty(b, g.xp_len, dtype=torch.float16, device="cuda")
     woq.woq_permute_x(ins[3], rs.perm_dev["m"], g, xp)
-    nbytes = woq.lib().woq_qgemm_int4o_splitk_workspace(dev.N, b, 8)
-    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     y = torch.empty_like(outs[3])
-    woq.woq_qgemm_int4o_splitk(dev.desc, xp, y, 8, ws)
+    split = b > 8
+    if split:
+        nbytes = woq.lib().woq_qgemm_int4o_splitk_workspace(dev.N, b, 8)
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+        woq.woq_qgemm_int4o_splitk(dev.desc, xp, y, 8, ws)
+    else:
+        woq.woq_qgemm_int4o(dev.desc, xp, y)
     np.testing.assert_array_equal(host(y).view(np.uint16), got[3].view(np.uint16))
     # q|k|v and o fold their permutation at b = 3 (one launch each); every
-    # other product is a permutation launch plus a product launch, and the
+    # other product is a permutation launch plus a product launch, and a
     # split down product adds the reduction
-    assert runner.launches(b) == (7 if b == 3 else 9)
+    assert runner.launches(b) == (6 if b == 3 else 8) + split
     perms = oracle_perms(spec)
     for gi, (nm, ip) in enumerate(GROUPS):
         err = O.normwise_rel_err(got[gi].astype(np.float64), oracle_group(spec, perms, 0, nm, ip, b))
@@ -196,7 +201,7 @@ def test_config2_stack_full_size(gpu_lib):
 def test_config4_layers_full_size_every_batch(gpu_lib):
     """Two layers of the 70B-shaped INT4O stack at full size through the
     runner, in the launch configuration the benchmark times (vector kernel at
-    b = 1, matrix cores at 8 and 32, split-K on down from b = 3): sampled rows
+    b = 1, matrix cores at 8 and 32, split-K on down above b = 8): sampled rows
     of every product against the oracle.  The permutations are the planted
     sets (the selection is covered elsewhere), which keeps the test short."""
     spec = synth.stack_spec(4)

@@ -92,14 +92,17 @@ inline bool int4o_use_valu(int64_t N, const woq_int4o_geom& g, int64_t b) {
 }
 
 // K splits the stack runner gives a matrix-core INT4O product (0: none).
-// Rows of 128 groups or more (the 70B-shaped down product, 224 groups) are
-// split in 8: every workgroup then covers 128 rows and one eighth of K, which
-// cuts the activation staging per weight byte (70B down at b = 8: 38 -> 33 us,
-// at b = 32: 62 -> 46 us, the reduction launch included); shorter rows gained
-// nothing.
+// Rows of 128 groups or more (the 70B-shaped down product, 224 groups) at
+// 9 <= b <= 32 are split in 8: every workgroup then covers 128 rows and one
+// eighth of K, which cuts the activation staging per weight byte (70B down at
+// b = 32: 62 -> 46 us, the reduction launch included); shorter rows gained
+// nothing.  At b <= 8, where eight staged columns keep the staging small, the
+// unsplit two-tile plan of sixteen waves is as fast or faster and saves the
+// reduction launch (measured on MI355X, 70B down: 32.7 -> 31.0 us at b = 4,
+// 33.7 -> 33.3 us at b = 8).
 constexpr int INT4O_SPLITS = 8;
 inline int int4o_splitk(int64_t N, const woq_int4o_geom& g, int64_t b) {
-    if (int4o_use_valu(N, g, b) || g.G4 < 128 || b > 32) return 0;
+    if (int4o_use_valu(N, g, b) || g.G4 < 128 || b <= 8 || b > 32) return 0;
     return INT4O_SPLITS;
 }
 
