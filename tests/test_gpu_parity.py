@@ -480,6 +480,31 @@ def test_int4o_mfma_long_rows_small_batch(gpu_lib, b, N, K):
     check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma long rows b={b} {N}x{K}")
 
 
+@pytest.mark.parametrize("b,N,K", [(9, 10250, 8300), (16, 8200, 8300), (17, 8190, 8300), (20, 12300, 8300),
+                                   (32, 10250, 8300), (32, 8190, 8300)])
+def test_int4o_mfma_long_rows_wide_batch(gpu_lib, b, N, K):
+    """Matrix-core products on rows of 64 groups or more at 9 <= b <= 32 (one
+    or two column tiles of 16 batch columns), in every plan of one workgroup
+    per compute unit: two tiles of eight waves (512 and 513 tiles, ragged
+    last tile), three of four (641 tiles, the last of 10 rows), four of four
+    (769 tiles); sampled rows including the first and last against the
+    oracle."""
+    _print_case("int4o mfma long rows wide batch", b, N, K)
+    rng = np.random.default_rng(b * 11 + N + K)
+    g = woq.woq_int4o_geometry(K)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x, force_mfma=True)
+    rows = np.unique(np.concatenate([np.arange(16), np.sort(rng.choice(N, 100, replace=False)),
+                                     np.arange(N - 16, N)]))
+    check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma long rows b={b} {N}x{K}")
+
+
 @pytest.mark.parametrize("b,N,K,splits", [(3, 1000, 16400, 8), (8, 1000, 16400, 2), (17, 300, 16400, 5),
                                           (32, 2056, 16400, 8), (8, 16, 2000, 16), (5, 33, 1000, 1)])
 def test_int4o_splitk_entry_point(gpu_lib, b, N, K, splits):

@@ -1307,22 +1307,20 @@ hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
     if constexpr (NBT >= 3) {
         return launch_int4o_mfma_ts<NBT, 2, 2>(a, b, tiles, s);
     } else {
-        // with 8 staged columns (b <= 8, rows of 64 groups or more) these
-        // products are bound by the loads in flight per compute unit: one
-        // workgroup per compute unit, as many waves as fit, and the fewest
-        // tiles per workgroup that still place every tile in one round (two
-        // tiles of eight waves, three of four, else four of four; measured on
-        // MI355X against the one plan of earlier builds: 70B o at b = 8
-        // 18.0 -> 17.5 us and at b = 4 17.4 -> 16.7 us, 70B q|k|v 20.6 ->
-        // 19.6 and 19.8 -> 19.0 us; deeper weight windows and the other
-        // plans of 4-16 waves were slower)
-        if constexpr (NBT == 1) {
-            if (tiles >= 256 && b <= 8 && a.G4 >= 64) {
-                const int per = (int)woq::ceil_div(tiles, compute_units());
-                if (per <= 2) return launch_int4o_mfma_ts<NBT, 2, 8>(a, b, tiles, s);
-                if (per == 3) return launch_int4o_mfma_ts<NBT, 3, 4>(a, b, tiles, s);
-                return launch_int4o_mfma_ts<NBT, 4, 4>(a, b, tiles, s);
-            }
+        // on rows of 64 groups or more these products are bound by the loads
+        // in flight per compute unit: one workgroup per compute unit, as many
+        // waves as fit, and the fewest tiles per workgroup that still place
+        // every tile in one round (two tiles of eight waves, three of four,
+        // else four of four; measured on MI355X against the one plan of
+        // earlier builds: 70B o 18.0 -> 17.5 us at b = 8, 17.4 -> 16.7 us at
+        // b = 4 and 24.3 -> 23.3 us at b = 32, 70B q|k|v 20.6 -> 19.6, 19.8
+        // -> 19.0 and 29.6 -> 25.8 us; deeper weight windows, longer chunks
+        // and the other plans of 4-16 waves were slower)
+        if (tiles >= 256 && a.G4 >= 64) {
+            const int per = (int)woq::ceil_div(tiles, compute_units());
+            if (per <= 2) return launch_int4o_mfma_ts<NBT, 2, 8>(a, b, tiles, s);
+            if (per == 3) return launch_int4o_mfma_ts<NBT, 3, 4>(a, b, tiles, s);
+            return launch_int4o_mfma_ts<NBT, 4, 4>(a, b, tiles, s);
         }
         if (tiles >= 640) return launch_int4o_mfma_ts<NBT, 4, 2>(a, b, tiles, s);
         if (tiles >= 256) return launch_int4o_mfma_ts<NBT, 2, 4>(a, b, tiles, s);
