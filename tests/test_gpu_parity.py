@@ -459,11 +459,10 @@ def test_int4o_mfma_long_rows_small_batch(gpu_lib, b, N, K):
     """Matrix-core products on rows of 64 groups or more at b <= 8, which stage
     only 8 activation columns in chunks of 16 groups: ragged row counts, a
     partial last chunk, and every plan of one workgroup per compute unit on
-    256 of them - two tiles of eight waves (N = 4100, 8190: 512 tiles, the
-    last of 14 rows; 8200: 513 tiles, three per workgroup), three of four
-    (N = 10250: 641 tiles, the last of 10 rows), four of four (N = 12300: 769
-    tiles, the last of 12 rows) - on sampled rows including the first and
-    last."""
+    256 of them - two tiles of eight waves (N = 4100: 257 tiles; 8190: 512
+    tiles, the last of 14 rows), three of four (N = 8200: 513 tiles; 10250:
+    641 tiles, the last of 10 rows), four of four (N = 12300: 769 tiles, the
+    last of 12 rows) - on sampled rows including the first and last."""
     _print_case("int4o mfma long rows", b, N, K)
     rng = np.random.default_rng(b * 7 + N + K)
     g = woq.woq_int4o_geometry(K)
@@ -485,10 +484,10 @@ def test_int4o_mfma_long_rows_small_batch(gpu_lib, b, N, K):
 def test_int4o_mfma_long_rows_wide_batch(gpu_lib, b, N, K):
     """Matrix-core products on rows of 64 groups or more at 9 <= b <= 32 (one
     or two column tiles of 16 batch columns), in every plan of one workgroup
-    per compute unit: two tiles of eight waves (512 and 513 tiles, ragged
-    last tile), three of four (641 tiles, the last of 10 rows), four of four
-    (769 tiles); sampled rows including the first and last against the
-    oracle."""
+    per compute unit: two tiles of eight waves (512 tiles, the last of 14
+    rows), three of four (513 tiles, the last of 8 rows; 641 tiles, the last
+    of 10 rows), four of four (769 tiles, the last of 12 rows); sampled rows
+    including the first and last against the oracle."""
     _print_case("int4o mfma long rows wide batch", b, N, K)
     rng = np.random.default_rng(b * 11 + N + K)
     g = woq.woq_int4o_geometry(K)
