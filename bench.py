@@ -342,8 +342,14 @@ def main():
     launches = runner.launches(b)
     kern_ms = sum(step_ms)
     if spec.fmt == "int4o":
-        kname = ("qgemv_int4o_tile (vector kernel; permutation folded in)" if b <= 2 else
-                 "woq_permute_x + qgemm_int4o_mfma" + (" + split-K reduction" if launches > 2 * len(shapes) else ""))
+        if b <= 2:
+            kname = "qgemv_int4o_tile (vector kernel; permutation folded in)"
+        elif launches > 2 * len(shapes):
+            kname = "woq_permute_x + qgemm_int4o_mfma + split-K reduction"
+        elif launches == 2 * len(shapes):
+            kname = "woq_permute_x + qgemm_int4o_mfma"
+        else:
+            kname = "qgemm_int4o_mfma (permutation folded in where the permuted row fits on chip)"
     else:
         kname = "qgemv_int8_valu" if b < 4 else "qgemv_int8_valu + qgemm_int8_mfma"
     # Dispatch-boundary spans of consecutive launches overlap by part of the

@@ -350,6 +350,27 @@ int woq_qgemv_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, cons
                       int64_t b, uint16_t* y, int64_t ldy, void* stream);
 int woq_qgemv_int4o_x_supported(const woq_int4o_geom* g, int64_t b);
 
+/*
+ * woq_permute_x and woq_qgemm_int4o in one launch, on the matrix cores: the
+ * same result bit for bit (the same plans, groups, matrix-core steps and
+ * reductions).  x is read in its natural channel order (fp16 [b, ldx], all b
+ * rows, 16-byte aligned, ldx a multiple of 8 and >= K; y as for
+ * woq_qgemm_int4o); each workgroup scatters it through pos (device copy of
+ * woq_perm_positions, 16-byte aligned) into the whole permuted, split row of
+ * its 8 staged batch columns, held in on-chip memory (16 bytes per 8
+ * channels of the padded row, about 130 KB at K = 8192) while the weights
+ * stream, so the permutation needs no launch of its own (the OTF-LLM page's
+ * global static permutation, "Architecture & Key Innovations", applied
+ * where the product reads its input).  WOQ_EUNSUPPORTED unless
+ * woq_qgemm_int4o_x_supported(g, N, b): 1 <= b <= 8, rows of 64 groups or
+ * more, xp_len <= 65535, the staged row fits the device's LDS per workgroup
+ * and the product's workgroups (one per compute unit) fit the device in one
+ * round; callers then use the two-call form.  Asynchronous on stream.
+ */
+int woq_qgemm_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, const uint16_t* pos,
+                      int64_t b, uint16_t* y, int64_t ldy, void* stream);
+int woq_qgemm_int4o_x_supported(const woq_int4o_geom* g, int64_t N, int64_t b);
+
 /* The matrix-core (MFMA) kernel of woq_qgemv_int4o for any 1 <= b <= 64
  * (xp and y as there: all b rows). */
 int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_t* y,

@@ -91,11 +91,17 @@ def int4o_run(parts, g, perm, x, force_mfma=False):
         else:
             # the two-call form runs the matrix-core kernel here: same values up to summation order
             assert O.normwise_rel_err(y1.astype(np.float64), y_host.astype(np.float64)) <= TOL
+    if (force_mfma or b > 4) and woq.woq_qgemm_int4o_x_supported(g, dw.N, b):
+        # the matrix-core product with the permutation folded in: the same bits
+        y2 = one_launch(dw, g, perm, x, mfma=True)
+        np.testing.assert_array_equal(y2.view(np.uint16), y_host.view(np.uint16),
+                                      err_msg="one-launch matrix-core product differs from the two-call form")
     return y_host.astype(np.float64), _host(xp)
 
 
-def one_launch(dw, g, perm, x, ldx=None):
-    """woq_qgemv_int4o_x on x stored with leading dimension ldx (>= K, multiple of 8)."""
+def one_launch(dw, g, perm, x, ldx=None, mfma=False):
+    """woq_qgemv_int4o_x (mfma: woq_qgemm_int4o_x) on x stored with leading
+    dimension ldx (>= K, multiple of 8)."""
     b, K = x.shape
     ldx = ldx or -(-K // 8) * 8
     xpad = np.full((b, ldx), np.float16(3.0), np.float16)     # padding must not leak into the result
@@ -103,7 +109,7 @@ def one_launch(dw, g, perm, x, ldx=None):
     pos = _dev(woq.woq_perm_positions(perm, g))
     y = _empty16(b, dw.N)
     y.fill_(7.0)
-    woq.woq_qgemv_int4o_x(dw.desc, _dev(xpad), pos, y, ldx=ldx)
+    (woq.woq_qgemm_int4o_x if mfma else woq.woq_qgemv_int4o_x)(dw.desc, _dev(xpad), pos, y, ldx=ldx)
     return _host(y)
 
 
@@ -379,6 +385,65 @@ def test_int4o_one_launch_rejects_unsupported(gpu_lib):
     with pytest.raises(woq.WoqError) as e:
         woq.woq_qgemv_int4o_x(dw.desc, x, pos, _empty16(2, 4))
     assert e.value.status == woq.WOQ_EUNSUPPORTED
+
+
+def test_int4o_mfma_one_launch_rejects_unsupported(gpu_lib):
+    """The matrix-core one-launch form refuses what it does not cover (b above
+    8, rows whose permuted row does not fit on chip, rows under 64 groups)
+    with WOQ_EUNSUPPORTED, before any launch."""
+    for K, N, b in [(28672, 8192, 8), (8192, 4096, 9), (3072, 4096, 8)]:
+        g = woq.woq_int4o_geometry(K)
+        assert not woq.woq_qgemm_int4o_x_supported(g, N, b), (K, N, b)
+    g = woq.woq_int4o_geometry(28672)
+    rng = np.random.default_rng(2)
+    perm = O.global_perm(28672, np.sort(rng.choice(28672, g.n_out, replace=False)))
+    W = (rng.standard_normal((4, 28672)) * 0.02).astype(np.float32)
+    dw = woq.DeviceInt4o(int4o_parts([W], perm, g.n_out), g)
+    x = _dev(np.zeros((8, 28672), np.float16))
+    pos = _dev(woq.woq_perm_positions(perm, g))
+    with pytest.raises(woq.WoqError) as e:
+        woq.woq_qgemm_int4o_x(dw.desc, x, pos, _empty16(8, 4))
+    assert e.value.status == woq.WOQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("N,K,b", [(10240, 8192, 8), (8192, 8192, 8), (57344, 8192, 8), (8192, 8192, 5),
+                                   (10240, 8192, 3), (57344, 8192, 1), (8190, 8300, 7), (12300, 8200, 6),
+                                   (700, 8200, 4), (16, 8192, 2)])
+def test_int4o_mfma_one_launch_full_shapes(gpu_lib, N, K, b):
+    """The matrix-core product with the permutation folded in
+    (woq_qgemm_int4o_x) against the two-call form (woq_permute_x, then
+    woq_qgemm_int4o) bit for bit, on random device weights in the 70B-shaped
+    products' layout and plans (every plan of 8 staged columns: one tile per
+    workgroup below 256 tiles, two, three and four tiles of one workgroup per
+    compute unit, seven or eight tiles of two per wave from 2048 tiles),
+    with a random permutation and x stored with a padded leading dimension
+    whose padding must not leak into the result."""
+    import torch
+    _print_case("int4o mfma one launch", N, K, b)
+    g = woq.woq_int4o_geometry(K)
+    assert woq.woq_qgemm_int4o_x_supported(g, N, b)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(N + K + b)
+    cb, sb, wb = woq.woq_int4o_dev_sizes(N, g)
+    codes = torch.randint(0, 256, (cb,), dtype=torch.uint8, device="cuda", generator=gen)
+    scales = (torch.rand(sb // 2, device="cuda", generator=gen) * 0.01).half()
+    wout = (torch.rand(max(1, wb // 2), device="cuda", generator=gen) * 0.01).half()
+    w = woq.Int4oW()
+    w.codes, w.scales, w.w_out, w.N, w.geom = codes.data_ptr(), scales.data_ptr(), wout.data_ptr(), N, g
+    perm = np.random.default_rng(K).permutation(K).astype(np.int32)
+    ldx = -(-K // 8) * 8 + 24
+    x = torch.full((b, ldx), 3.0, dtype=torch.float16, device="cuda")
+    x[:, :K] = torch.randn(b, K, device="cuda", generator=gen).half()
+    xp = _empty16(b, g.xp_len)
+    woq.woq_permute_x(x[:, :K].contiguous(), _dev(perm), g, xp)
+    y2 = _empty16(b, N)
+    woq.woq_qgemm_int4o(w, xp, y2)
+    y1 = _empty16(b, N)
+    y1.fill_(7.0)
+    woq.woq_qgemm_int4o_x(w, x, _dev(woq.woq_perm_positions(perm, g)), y1, ldx=ldx)
+    h1, h2 = _host(y1), _host(y2)
+    assert np.all(np.isfinite(h2))
+    np.testing.assert_array_equal(h1.view(np.uint16), h2.view(np.uint16))
 
 
 def test_batch_prefix_invariant(gpu_lib):

@@ -795,6 +795,12 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int8_mfma(Int8Args a, int b)
 
 // ------------------------------------------------ INT4O, matrix cores (b >= 8)
 
+// Column stride (fp16) of the whole-row staging of the matrix-core kernel: the
+// row rounded up to 128 channels plus 8, so that consecutive columns start 16
+// bytes apart modulo 256 bytes, as the padded chunk buffers of the staged form
+// do (fewer LDS bank conflicts on the B-operand reads).
+__host__ __device__ inline int int4o_whole_stride(int xp_len) { return ((xp_len + 127) & ~127) + 8; }
+
 // A workgroup of T x S waves owns T tiles of 16 output rows; the S waves of a
 // tile split the groups of every K chunk (CH groups) between them.  Lane l
 // holds row l & 15 of its tile and the 16-byte chunk l >> 4 of each group (32
@@ -813,9 +819,20 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int8_mfma(Int8Args a, int b)
 // unconditional (clamped to a valid address, results unused), so the number
 // of loads in flight is the same on every path and each wait is exact.
 // Partial sums of the S waves of a tile meet in LDS.
-template <int NBT, int T, int S, int RB, bool HALF>
-__global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int b) {
+//
+// WHOLE (8 staged columns only): the permutation is folded in instead.  The
+// workgroup gathers the whole permuted row of all 8 columns into LDS once,
+// scattered from the natural-order activations ga.x through the
+// channel-position table ga.pos (as the vector kernel does) while its first
+// weight window is in flight; the chunk loop then runs without staging or
+// barriers, and lanes of batch columns 8..15 read columns 0..7 again (their
+// outputs are never stored; the MFMA columns are independent).  Groups, their
+// order per wave, the matrix-core steps and the reductions are those of the
+// staged form, so both give the same bits.
+template <int NBT, int T, int S, int RB, bool HALF, bool WHOLE = false>
+__global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int b, GatherArgs ga) {
     static_assert(!HALF || NBT == 1, "half-width staging is for one column tile");
+    static_assert(!WHOLE || HALF, "the whole-row form stages 8 columns");
     constexpr int W = T * S;
     // groups per chunk: with the K split, chunks of 8 groups halve the
     // barriers per group (measured faster on MI355X); wide batches are bound
@@ -844,8 +861,11 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     // holds zeros for the whole kernel (no branch, no register clears)
     constexpr int XCOLS = HALF ? COLS + 1 : COLS;
     constexpr int XSB = 2 * 2 * XCOLS * XS;
-    __shared__ __align__(16) uint16_t lds[(XSB > RED ? XSB : RED) / 2];
+    __shared__ __align__(16) uint16_t lds[WHOLE ? 8 : (XSB > RED ? XSB : RED) / 2];
     uint16_t (*xs)[XCOLS][XS] = reinterpret_cast<uint16_t (*)[XCOLS][XS]>(lds);
+    // WHOLE: the permuted rows of the 8 staged columns, [8][XW] fp16 (dynamic LDS)
+    extern __shared__ __align__(16) uint16_t xw[];
+    const int XW = int4o_whole_stride(a.xp_len);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -879,10 +899,11 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
         for (int t = 0; t < NBT; ++t) acc[r][t] = (f4){0.f, 0.f, 0.f, 0.f};
 
     // columns b .. XCOLS-1 of both buffers hold zeros for the whole kernel
-    for (int e = tid; e < 2 * XCOLS * XS; e += 64 * W) {
-        const int col = (e / XS) % XCOLS;
-        if (col >= b) lds[e] = 0;
-    }
+    if constexpr (!WHOLE)
+        for (int e = tid; e < 2 * XCOLS * XS; e += 64 * W) {
+            const int col = (e / XS) % XCOLS;
+            if (col >= b) lds[e] = 0;
+        }
 
     // staging: piece p of chunk k -> column p / PPC, channels 8 (p % PPC) of the chunk
     uint4 stg[2][NPT];
@@ -953,14 +974,33 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     constexpr int WC = P / KC;                        // chunks the window spans
     uint4 wq[P][RB];
     uint2 sc[P][RB];
+    // WHOLE: the first pieces of the row (a channel-position piece and the 8
+    // columns' activations for it) go out before the weight window
+    constexpr int SCW = WHOLE ? (W >= 16 ? 1 : 2) : 1;
+    const int npieces = (ga.K + 7) >> 3;
+    const int ldx16 = ga.ldx >> 3;
+    uint4 pvw[SCW], xvw[SCW][WHOLE ? 8 : 1];
+    if constexpr (WHOLE) {
 #pragma unroll
-    for (int c2 = 0; c2 < 2 - WC; ++c2) {
-        stage_load(stg[c2], c2);
+        for (int i = 0; i < SCW; ++i) {
+            const int p = tid + i * 64 * W;
+            const int pp = p < npieces ? p : 0;
+            pvw[i] = as_uint4(((const g_u32x4*)ga.pos)[pp]);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8)
+                xvw[i][c8] = as_uint4(((const g_u32x4*)ga.x)[(c8 < b ? c8 : 0) * ldx16 + pp]);
+        }
         __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+        for (int c2 = 0; c2 < 2 - WC; ++c2) {
+            stage_load(stg[c2], c2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 #pragma unroll
     for (int cp = -WC; cp < 0; ++cp) {
-        if (cp + 2 >= 0) {
+        if (!WHOLE && cp + 2 >= 0) {
             stage_load(stg[(cp + 2) & 1], cp + 2);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -976,15 +1016,45 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (nchunks > 0) stage_store(stg[0], 0, 0);
+    if constexpr (WHOLE) {
+        // scatter the row (columns b..7 hold copies of column 0, never used)
+        // into its permuted positions; then zero the padding of the permuted
+        // row: [K_bg, 128 G4) and [128 G4 + n_out, xp_len)
+#pragma unroll
+        for (int i = 0; i < SCW; ++i) {
+            const int p = tid + i * 64 * W;
+            if (p < npieces) {
+                if (p == npieces - 1 && (ga.K & 7)) scatter8<8>(xw, XW, xvw[i], pvw[i]);
+                else scatter8_full<8>(xw, XW, xvw[i], pvw[i], (lane >> 3) & 3);
+            }
+        }
+        for (int p = tid + SCW * 64 * W; p < npieces; p += 64 * W) {
+            uint4 x1[8];
+            const uint4 p1 = as_uint4(((const g_u32x4*)ga.pos)[p]);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) x1[c8] = as_uint4(((const g_u32x4*)ga.x)[(c8 < b ? c8 : 0) * ldx16 + p]);
+            if (p == npieces - 1 && (ga.K & 7)) scatter8<8>(xw, XW, x1, p1);
+            else scatter8_full<8>(xw, XW, x1, p1, (lane >> 3) & 3);
+        }
+        for (int k = ga.K_bg + tid; k < bgl; k += 64 * W)
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) xw[c8 * XW + k] = 0;
+        for (int k = bgl + ga.n_out + tid; k < xp_len; k += 64 * W)
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) xw[c8 * XW + k] = 0;
+    } else {
+        if (nchunks > 0) stage_store(stg[0], 0, 0);
+    }
     lds_barrier();
     const uint32_t bias = bias_reg();
     // one chunk: stage the loads of chunk k + 2, consume this wave's KC groups
     // (a slot is refilled only after its group's products, so the refill
     // lands in the same registers), write chunk k + 1 to the other buffer
     auto chunk = [&](int k, int cb) {
-        stage_load(stg[cb & 1], k + 2);          // chunk k's registers are free again
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!WHOLE) {
+            stage_load(stg[cb & 1], k + 2);      // chunk k's registers are free again
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
             const int u = (cb * KC + kk) % P;
@@ -1021,7 +1091,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
                 h8 Bv[4];
                 {
                     const int col = HALF ? (m < COLS ? m : COLS) : 16 * t + m;
-                    const lx_ptr xb = (lx_ptr)&xs[cb & 1][col][128 * gl + 32 * c];
+                    const lx_ptr xb = WHOLE ? (lx_ptr)&xw[(m & 7) * XW + 128 * (gv ? g : 0) + 32 * c]
+                                            : (lx_ptr)&xs[cb & 1][col][128 * gl + 32 * c];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
                 }
@@ -1048,8 +1119,10 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
             __builtin_amdgcn_sched_barrier(0);
         }
         // chunk k + 1 (loaded during chunk k - 1) into the other buffer, last read in chunk k - 1
-        if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1, k + 1);
-        lds_barrier();
+        if constexpr (!WHOLE) {
+            if (k + 1 < nchunks) stage_store(stg[(cb + 1) & 1], (cb + 1) & 1, k + 1);
+            lds_barrier();
+        }
     };
     // whole unrolled bodies first (k & 1 == cb & 1 and the slots of chunk k
     // are fixed by cb), then the last nchunks % UNR chunks
@@ -1083,7 +1156,11 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
             for (int t = 0; t < NBT; ++t) {
                 const int bc = t * 16 + m;
                 const bool okb = bc < b && in;
-                Bo[q][t] = __builtin_bit_cast(h8, load_x16((gx_ptr)(xo_base + (okb ? (int64_t)bc * xp_len + col0 : 0))));
+                if constexpr (WHOLE)
+                    Bo[q][t] = __builtin_bit_cast(h8, load_x16((lx_ptr)&xw[(m & 7) * XW + bgl + (in ? col0 : 0)]));
+                else
+                    Bo[q][t] = __builtin_bit_cast(
+                        h8, load_x16((gx_ptr)(xo_base + (okb ? (int64_t)bc * xp_len + col0 : 0))));
                 if (!okb) Bo[q][t] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
             }
         }
@@ -1099,7 +1176,7 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     // lane (c, m) holds rows 4c .. 4c + 3 of the tile, batch column 16t + m
     if (S > 1) {
         typedef float RedTile[RB][NBT][16][17];
-        RedTile* red = reinterpret_cast<RedTile*>(lds);
+        RedTile* red = reinterpret_cast<RedTile*>(WHOLE ? xw : lds);
         __syncthreads();                               // the staging buffers are dead
 #pragma unroll
         for (int r = 0; r < RB; ++r)
@@ -1273,19 +1350,40 @@ hipError_t launch_int8_mfma(const Int8Args& a, int b, hipStream_t s) {
     return launch_int8_mfma_ts<2, 4>(a, b, s);
 }
 
+// Dynamic LDS of the whole-row form: the 8 staged columns of the permuted row.
+size_t int4o_whole_lds_bytes(int64_t xp_len) { return (size_t)16 * int4o_whole_stride((int)xp_len); }
+
+// Allow a kernel the dynamic LDS it is launched with (above the default
+// limit), once per kernel and size.
+template <class K>
+void allow_dynamic_lds(K kernel, size_t bytes) {
+    static std::atomic<size_t> allowed{0};
+    if (bytes <= allowed.load(std::memory_order_relaxed)) return;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes) == hipSuccess)
+        allowed.store(bytes, std::memory_order_relaxed);
+}
+
 template <int NBT, int T, int S, int RB = 1>
-hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s, int splits = 1) {
+hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_t s, int splits = 1,
+                                const GatherArgs* ga = nullptr) {
+    const GatherArgs none = {};
+    const dim3 grid((unsigned)woq::ceil_div(tiles, T * RB), (unsigned)splits), block(64 * T * S);
     // up to 8 batch columns on long rows: stage 8 columns only, in chunks of
     // 16 groups (70B down at b = 8: 42.6 -> 37.5 us; on rows of 24 groups the
-    // longer chunks were slower)
+    // longer chunks were slower), or (ga) the whole row, gathered through the
+    // channel positions
     if constexpr (NBT == 1) {
-        if (b <= 8 && a.G4 >= 64)
-            return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, true>,
-                                 dim3((unsigned)woq::ceil_div(tiles, T * RB), (unsigned)splits), dim3(64 * T * S), 0,
-                                 s, a, b);
+        if (b <= 8 && a.G4 >= 64) {
+            if (ga) {
+                const size_t lds = int4o_whole_lds_bytes(a.xp_len);
+                allow_dynamic_lds(qgemm_int4o_mfma<NBT, T, S, RB, true, true>, lds);
+                return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, true, true>, grid, block, lds, s, a, b, *ga);
+            }
+            return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, true>, grid, block, 0, s, a, b, none);
+        }
     }
-    return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, false>,
-                         dim3((unsigned)woq::ceil_div(tiles, T * RB), (unsigned)splits), dim3(64 * T * S), 0, s, a, b);
+    return launch_kernel(qgemm_int4o_mfma<NBT, T, S, RB, false>, grid, block, 0, s, a, b, none);
 }
 
 // Tiles per workgroup (T), waves per tile (S) and tiles per wave (RB) of the
@@ -1296,13 +1394,15 @@ hipError_t launch_int4o_mfma_ts(const Int4oArgs& a, int b, int tiles, hipStream_
 // at b = 8 and 88 -> 67 us at b = 32) and share the staged activations among
 // eight waves; narrower ones split K over more waves so that every compute
 // unit has loads in flight (there, two tiles per wave were slower).
+// (the whole-row form, ga, takes the same plans: int4o_half_grid mirrors
+// the choice for 8 staged columns)
 template <int NBT>
-hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
+hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s, const GatherArgs* ga = nullptr) {
     const int tiles = (int)woq::ceil_div(a.N, 16);
     if (tiles >= 2048) {
         constexpr int RB = NBT <= 2 ? 2 : 1;
-        if (seven_tiles_fill(tiles, RB)) return launch_int4o_mfma_ts<NBT, 7, 1, RB>(a, b, tiles, s);
-        return launch_int4o_mfma_ts<NBT, 8, 1, RB>(a, b, tiles, s);
+        if (seven_tiles_fill(tiles, RB)) return launch_int4o_mfma_ts<NBT, 7, 1, RB>(a, b, tiles, s, 1, ga);
+        return launch_int4o_mfma_ts<NBT, 8, 1, RB>(a, b, tiles, s, 1, ga);
     }
     if constexpr (NBT >= 3) {
         return launch_int4o_mfma_ts<NBT, 2, 2>(a, b, tiles, s);
@@ -1318,14 +1418,39 @@ hipError_t launch_int4o_mfma(const Int4oArgs& a, int b, hipStream_t s) {
         // and the other plans of 4-16 waves were slower)
         if (tiles >= 256 && a.G4 >= 64) {
             const int per = (int)woq::ceil_div(tiles, compute_units());
-            if (per <= 2) return launch_int4o_mfma_ts<NBT, 2, 8>(a, b, tiles, s);
-            if (per == 3) return launch_int4o_mfma_ts<NBT, 3, 4>(a, b, tiles, s);
-            return launch_int4o_mfma_ts<NBT, 4, 4>(a, b, tiles, s);
+            if (per <= 2) return launch_int4o_mfma_ts<NBT, 2, 8>(a, b, tiles, s, 1, ga);
+            if (per == 3) return launch_int4o_mfma_ts<NBT, 3, 4>(a, b, tiles, s, 1, ga);
+            return launch_int4o_mfma_ts<NBT, 4, 4>(a, b, tiles, s, 1, ga);
         }
-        if (tiles >= 640) return launch_int4o_mfma_ts<NBT, 4, 2>(a, b, tiles, s);
-        if (tiles >= 256) return launch_int4o_mfma_ts<NBT, 2, 4>(a, b, tiles, s);
-        return launch_int4o_mfma_ts<NBT, 1, 8>(a, b, tiles, s);
+        if (tiles >= 640) return launch_int4o_mfma_ts<NBT, 4, 2>(a, b, tiles, s, 1, ga);
+        if (tiles >= 256) return launch_int4o_mfma_ts<NBT, 2, 4>(a, b, tiles, s, 1, ga);
+        return launch_int4o_mfma_ts<NBT, 1, 8>(a, b, tiles, s, 1, ga);
     }
+}
+
+// Workgroups of launch_int4o_mfma<1> on rows of 64 groups or more at b <= 8
+// (the plans above, 8 staged columns).
+int int4o_half_grid(int tiles) {
+    if (tiles >= 2048) return (int)woq::ceil_div(tiles, (seven_tiles_fill(tiles, 2) ? 7 : 8) * 2);
+    if (tiles >= 256) {
+        const int per = (int)woq::ceil_div(tiles, compute_units());
+        return (int)woq::ceil_div(tiles, per <= 2 ? 2 : per == 3 ? 3 : 4);
+    }
+    return tiles;
+}
+
+// LDS per workgroup of the current device, read once per device.
+int lds_per_block() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n < 1)
+            n = 65536;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Split-K launches: each workgroup covers more rows (fewer workgroups along
@@ -1448,6 +1573,35 @@ int woq_qgemm_int4o(const woq_int4o_w* w, const uint16_t* xp, int64_t b, uint16_
         default: e = launch_int4o_mfma<4>(a, (int)b, s); break;
     }
     return launch_status(e);
+}
+
+int woq_qgemm_int4o_x_supported(const woq_int4o_geom* g, int64_t N, int64_t b) {
+    if (!g || b < 1 || b > 8 || N < 1 || N > (int64_t)INT32_MAX - 64 || g->G4 < 64 || g->xp_len > 65535) return 0;
+    if (int4o_whole_lds_bytes(g->xp_len) + 64 > (size_t)lds_per_block()) return 0;
+    // one workgroup per compute unit (the LDS allows no more), in one round
+    return int4o_half_grid((int)woq::ceil_div(N, 16)) <= compute_units();
+}
+
+int woq_qgemm_int4o_x(const woq_int4o_w* w, const uint16_t* x, int64_t ldx, const uint16_t* pos, int64_t b,
+                      uint16_t* y, int64_t ldy, void* stream) {
+    int st = check_int4o_w(w);
+    if (st) return st;
+    const woq_int4o_geom& g = w->geom;
+    if (b < 0 || ldx < g.K || ldy < w->N || ldx > INT32_MAX || ldy > INT32_MAX) return WOQ_EINVAL;
+    if (b == 0 || w->N == 0) return WOQ_OK;
+    if (!x || !pos || !y) return WOQ_EINVAL;
+    if (!woq::aligned16(x) || !woq::aligned16(pos) || (ldx & 7) || ((uintptr_t)y & 1u)) return WOQ_EALIGN;
+    if (!woq_qgemm_int4o_x_supported(&g, w->N, b)) return WOQ_EUNSUPPORTED;
+    // a.xp = x: the kernel's clamped, unused loads need a valid address
+    Int4oArgs a = make_int4o_args(w, x, y, ldy);
+    GatherArgs ga;
+    ga.x = x;
+    ga.pos = pos;
+    ga.K = (int)g.K;
+    ga.K_bg = (int)g.K_bg;
+    ga.n_out = (int)g.n_out;
+    ga.ldx = (int)ldx;
+    return launch_status(launch_int4o_mfma<1>(a, (int)b, (hipStream_t)stream, &ga));
 }
 
 int64_t woq_qgemm_int4o_splitk_workspace(int64_t N, int64_t b, int32_t splits) {

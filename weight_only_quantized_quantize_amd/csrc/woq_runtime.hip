@@ -95,9 +95,19 @@ int make_positions(woq_stack* st) {
 // up to 16384 x 8704 channels (the earlier rule): 109-112 -> 102 us per layer
 // at b = 1 and 138-142 -> 131 us at b = 2 with a timing event around each
 // launch; the whole 80-layer step without events went from 7.20 to 7.17 ms.
-bool fold_permutation(const woq_stack_step& s, int64_t b) {
+//
+// Where the matrix-core kernel serves the batch (b <= 8), rows of 64 groups
+// or more whose permuted row fits on chip fold it the same way
+// (woq_qgemm_int4o_x: each workgroup gathers the row of its 8 staged columns
+// instead of staging the permuted copy chunk by chunk).
+// 0: a permutation launch before the product; 1: folded into the vector
+// kernel; 2: folded into the matrix-core kernel.
+int fold_permutation(const woq_stack_step& s, int64_t b) {
     const woq_int4o_geom& g = s.w4.geom;
-    return woq::int4o_use_valu(s.w4.N, g, b) && woq_qgemv_int4o_x_supported(&g, b) && (g.K & 7) == 0;
+    if ((g.K & 7) != 0) return 0;
+    if (woq::int4o_use_valu(s.w4.N, g, b)) return woq_qgemv_int4o_x_supported(&g, b) ? 1 : 0;
+    if (woq::int4o_splitk(s.w4.N, g, b)) return 0;
+    return woq_qgemm_int4o_x_supported(&g, s.w4.N, b) ? 2 : 0;
 }
 
 // One step (the step table's entry i, or a copy of it whose weight pointers
@@ -115,9 +125,11 @@ int run_step(woq_stack* st, size_t i, const woq_stack_step& s, const uint16_t* x
         }
         bool on;
     } bracket(ev);
-    if (s.fmt == WOQ_FMT_INT4O && st->pos[i] && fold_permutation(s, b) && woq::aligned16(x)) {
+    if (s.fmt == WOQ_FMT_INT4O && st->pos[i] && woq::aligned16(x)) {
         // permutation folded into the product: one launch
-        return woq_qgemv_int4o_x(&s.w4, x, s.w4.geom.K, st->pos[i], b, y, s.w4.N, stream);
+        const int fold = fold_permutation(s, b);
+        if (fold == 1) return woq_qgemv_int4o_x(&s.w4, x, s.w4.geom.K, st->pos[i], b, y, s.w4.N, stream);
+        if (fold == 2) return woq_qgemm_int4o_x(&s.w4, x, s.w4.geom.K, st->pos[i], b, y, s.w4.N, stream);
     }
     if (s.fmt == WOQ_FMT_INT8) return woq_qgemv_int8(&s.w8, x, s.w8.K, b, y, s.w8.N, stream);
     int rc = woq_permute_x(x, s.w4.geom.K, s.perm, b, &s.w4.geom, st->xp, stream);
@@ -204,7 +216,7 @@ int woq_stack_launches(const woq_stack* st, int64_t b, int32_t* launches) {
     int32_t n = 0;
     for (size_t i = 0; i < st->steps.size(); ++i) {
         const woq_stack_step& s = st->steps[i];
-        n += (s.fmt == WOQ_FMT_INT4O && !(st->pos[i] && fold_permutation(s, b))) ? 2 : 1;
+        n += (s.fmt == WOQ_FMT_INT4O && !(st->pos[i] && fold_permutation(s, b) != 0)) ? 2 : 1;
         if (s.fmt == WOQ_FMT_INT4O && woq::int4o_splitk(s.w4.N, s.w4.geom, b)) n += 1;   // the reduction
     }
     *launches = n;

@@ -94,6 +94,9 @@ _SIGS = {
     "woq_qgemv_int4o_x": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                   c_void_p]),
     "woq_qgemv_int4o_x_supported": (c_int, [POINTER(Int4oGeom), c_int64]),
+    "woq_qgemm_int4o_x": (c_int, [POINTER(Int4oW), c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                  c_void_p]),
+    "woq_qgemm_int4o_x_supported": (c_int, [POINTER(Int4oGeom), c_int64, c_int64]),
     "woq_stack_create": (c_int, [POINTER(StackStep), c_int32, c_int64, POINTER(c_void_p)]),
     "woq_stack_run": (c_int, [c_void_p, POINTER(c_void_p), POINTER(c_void_p), c_int64, c_void_p]),
     "woq_stack_launches": (c_int, [c_void_p, c_int64, POINTER(c_int32)]),
@@ -399,6 +402,20 @@ def woq_qgemv_int4o_x(w: Int4oW, x, pos_dev, y, stream=None, b: int | None = Non
     need_rows(b, x, y)
     _check(_lib().woq_qgemv_int4o_x(ctypes.byref(w), _ptr(x), ldx or x.shape[1], _ptr(pos_dev), b, _ptr(y),
                                     y.shape[1], _stream(stream)), "woq_qgemv_int4o_x")
+    return y
+
+
+def woq_qgemm_int4o_x_supported(g: Int4oGeom, N: int, b: int) -> bool:
+    return bool(_lib().woq_qgemm_int4o_x_supported(ctypes.byref(g), N, b))
+
+
+def woq_qgemm_int4o_x(w: Int4oW, x, pos_dev, y, stream=None, b: int | None = None, ldx: int | None = None):
+    """The matrix-core product with the permutation folded in: x in its
+    natural channel order, pos_dev the device copy of woq_perm_positions."""
+    b = x.shape[0] if b is None else b
+    need_rows(b, x, y)
+    _check(_lib().woq_qgemm_int4o_x(ctypes.byref(w), _ptr(x), ldx or x.shape[1], _ptr(pos_dev), b, _ptr(y),
+                                    y.shape[1], _stream(stream)), "woq_qgemm_int4o_x")
     return y
 
 
