@@ -330,6 +330,22 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert lib.woq_qgemv_int8(w8, 16, 68, 1, 16, 8, None) == woq.WOQ_EALIGN   # ldx % 8
     assert lib.woq_qgemv_int8(w8, 16, 64, 9, 16, 8, None) == woq.WOQ_EINVAL   # b > 8
     assert lib.woq_permute_x(16, 100, 16, 1, g, 16, None) == woq.WOQ_EINVAL    # ldx < K
+    # the matrix-core one-launch form: argument checks before the support
+    # check and before any HIP call
+    assert lib.woq_qgemm_int4o_x(w, 16, 200, 16, 1, 16, 8, None) == woq.WOQ_EINVAL     # ldx < K
+    assert lib.woq_qgemm_int4o_x(w, 16, 256, 16, -1, 16, 8, None) == woq.WOQ_EINVAL    # b < 0
+    assert lib.woq_qgemm_int4o_x(w, 16, 256, 16, 1, 16, 4, None) == woq.WOQ_EINVAL     # ldy < N
+    assert lib.woq_qgemm_int4o_x(w, 16, 256, 16, 0, 16, 8, None) == woq.WOQ_OK         # b == 0: no-op
+    assert lib.woq_qgemm_int4o_x(w, 18, 256, 16, 1, 16, 8, None) == woq.WOQ_EALIGN     # x misaligned
+    assert lib.woq_qgemm_int4o_x(w, 16, 260, 16, 1, 16, 8, None) == woq.WOQ_EALIGN     # ldx % 8
+    assert lib.woq_qgemm_int4o_x(w, 16, 256, 24, 1, 16, 8, None) == woq.WOQ_EALIGN     # pos misaligned
+    assert lib.woq_qgemm_int4o_x(w, None, 256, 16, 1, 16, 8, None) == woq.WOQ_EINVAL   # no x
+    assert lib.woq_qgemm_int4o_x(bad, 16, 256, 16, 1, 16, 8, None) == woq.WOQ_EINVAL   # bad geometry
+    # rows under 64 groups and batches above 8 are never supported
+    assert lib.woq_qgemm_int4o_x(w, 16, 256, 16, 1, 16, 8, None) == woq.WOQ_EUNSUPPORTED
+    assert not woq.woq_qgemm_int4o_x_supported(woq.woq_int4o_geometry(3072), 4096, 8)
+    assert not woq.woq_qgemm_int4o_x_supported(woq.woq_int4o_geometry(8192), 8192, 9)
+    assert not woq.woq_qgemm_int4o_x_supported(woq.woq_int4o_geometry(8192), 0, 8)
 
 
 # -------------------------------------------------------------------- pager
