@@ -446,11 +446,14 @@ int woq_stack_create(const woq_stack_step* steps, int32_t n_steps, int64_t max_b
  * Run every step once, in order, on `stream`: an INT4O step is one
  * woq_qgemv_int4o_x launch wherever its vector kernel serves the batch and
  * that form applies (woq_qgemv_int4o_x_supported, K a multiple of 8, the
- * input 16-byte aligned), otherwise woq_permute_x followed by the matrix-core
- * product (woq_qgemm_int4o; on rows of 128 groups or more at 9 <= b <= 32 its
+ * input 16-byte aligned), one woq_qgemm_int4o_x launch wherever the
+ * matrix-core kernel serves it without a K split and that form applies
+ * (woq_qgemm_int4o_x_supported, K a multiple of 8, the input 16-byte
+ * aligned), otherwise woq_permute_x followed by the matrix-core product
+ * (woq_qgemm_int4o; on rows of 128 groups or more at 9 <= b <= 32 its
  * split-K form, woq_qgemm_int4o_splitk with 8 ranges and a runner-owned
  * workspace, two launches); an INT8 step is one woq_qgemv_int8 launch.  The
- * one-launch and two-launch vector forms give the same bits.
+ * one-launch and two-launch forms give the same bits.
  * inputs[slot] are fp16 [b, K of the step]
  * activations (rows contiguous), outputs[slot] fp16 [b, N of the step]; the
  * two pointer arrays must have an entry for every slot a step names, and each

@@ -201,7 +201,8 @@ def test_config2_stack_full_size(gpu_lib):
 def test_config4_layers_full_size_every_batch(gpu_lib):
     """Two layers of the 70B-shaped INT4O stack at full size through the
     runner, in the launch configuration the benchmark times (vector kernel at
-    b = 1, matrix cores at 8 and 32, split-K on down above b = 8): sampled rows
+    b = 1, matrix cores at 8 and 32 with the permutation folded in at b = 8
+    where the row fits on chip, split-K on down above b = 8): sampled rows
     of every product against the oracle.  The permutations are the planted
     sets (the selection is covered elsewhere), which keeps the test short."""
     spec = synth.stack_spec(4)
@@ -241,6 +242,14 @@ def test_config4_layers_full_size_every_batch(gpu_lib):
                 err = O.normwise_rel_err(got[4 * layer + gi][:, cols].astype(np.float64), np.concatenate(refs, axis=1))
                 print(f"b={b} layer {layer} {'|'.join(names)}: {err:.3e}", flush=True)
                 assert err <= TOL
+    # the launches the benchmark times: at b = 1 one per product (the
+    # permutation folded into the vector kernel); at b = 8 one for q|k|v, o
+    # and gate|up (folded into the matrix-core kernel) and two for down (its
+    # 28672-channel row does not fit on chip); at b = 32 two per product and
+    # the split-K reduction of down
+    assert runner.launches(1) == 4 * layers
+    assert runner.launches(8) == 5 * layers
+    assert runner.launches(32) == 9 * layers
     runner.close()
 
 
