@@ -569,6 +569,30 @@ def test_int4o_mfma_long_rows_wide_batch(gpu_lib, b, N, K):
     check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma long rows b={b} {N}x{K}")
 
 
+@pytest.mark.parametrize("b,N,K", [(24, 32770, 1100), (9, 32800, 2200), (32, 32790, 4100), (17, 36000, 1000)])
+def test_int4o_mfma_wide_plans_above_b8(gpu_lib, b, N, K):
+    """The widest matrix-core plans above b = 8 (seven or eight tiles of two
+    per wave, one wave per tile group), which multiply the biased codes and
+    seed each group's low-nibble sum with minus its activation correction:
+    ragged tile counts (a last workgroup only partly filled), groups that
+    end inside the last chunk and rows whose last group is partial, on
+    sampled rows including the first and last against the oracle."""
+    _print_case("int4o mfma wide plans", b, N, K)
+    rng = np.random.default_rng(b * 13 + N + K)
+    g = woq.woq_int4o_geometry(K)
+    outs = np.sort(rng.choice(K, g.n_out, replace=False))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, outs] *= 10
+    x = rng.standard_normal((b, K)).astype(np.float32)
+    x[:, outs] *= 20
+    x = x.astype(np.float16)
+    perm = O.global_perm(K, outs)
+    y, _ = int4o_run(int4o_parts([W], perm, g.n_out), g, perm, x, force_mfma=True)
+    rows = np.unique(np.concatenate([np.arange(16), np.sort(rng.choice(N, 100, replace=False)),
+                                     np.arange(N - 16, N)]))
+    check(y[:, rows], int4o_ref([W[rows]], perm, g.n_out, x), f"mfma wide plans b={b} {N}x{K}")
+
+
 @pytest.mark.parametrize("b,N,K,splits", [(3, 1000, 16400, 8), (8, 1000, 16400, 2), (17, 300, 16400, 5),
                                           (32, 2056, 16400, 8), (8, 16, 2000, 16), (5, 33, 1000, 1)])
 def test_int4o_splitk_entry_point(gpu_lib, b, N, K, splits):

@@ -829,10 +829,22 @@ __host__ __device__ inline int int4o_whole_stride(int xp_len) { return ((xp_len 
 // outputs are never stored; the MFMA columns are independent).  Groups, their
 // order per wave, the matrix-core steps and the reductions are those of the
 // staged form, so both give the same bits.
+//
+// BIAS (plans of one wave per tile group and two tiles per wave, 16 or more
+// staged columns): the code pairs enter the matrix cores with their exponent
+// bias (code + 1032, 16 code + 1152) instead of having it subtracted, as in
+// the vector kernel, and the low-nibble accumulator of each group starts from
+// minus the group's correction 1032 (sum of the activations over the group's
+// low-nibble channels) + 72 (sum over the high-nibble ones), which the staging
+// computes per group and batch column from the pieces it writes (four dot2
+// per piece and a fixed-order sum over the 16 lanes that hold a group).  The
+// products stay exact; the cancellation costs about 1e-5 of a group's
+// magnitude in fp32.
 template <int NBT, int T, int S, int RB, bool HALF, bool WHOLE = false>
 __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int b, GatherArgs ga) {
     static_assert(!HALF || NBT == 1, "half-width staging is for one column tile");
     static_assert(!WHOLE || HALF, "the whole-row form stages 8 columns");
+    constexpr bool BIAS = !HALF && !WHOLE && S == 1 && RB == 2;
     constexpr int W = T * S;
     // groups per chunk: with the K split, chunks of 8 groups halve the
     // barriers per group (measured faster on MI355X); wide batches are bound
@@ -863,6 +875,8 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
     constexpr int XSB = 2 * 2 * XCOLS * XS;
     __shared__ __align__(16) uint16_t lds[WHOLE ? 8 : (XSB > RED ? XSB : RED) / 2];
     uint16_t (*xs)[XCOLS][XS] = reinterpret_cast<uint16_t (*)[XCOLS][XS]>(lds);
+    // BIAS: minus the correction of each group of the staged chunk, per column
+    __shared__ float ncorr[BIAS ? 2 * CH * COLS : 1];
     // WHOLE: the permuted rows of the 8 staged columns, [8][XW] fp16 (dynamic LDS)
     extern __shared__ __align__(16) uint16_t xw[];
     const int XW = int4o_whole_stride(a.xp_len);
@@ -926,6 +940,25 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
                 const bool ok = k * CH * 128 + 8 * off < bgl;   // past the last group: zeros
                 *(__attribute__((address_space(3))) u32x4*)&xs[buf][col][8 * off] =
                     ok ? (u32x4){r[i].x, r[i].y, r[i].z, r[i].w} : (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+        if constexpr (BIAS) {
+            // the 16 pieces of a (group, column) sit on the 16 lanes of one
+            // row (PPC and the thread count are multiples of 16); pieces of
+            // even index within their group meet low-nibble codes (weight
+            // 1032), odd ones high-nibble codes (72)
+#pragma unroll
+            for (int i = 0; i < NPT; ++i) {
+                const int p = tid + i * 64 * W;
+                const int col = p / PPC, off = p % PPC;
+                const bool ok = col < b && k * CH * 128 + 8 * off < bgl;
+                const h2 wt = as_h2((off & 1) ? 0x54805480u : 0x64086408u);
+                float v = dot2(as_h2(r[i].x), wt, 0.0f);
+                v = dot2(as_h2(r[i].y), wt, v);
+                v = dot2(as_h2(r[i].z), wt, v);
+                v = dot2(as_h2(r[i].w), wt, v);
+                v = row16_sum(ok ? v : 0.0f);
+                if ((lane & 15) == 0 && col < COLS) ncorr[(buf * CH + (off >> 4)) * COLS + col] = -v;
             }
         }
     };
@@ -1074,7 +1107,18 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
                 sf[r][3] = h_to_f((uint16_t)(s1 >> 16));
                 Int4Pairs pr[4];
 #pragma unroll
-                for (int d = 0; d < 4; ++d) pr[d] = int4_pairs(wd[d], bias);
+                for (int d = 0; d < 4; ++d) {
+                    if constexpr (BIAS) {
+                        // biased pairs (the correction seeds the low-nibble sum)
+                        const uint32_t sh = wd[d] >> 8;
+                        pr[d].lo0 = as_h2((wd[d] & 0x000F000Fu) | bias);
+                        pr[d].lo1 = as_h2((sh & 0x000F000Fu) | bias);
+                        pr[d].hi0 = as_h2((wd[d] & 0x00F000F0u) | bias);
+                        pr[d].hi1 = as_h2((sh & 0x00F000F0u) | bias);
+                    } else {
+                        pr[d] = int4_pairs(wd[d], bias);
+                    }
+                }
 #pragma unroll
                 for (int Pp = 0; Pp < 2; ++Pp) {
                     const Int4Pairs& e0 = pr[2 * Pp];
@@ -1096,9 +1140,14 @@ __global__ __launch_bounds__(64 * T * S) void qgemm_int4o_mfma(Int4oArgs a, int 
 #pragma unroll
                     for (int q = 0; q < 4; ++q) Bv[q] = __builtin_bit_cast(h8, load_x16(xb + 8 * q));
                 }
+                f4 seed = (f4){0.f, 0.f, 0.f, 0.f};
+                if constexpr (BIAS) {
+                    const float nc = ncorr[((cb & 1) * CH + gl) * COLS + 16 * t + m];
+                    seed = (f4){nc, nc, nc, nc};
+                }
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
-                    f4 lo = (f4){0.f, 0.f, 0.f, 0.f}, hi = (f4){0.f, 0.f, 0.f, 0.f};
+                    f4 lo = seed, hi = (f4){0.f, 0.f, 0.f, 0.f};
                     lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][0], Bv[0], lo, 0, 0, 0);
                     hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][1], Bv[1], hi, 0, 0, 0);
                     lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][2], Bv[2], lo, 0, 0, 0);

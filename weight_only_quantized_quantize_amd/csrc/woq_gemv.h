@@ -252,6 +252,15 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+// Sum of v over the 16 lanes of its row, returned to every lane of the row,
+// in a fixed order (the first four exchanges of wave_sum_dpp).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_move<0xB1>(v);
+    v += dpp_move<0x4E>(v);
+    v += dpp_move<0x141>(v);
+    v += dpp_move<0x140>(v);
+    return v;
+}
 __device__ __forceinline__ float wave_sum_dpp(float v) {
     v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
     v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
